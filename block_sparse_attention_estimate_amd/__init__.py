@@ -1,0 +1,249 @@
+"""MI355X (gfx950) training-free block/stripe-sparse attention.
+
+Thin Python binding of libsa.so (C ABI in include/sa.h).  The functions here only marshal
+arguments: device memory and streams come from PyTorch, every computation runs in the
+library's HIP kernels, and nothing falls back to another implementation -- a missing or
+unbuilt library raises.
+
+Entry points (same names as the C ABI):
+  estimate_mask(q, k, theta, ...)       -> Lists     (sa_estimate_mask)
+  sparse_prefill(q, k, v, lists, ...)   -> (o, lse)  (sa_sparse_prefill)
+  build_block_summary(k_cache, ...)     -> kbar      (sa_build_block_summary)
+  sparse_decode(q, k_cache, v_cache, kbar, cache_len, ...) -> (o, lse, selected)
+  workspace_size(op, ...)                            (sa_workspace_size)
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import (SA_BLOCK, SA_STRIPE, SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE,  # noqa: F401
+                   SaError)
+
+__all__ = ["Lists", "estimate_mask", "sparse_prefill", "build_block_summary", "sparse_decode",
+           "workspace_size", "SaError", "load_library"]
+
+
+def load_library():
+    return _lib.load()
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _gran(g) -> int:
+    if g in ("block", SA_BLOCK):
+        return SA_BLOCK
+    if g in ("stripe", SA_STRIPE):
+        return SA_STRIPE
+    raise ValueError(f"granularity must be 'block' or 'stripe', got {g!r}")
+
+
+def _check_bf16(name, t, ndim):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA bfloat16 tensor")
+    if t.dim() != ndim or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be {ndim}-D with a contiguous last dimension")
+
+
+def _prefill_shape(q, k, v=None, o=None) -> _lib.SaShape:
+    _check_bf16("q", q, 4)
+    _check_bf16("k", k, 4)
+    B, N, Hq, D = q.shape
+    s = _lib.SaShape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = B, Hq, k.shape[2], D
+    s.seq_q, s.seq_k = N, k.shape[1]
+    s.q_stride[:] = q.stride()[:3]
+    s.k_stride[:] = k.stride()[:3]
+    vv = v if v is not None else k
+    s.v_stride[:] = vv.stride()[:3]
+    oo = o if o is not None else q
+    s.o_stride[:] = oo.stride()[:3]
+    return s
+
+
+def _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale, n_q_heads):
+    p = _lib.SaSparseParams()
+    p.block_q, p.block_k, p.sink_tokens, p.local_tokens = block_q, block_k, sink, local
+    p.granularity = _gran(granularity)
+    p.softmax_scale = float(softmax_scale or 0.0)
+    arr = None
+    if theta is not None:
+        th = torch.as_tensor(theta, dtype=torch.float32).reshape(-1)
+        if th.numel() == 1:
+            th = th.expand(n_q_heads)
+        if th.numel() != n_q_heads:
+            raise ValueError("theta needs one value per query head")
+        arr = (ctypes.c_float * n_q_heads)(*[float(x) for x in th.tolist()])
+        p.theta = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    return p, arr
+
+
+@dataclass
+class Lists:
+    """Per (batch, KV head, query block) kept lists: counts [B, Hkv, nQB] int32 and idx
+    [B, Hkv, nQB, stride] int32 (ascending block or column ids), optional margins."""
+    counts: torch.Tensor
+    idx: torch.Tensor
+    stride: int
+    granularity: str
+    margins: torch.Tensor | None = None
+
+    def c_struct(self) -> _lib.SaLists:
+        ls = _lib.SaLists()
+        ls.counts = _ptr(self.counts)
+        ls.idx = _ptr(self.idx)
+        ls.stride = self.stride
+        ls.margins = _ptr(self.margins)
+        return ls
+
+    def overflowed(self) -> bool:
+        """True when some stripe row had more entries than ``stride`` (synchronises)."""
+        return bool((self.counts > self.stride).any().item())
+
+
+def workspace_size(op, *, q=None, k=None, block_q=128, block_k=64, sink=32, local=256,
+                   granularity="block", theta=None, shape=None, decode_params=None) -> int:
+    lib = _lib.load()
+    if op == SA_OP_ESTIMATE:
+        s = _prefill_shape(q, k)
+        p, keep = _sparse_params(block_q, block_k, sink, local, granularity,
+                                 theta if theta is not None else 0.0, 0.0, q.shape[2])
+        return int(lib.sa_workspace_size(op, ctypes.byref(s), ctypes.byref(p)))
+    if op == SA_OP_DECODE:
+        return int(lib.sa_workspace_size(op, ctypes.byref(shape), ctypes.byref(decode_params)))
+    return 0
+
+
+def alloc_lists(q, k, *, block_q, block_k=64, granularity="block", stride=None,
+                margins=False) -> Lists:
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    nqb = -(-N // block_q)
+    nkb = -(-N // block_k)
+    gran = "stripe" if _gran(granularity) == SA_STRIPE else "block"
+    if stride is None:
+        stride = nkb if gran == "block" else N
+    counts = torch.empty((B, Hkv, nqb), dtype=torch.int32, device=q.device)
+    idx = torch.empty((B, Hkv, nqb, stride), dtype=torch.int32, device=q.device)
+    m = None
+    if margins:
+        ncand = nkb if gran == "block" else N
+        m = torch.full((B, Hkv, nqb, ncand), float("nan"), dtype=torch.float32, device=q.device)
+    return Lists(counts, idx, int(stride), gran, m)
+
+
+def estimate_mask(q, k, theta, *, block_q=128, block_k=64, sink=32, local=256,
+                  granularity="block", softmax_scale=0.0, stride=None, margins=False,
+                  workspace=None, out: Lists | None = None, stream=None) -> Lists:
+    """Anchor-based estimation pass (sa_estimate_mask).  q [B, N, Hq, d], k [B, N, Hkv, d]
+    bf16 CUDA tensors; theta scalar or [Hq] in logit units."""
+    lib = _lib.load()
+    s = _prefill_shape(q, k)
+    p, keep = _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale,
+                             q.shape[2])
+    lists = out if out is not None else alloc_lists(q, k, block_q=block_q, block_k=block_k,
+                                                    granularity=granularity, stride=stride,
+                                                    margins=margins)
+    need = int(lib.sa_workspace_size(SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ls = lists.c_struct()
+    _lib.check(lib.sa_estimate_mask(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k),
+                                    ctypes.byref(ls), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "sa_estimate_mask")
+    del keep
+    return lists
+
+
+def sparse_prefill(q, k, v, lists: Lists, *, block_q=128, block_k=64, sink=32, local=256,
+                   softmax_scale=0.0, out=None, lse=True, stream=None):
+    """Block/stripe-sparse attention over given lists (sa_sparse_prefill).
+    Returns (o [B, N, Hq, d] bf16, lse [B, Hq, N] fp32 or None)."""
+    lib = _lib.load()
+    _check_bf16("v", v, 4)
+    o = out if out is not None else torch.empty_like(q)
+    s = _prefill_shape(q, k, v, o)
+    p, keep = _sparse_params(block_q, block_k, sink, local, lists.granularity, None,
+                             softmax_scale, q.shape[2])
+    lse_t = None
+    if lse:
+        lse_t = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32,
+                            device=q.device)
+    ls = lists.c_struct()
+    _lib.check(lib.sa_sparse_prefill(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                     ctypes.byref(ls), _ptr(o), _ptr(lse_t), _stream(stream)),
+               "sa_sparse_prefill")
+    del keep
+    return o, lse_t
+
+
+def _decode_shape(q, k_cache, v_cache, o=None) -> _lib.SaShape:
+    _check_bf16("q", q, 3)
+    _check_bf16("k_cache", k_cache, 4)
+    B, Hq, D = q.shape
+    s = _lib.SaShape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = B, Hq, k_cache.shape[2], D
+    s.seq_q, s.seq_k = 1, k_cache.shape[1]
+    s.q_stride[:] = (q.stride(0), 0, q.stride(1))
+    s.k_stride[:] = k_cache.stride()[:3]
+    vv = v_cache if v_cache is not None else k_cache
+    s.v_stride[:] = vv.stride()[:3]
+    oo = o if o is not None else q
+    s.o_stride[:] = (oo.stride(0), 0, oo.stride(1))
+    return s
+
+
+def build_block_summary(k_cache, cache_len, *, block_k=64, n_q_heads=None, out=None, stream=None):
+    """Mean key per block (sa_build_block_summary): [B, ceil(L/bk), Hkv, d] bf16."""
+    lib = _lib.load()
+    _check_bf16("k_cache", k_cache, 4)
+    B, L, Hkv, D = k_cache.shape
+    s = _lib.SaShape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = B, n_q_heads or Hkv, Hkv, D
+    s.seq_q, s.seq_k = 1, L
+    s.k_stride[:] = k_cache.stride()[:3]
+    nkb = -(-L // block_k)
+    kbar = out if out is not None else torch.empty((B, nkb, Hkv, D), dtype=torch.bfloat16,
+                                                   device=k_cache.device)
+    _lib.check(lib.sa_build_block_summary(ctypes.byref(s), block_k, _ptr(k_cache), _ptr(cache_len),
+                                          _ptr(kbar), _stream(stream)), "sa_build_block_summary")
+    return kbar
+
+
+def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_k=64, sink=32,
+                  local=256, n_splits=0, softmax_scale=0.0, workspace=None, out=None,
+                  return_selected=True, stream=None):
+    """Top-K block-sparse decode (sa_sparse_decode).  q [B, Hq, d]; caches [B, L, Hkv, d].
+    Returns (o [B, Hq, d] bf16, lse [B, Hq] fp32, selected [B, Hkv, top_k] int32 or None)."""
+    lib = _lib.load()
+    _check_bf16("v_cache", v_cache, 4)
+    o = out if out is not None else torch.empty_like(q)
+    s = _decode_shape(q, k_cache, v_cache, o)
+    p = _lib.SaDecodeParams()
+    p.block_k, p.top_k_blocks, p.sink_tokens, p.local_tokens = block_k, top_k, sink, local
+    p.n_splits, p.softmax_scale = n_splits, float(softmax_scale or 0.0)
+    need = int(lib.sa_workspace_size(SA_OP_DECODE, ctypes.byref(s), ctypes.byref(p)))
+    if need == 0:
+        raise SaError(_lib.SA_ERR_PARAM, "sa_workspace_size(decode)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    B, Hq, _ = q.shape
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    sel = None
+    if return_selected:
+        sel = torch.empty((B, k_cache.shape[2], top_k), dtype=torch.int32, device=q.device)
+    _lib.check(lib.sa_sparse_decode(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(k_summary), _ptr(cache_len), _ptr(o),
+                                    _ptr(lse), _ptr(sel), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "sa_sparse_decode")
+    return o, lse, sel

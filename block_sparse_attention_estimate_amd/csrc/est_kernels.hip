@@ -1,0 +1,499 @@
+// Estimation pass for anchor-based block/stripe-sparse prefill on gfx950.
+//
+// AnchorAttention (arXiv 2505.23520) Eq. (1): anchor = max score over the initial and
+// local key regions, read from the row-max buffer (referee major comment 1); Eq. (2): keep
+// where avgpool(x_a) - avgpool(Q) K^T / sqrt(d) <= theta; Eq. (3): per-query-block index
+// set I.  SALE (arXiv 2505.24179), "What carries the argument": the estimate uses
+// quantised Q and K and the decision is one log-domain comparison.  KVpop (arXiv
+// 2607.05061), referee minor comment 4: grouped heads are combined with max.
+//
+// Kernels, in launch order:
+//   est_quant_k       one workgroup per (b, g, key tile): int8 keys + one scale per tile
+//   est_anchor_pool   one workgroup per (b, g, query block): anchor max on bf16 MFMA over the
+//                     sink + local keys, block mean, pooled query (fp64 sum), int8 pooled query
+//   est_score_block   int8 MFMA of key tiles against pooled queries, block max, margin,
+//                     max over the group's heads -> one keep bit per (query block, key block)
+//   est_score_stripe  same per key column (no block max)
+//   est_compact       bits | forced, causal -> ascending index lists + counts
+//
+// Floating-point steps that decide an integer (int8 codes, keep bits) use explicit
+// round-to-nearest operations (__fmul_rn, __fdiv_rn, rintf) in the order the oracle uses.
+#include "sa_common.h"
+#include "sa_internal.h"
+
+#define NEG_INF (-__builtin_huge_valf())
+
+// ---------------------------------------------------------------------------------------
+// int8 key tiles: a = max |K| over the tile, scale = a / 127, code = rint(K * (127 / a)).
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void est_quant_k(EstArgs a) {
+  constexpr int CH = D / 8;              // 16-byte chunks per key row
+  constexpr int PER = 64 * CH / 256;     // chunks per thread (tile of 64 keys)
+  const int J = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  u16x8 v[PER];
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int ch = tid + c * 256;
+    const int key = J * 64 + ch / CH;
+    const int dc = (ch % CH) * 8;
+    if (key < a.N) {
+      v[c] = *(const u16x8*)(a.k + b * a.ks0 + (int64_t)key * a.ks1 + g * a.ks2 + dc);
+    } else {
+      v[c] = (u16x8)(0);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf16_bits_to_float(v[c][e])));
+  }
+  __shared__ float red[4];
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float inv = 0.f, scale = 1.f;
+  if (amax > 0.f) {
+    inv = __fdiv_rn(127.0f, amax);
+    scale = __fdiv_rn(amax, 127.0f);
+  }
+  int8_t* dst = a.kq + ((int64_t)(b * a.Hkv + g) * a.nKB * 64) * D;
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int ch = tid + c * 256;
+    const int key = J * 64 + ch / CH;
+    const int dc = (ch % CH) * 8;
+    unsigned int w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float r = rintf(__fmul_rn(bf16_bits_to_float(v[c][e]), inv));
+      r = fminf(fmaxf(r, -127.f), 127.f);
+      const int qi = (int)r;
+      w[e >> 2] |= ((unsigned int)(qi & 0xFF)) << (8 * (e & 3));
+    }
+    *(u32x2*)(dst + (int64_t)key * D + dc) = (u32x2){w[0], w[1]};
+  }
+  if (tid == 0) a.sk[(b * a.Hkv + g) * a.nKB + J] = scale;
+}
+
+// ---------------------------------------------------------------------------------------
+// Anchor (Eq. 1), block mean of the anchor and pooled, quantised query (Eq. 2).
+// S^T = K_region Q^T on 32x32x16 bf16 MFMA: a lane owns one query row (column n) and
+// sees 16 of the 32 keys of each tile, so the row max is in-lane plus one half swap.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void est_anchor_pool(EstArgs a) {
+  constexpr int KS = D / 16;
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int G = a.G;
+  const int r0 = i * a.bq;
+  const int r1 = min(a.N, r0 + a.bq);
+  const int nrows = r1 - r0;
+  const int ntph = (a.bq + 31) / 32;
+  __shared__ float xa_s[8][128];
+  __shared__ float qbar_s[8][128];
+
+  for (int nt = wave; nt < G * ntph; nt += 4) {
+    const int hg = nt / ntph, tr = nt % ntph;
+    const int h = g * G + hg;
+    const int ra = r0 + tr * 32;
+    if (ra >= r1) continue;
+    const int row = ra + l32;
+    const int rowc = min(row, a.N - 1);
+    bf16x8 qf[KS];
+    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + h * a.qs2 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
+    float mx = NEG_INF;
+    const int hi = min(ra + 31, a.N - 1);
+    const int sink_end = min(a.sink, hi + 1);
+    const int sink_tiles_end = ((sink_end + 31) / 32) * 32;
+    const int lo = max(0, ra - a.local + 1);
+    const int win_start = max((lo / 32) * 32, sink_tiles_end);
+    const uint16_t* kb = a.k + b * a.ks0 + g * a.ks2 + half * 8;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int t_begin = pass == 0 ? 0 : win_start;
+      const int t_end = pass == 0 ? sink_tiles_end : hi + 1;
+      for (int ts = t_begin; ts < t_end; ts += 32) {
+        const int kr = min(ts + l32, a.N - 1);
+        const uint16_t* kp = kb + (int64_t)kr * a.ks1;
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 kf = *(const bf16x8*)(kp + ks * 16);
+          acc = mfma_bf16(kf, qf[ks], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
+          const bool ok = key <= row && (key < a.sink || key >= row - a.local + 1);
+          if (ok) mx = fmaxf(mx, acc[r]);
+        }
+      }
+    }
+    mx = fmaxf(mx, swap_halves(mx));
+    if (half == 0 && row < r1) xa_s[hg][row - r0] = __fmul_rn(mx, a.c);
+  }
+
+  // Pooled query: fp64 sum over the block's rows, one rounding to fp32, fp32 division.
+  for (int p = tid; p < G * D; p += 256) {
+    const int hg = p / D, dd = p % D;
+    const int h = g * G + hg;
+    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r0 * a.qs1 + h * a.qs2 + dd;
+    double s = 0.0;
+    for (int r = 0; r < nrows; ++r) s += bf16_bits_to_double(qp[(int64_t)r * a.qs1]);
+    qbar_s[hg][dd] = __fdiv_rn((float)s, (float)nrows);
+  }
+  __syncthreads();
+
+  for (int hg = wave; hg < G; hg += 4) {
+    // block mean of the anchor (fp64 accumulation)
+    double s = 0.0;
+    for (int r = lane; r < nrows; r += 64) s += (double)xa_s[hg][r];
+    s = wave_sum_d(s);
+    float amax = 0.f;
+    for (int dd = lane; dd < D; dd += 64) amax = fmaxf(amax, fabsf(qbar_s[hg][dd]));
+    amax = wave_max(amax);
+    float inv = 0.f, scale = 1.f;
+    if (amax > 0.f) {
+      inv = __fdiv_rn(127.0f, amax);
+      scale = __fdiv_rn(amax, 127.0f);
+    }
+    const int64_t rowid = ((int64_t)(b * a.Hkv + g) * a.nQB + i) * G + hg;
+    int8_t* dst = a.qq + rowid * D;
+    for (int dd = lane; dd < D; dd += 64) {
+      float r = rintf(__fmul_rn(qbar_s[hg][dd], inv));
+      r = fminf(fmaxf(r, -127.f), 127.f);
+      dst[dd] = (int8_t)(int)r;
+    }
+    if (lane == 0) {
+      a.sq[rowid] = scale;
+      a.abar[rowid] = (float)(s / (double)nrows);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Block scores.  D^T[key][row] = K_q . qbar_q^T on 32x32x32 int8 MFMA (exact int32); a lane
+// owns one (query block, head) row and 16 keys of each 32-key tile, so the block max is
+// in-lane plus one half swap.  Workgroup = 4 waves x 64 rows (256 rows), 32 key blocks.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void est_score_block(EstArgs a, int n_rt, int n_jc) {
+  constexpr int KS = D / 32;
+  constexpr int NT = 2;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  // blockIdx.x = (bg * n_rt + rt) * n_jc + jc, J-chunks of one row tile adjacent
+  const int lin = blockIdx.x;
+  const int jc = lin % n_jc;
+  const int rt = (lin / n_jc) % n_rt;
+  const int bg = lin / (n_jc * n_rt);
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.G;
+  const int rows_total = a.nQB * G;
+  const int R_last = min(rt * 256 + 255, rows_total - 1);
+  const int e_last = min(a.N, (R_last / G + 1) * a.bq) - 1;
+  const int J0 = jc * 32;
+  if (J0 * 64 > e_last) return;
+  const int J_end = min(J0 + 32, e_last / 64 + 1);
+
+  int rowR[NT], e_i[NT], jmax[NT];
+  float thr[NT], sqv[NT];
+  i32x4 qf[NT][KS];
+  const int64_t row_base = (int64_t)bg * rows_total;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int R = rt * 256 + wave * 64 + nt * 32 + l32;
+    rowR[nt] = R;
+    const int Rc = min(R, rows_total - 1);
+    const int iq = Rc / G, hg = Rc % G;
+    e_i[nt] = min(a.N, (iq + 1) * a.bq) - 1;
+    jmax[nt] = R < rows_total ? e_i[nt] / 64 : -1;
+    thr[nt] = a.abar[row_base + Rc] - a.theta[g * G + hg];
+    sqv[nt] = a.sq[row_base + Rc];
+    const int8_t* qp = a.qq + (row_base + Rc) * D + half * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[nt][ks] = *(const i32x4*)(qp + ks * 32);
+  }
+  const int e_min = min(a.N, ((rt * 256 + wave * 64) / G + 1) * a.bq) - 1;
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
+  unsigned int bits[NT] = {0u, 0u};
+
+  for (int J = J0; J < J_end; ++J) {
+    i32x16 acc[2][NT];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (i32x16){};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int8_t* kp = kbase + (int64_t)(J * 64 + mt * 32 + l32) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 kf = *(const i32x4*)(kp + ks * 32);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_i8(kf, qf[nt][ks], acc[mt][nt]);
+      }
+    }
+    const float skv = a.sk[(int64_t)bg * a.nKB + J];
+    const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      int m = INT32_MIN;
+      if (!need_mask) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = max(m, acc[mt][nt][r]);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+            if (key <= e_i[nt] && key < a.N) m = max(m, acc[mt][nt][r]);
+          }
+      }
+      m = max(m, swap_halves_i(m));
+      const bool cand = J <= jmax[nt];
+      float margin = NEG_INF;
+      if (cand && m != INT32_MIN) {
+        const float mult = __fmul_rn(__fmul_rn(sqv[nt], skv), a.c);
+        const float s_hat = __fmul_rn((float)m, mult);
+        margin = s_hat - thr[nt];
+      }
+      for (int o = 1; o < G; o <<= 1) margin = fmaxf(margin, __shfl_xor(margin, o));
+      if (margin >= 0.f) bits[nt] |= 1u << (J - J0);
+      if (a.margins && cand && half == 0 && (rowR[nt] % G) == 0) {
+        const int iq = rowR[nt] / G;
+        a.margins[((int64_t)bg * a.nQB + iq) * a.nKB + J] = margin;
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (half == 0 && rowR[nt] < rows_total && (rowR[nt] % G) == 0) {
+      const int iq = rowR[nt] / G;
+      a.bits[((int64_t)bg * a.nQB + iq) * a.W + jc] = bits[nt];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Stripe scores.  D[row][key] = qbar_q . K_q^T: rows are the A operand, keys the B operand,
+// so a lane owns one key column and 16 rows; one compare per element becomes a wave
+// ballot that holds, per row pair, the keep bits of 32 consecutive columns.
+// Workgroup = 4 waves x 64 rows, 32 key tiles of 64 columns.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void est_score_stripe(EstArgs a, int n_rt, int n_jc) {
+  constexpr int KS = D / 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int lin = blockIdx.x;
+  const int jc = lin % n_jc;
+  const int rt = (lin / n_jc) % n_rt;
+  const int bg = lin / (n_jc * n_rt);
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.G;
+  const int rows_total = a.nQB * G;
+  const int R_last = min(rt * 256 + 255, rows_total - 1);
+  const int e_last = min(a.N, (R_last / G + 1) * a.bq) - 1;
+  const int J0 = jc * 32;
+  if (J0 * 64 > e_last) return;
+  const int J_end = min(J0 + 32, e_last / 64 + 1);
+  const int64_t row_base = (int64_t)bg * a.nQB * G;
+  const int Rw = rt * 256 + wave * 64;                  // first row of this wave
+  if (Rw >= rows_total) return;
+
+  // A operand: pooled query rows Rw + mt*32 + l32
+  i32x4 qf[2][KS];
+  for (int mt = 0; mt < 2; ++mt) {
+    const int Rc = min(Rw + mt * 32 + l32, rows_total - 1);
+    const int8_t* qp = a.qq + (row_base + Rc) * D + half * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[mt][ks] = *(const i32x4*)(qp + ks * 32);
+  }
+  // Per-register row data: register r of m-tile mt holds row Rw + mt*32 + half*4 + 8(r/4) + r%4
+  float thr[2][16], sqv[2][16];
+  int erow[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int R = Rw + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+      const int Rc = min(R, rows_total - 1);
+      const int hg = Rc % G;
+      thr[mt][r] = a.abar[row_base + Rc] - a.theta[g * G + hg];
+      sqv[mt][r] = a.sq[row_base + Rc];
+      erow[mt][r] = R < rows_total ? min(a.N, (Rc / G + 1) * a.bq) - 1 : -1;
+    }
+  const int e_min = min(a.N, (Rw / G + 1) * a.bq) - 1;
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
+  for (int J = J0; J < J_end; ++J) {
+    i32x16 acc[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (i32x16){};
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int8_t* kp = kbase + (int64_t)(J * 64 + nt * 32 + l32) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 kf = *(const i32x4*)(kp + ks * 32);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma_i8(qf[mt][ks], kf, acc[mt][nt]);
+      }
+    }
+    const float skv = a.sk[(int64_t)bg * a.nKB + J];
+    const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int key = J * 64 + nt * 32 + l32;
+      const int wi = J * 2 + nt;                         // bit word of columns [key - l32, +32)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        // register r = 4*ag + bb of this m-tile is row Rw + mt*32 + half*4 + 8*ag + bb
+#pragma unroll
+        for (int ag = 0; ag < 4; ++ag) {
+          float mv[4];
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int r = 4 * ag + bb;
+            const float mult = __fmul_rn(__fmul_rn(sqv[mt][r], skv), a.c);
+            float margin = __fmul_rn((float)acc[mt][nt][r], mult) - thr[mt][r];
+            if ((need_mask && key > erow[mt][r]) || erow[mt][r] < 0) margin = NEG_INF;
+            mv[bb] = margin;
+          }
+          const int Rg = Rw + mt * 32 + 8 * ag;        // first row of this 8-row group
+          if (G <= 4) {
+            // G consecutive rows (same half) form one query block: OR their ballots
+            unsigned long long word = 0ull;
+            float mg = NEG_INF;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              word |= __ballot(mv[bb] >= 0.f);
+              mg = fmaxf(mg, mv[bb]);
+              if (((bb + 1) % G) == 0) {
+                const int b0 = bb + 1 - G;
+                const int R_lo = Rg + b0, R_hi = Rg + 4 + b0;
+                if (lane == 0) {
+                  if (R_lo < rows_total) a.bits[(row_base / G + R_lo / G) * a.W + wi] = (unsigned int)word;
+                  if (R_hi < rows_total) a.bits[(row_base / G + R_hi / G) * a.W + wi] = (unsigned int)(word >> 32);
+                }
+                if (a.margins) {
+                  const int R = Rg + half * 4 + b0;
+                  if (R < rows_total && key <= erow[mt][4 * ag + b0])
+                    a.margins[((int64_t)bg * a.nQB + R / G) * a.N + key] = mg;
+                }
+                word = 0ull;
+                mg = NEG_INF;
+              }
+            }
+          } else {
+            // G == 8: rows Rg .. Rg+7 (both halves) are one query block
+            unsigned long long word = 0ull;
+            float mg = NEG_INF;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              word |= __ballot(mv[bb] >= 0.f);
+              mg = fmaxf(mg, mv[bb]);
+            }
+            mg = fmaxf(mg, swap_halves(mg));
+            if (lane == 0 && Rg < rows_total)
+              a.bits[(row_base / G + Rg / G) * a.W + wi] = (unsigned int)word | (unsigned int)(word >> 32);
+            if (a.margins && half == 0 && Rg < rows_total && key <= erow[mt][4 * ag])
+              a.margins[((int64_t)bg * a.nQB + Rg / G) * a.N + key] = mg;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Compaction: per (b, g, i) row, keep = (bits | forced) & causal candidates, written as
+// ascending indices; `unit` = block_k (block lists) or 1 (stripe lists).
+// ---------------------------------------------------------------------------------------
+static __device__ __forceinline__ unsigned int range_bits(int w, int lo, int hi) {
+  // bits of x in [lo, hi] within word w (x = w*32 + bit)
+  const int base = w * 32;
+  const int a = max(lo - base, 0);
+  const int b = min(hi - base, 31);
+  if (a > b) return 0u;
+  const unsigned int upper = (b == 31) ? 0xFFFFFFFFu : ((1u << (b + 1)) - 1u);
+  const unsigned int lower = (1u << a) - 1u;
+  return upper & ~lower;
+}
+
+__global__ __launch_bounds__(256) void est_compact(EstArgs a, int unit) {
+  const int row = blockIdx.x;
+  const int iq = row % a.nQB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = iq * a.bq;
+  const int e = min(a.N, r0 + a.bq) - 1;
+  const int lo = max(0, r0 - a.local + 1);
+  const int ncand = e / unit + 1;
+  const int nwords = (ncand + 31) / 32;
+  const int sink_last = (a.sink + unit - 1) / unit - 1;      // forced sink candidates [0, sink_last]
+  const int win_lo = lo / unit, win_hi = e / unit;
+  const uint32_t* wrow = a.bits + (int64_t)row * a.W;
+  const int per = (nwords + 255) / 256;
+  const int w0 = tid * per, w1 = min(w0 + per, nwords);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) {
+    unsigned int word = wrow[w] | range_bits(w, 0, sink_last) | range_bits(w, win_lo, win_hi);
+    word &= range_bits(w, 0, ncand - 1);
+    cnt += __popc(word);
+  }
+  // block-wide exclusive scan of cnt
+  __shared__ int wsum[4];
+  int incl = cnt;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = incl - cnt;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  int32_t* out = a.idx + (int64_t)row * a.stride;
+  int pos = base;
+  for (int w = w0; w < w1; ++w) {
+    unsigned int word = wrow[w] | range_bits(w, 0, sink_last) | range_bits(w, win_lo, win_hi);
+    word &= range_bits(w, 0, ncand - 1);
+    while (word) {
+      const int bit = __builtin_ctz(word);
+      word &= word - 1u;
+      if (pos < a.stride) out[pos] = w * 32 + bit;
+      ++pos;
+    }
+  }
+  if (tid == 0) a.counts[row] = total;
+}
+
+// ---------------------------------------------------------------------------------------
+template <int D>
+static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream_t s) {
+  hipLaunchKernelGGL(est_quant_k<D>, dim3(a.nKB, a.Hkv, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(est_anchor_pool<D>, dim3(a.nQB, a.Hkv, a.B), dim3(256), 0, s, a);
+  const int rows_total = a.nQB * a.G;
+  const int n_rt = (rows_total + 255) / 256;
+  const int n_jc = (a.nKB + 31) / 32;
+  const int grid = a.B * a.Hkv * n_rt * n_jc;
+  if (granularity == SA_STRIPE) {
+    hipLaunchKernelGGL(est_score_stripe<D>, dim3(grid), dim3(256), 0, s, a, n_rt, n_jc);
+    hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, 1);
+  } else {
+    hipLaunchKernelGGL(est_score_block<D>, dim3(grid), dim3(256), 0, s, a, n_rt, n_jc);
+    hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, a.bk);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_estimate(const EstArgs& a, int granularity, hipStream_t s) {
+  if (a.D == 64) return launch_estimate_d<64>(a, granularity, s);
+  return launch_estimate_d<128>(a, granularity, s);
+}

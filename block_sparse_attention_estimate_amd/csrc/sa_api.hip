@@ -1,0 +1,307 @@
+// C ABI of libsa: host-side validation, workspace carve-out and kernel launches.
+// Every check runs before the first launch; on error nothing is launched.
+#include <math.h>
+#include <string.h>
+
+#include "sa_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+float resolve_scale(float s, int d) {
+  if (s > 0.f) return s;
+  return (float)(1.0 / sqrt((double)d));
+}
+
+sa_status check_shape_common(const sa_shape* s) {
+  if (!s) return SA_ERR_NULL;
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->seq_q < 1 || s->seq_k < 1)
+    return SA_ERR_SHAPE;
+  if (s->n_q_heads % s->n_kv_heads != 0) return SA_ERR_SHAPE;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (s->head_dim != 64 && s->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (s->n_q_heads > SA_MAX_Q_HEADS) return SA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+bool strides_ok(const int64_t st[3]) {
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || (st[i] % 8) != 0) return false;
+  return true;
+}
+
+sa_status check_prefill_shape(const sa_shape* s) {
+  sa_status st = check_shape_common(s);
+  if (st != SA_OK) return st;
+  if (s->seq_q != s->seq_k) return SA_ERR_SHAPE;
+  if (s->seq_q >= (1 << 30)) return SA_ERR_UNSUPPORTED;
+  if (!strides_ok(s->q_stride) || !strides_ok(s->k_stride) || !strides_ok(s->v_stride) ||
+      !strides_ok(s->o_stride))
+    return SA_ERR_SHAPE;
+  // head and token strides must at least cover one row of head_dim elements
+  if (s->q_stride[2] < s->head_dim || s->k_stride[2] < s->head_dim ||
+      s->v_stride[2] < s->head_dim || s->o_stride[2] < s->head_dim)
+    return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+sa_status check_sparse_params(const sa_shape* s, const sa_sparse_params* p, bool need_theta) {
+  if (!p) return SA_ERR_NULL;
+  if (need_theta && !p->theta) return SA_ERR_NULL;
+  if (p->granularity != SA_BLOCK && p->granularity != SA_STRIPE) return SA_ERR_PARAM;
+  if (p->sink_tokens < 0 || p->local_tokens < 1) return SA_ERR_PARAM;
+  if (p->block_q != 64 && p->block_q != 128) return SA_ERR_UNSUPPORTED;
+  if (p->block_k != 64) return SA_ERR_UNSUPPORTED;
+  if (isnan(p->softmax_scale) || isinf(p->softmax_scale)) return SA_ERR_PARAM;
+  if (need_theta)
+    for (int h = 0; h < s->n_q_heads; ++h)
+      if (isnan(p->theta[h])) return SA_ERR_PARAM;
+  return SA_OK;
+}
+
+struct EstLayout {
+  size_t kq, sk, qq, sq, abar, bits, total;
+  int W;
+};
+
+EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p) {
+  EstLayout L{};
+  const int N = s->seq_q, D = s->head_dim, B = s->batch, Hkv = s->n_kv_heads, Hq = s->n_q_heads;
+  const int nQB = ceil_div(N, p->block_q), nKB = ceil_div(N, p->block_k);
+  // stripe bit rows cover the padded key range (whole 64-key tiles)
+  const int ncand = p->granularity == SA_STRIPE ? nKB * 64 : nKB;
+  L.W = ceil_div(ncand, 32);
+  size_t off = 0;
+  L.kq = off;   off = align_up(off + (size_t)B * Hkv * nKB * 64 * D);
+  L.sk = off;   off = align_up(off + (size_t)B * Hkv * nKB * sizeof(float));
+  L.qq = off;   off = align_up(off + (size_t)B * Hq * nQB * D);
+  L.sq = off;   off = align_up(off + (size_t)B * Hq * nQB * sizeof(float));
+  L.abar = off; off = align_up(off + (size_t)B * Hq * nQB * sizeof(float));
+  L.bits = off; off = align_up(off + (size_t)B * Hkv * nQB * L.W * sizeof(uint32_t));
+  L.total = off;
+  return L;
+}
+
+struct DecLayout {
+  size_t scores, selected, partial, total;
+};
+
+int decode_splits(const sa_shape* s, const sa_decode_params* p) {
+  if (p->n_splits > 0) return p->n_splits;
+  // enough workgroups to cover the chip several times over
+  int n = 1;
+  while ((int64_t)s->batch * s->n_kv_heads * n < 2048 && n < 64) n <<= 1;
+  return n;
+}
+
+DecLayout dec_layout(const sa_shape* s, const sa_decode_params* p) {
+  DecLayout L{};
+  const int nKB = ceil_div(s->seq_k, p->block_k);
+  const int ns = decode_splits(s, p);
+  size_t off = 0;
+  L.scores = off;   off = align_up(off + (size_t)s->batch * s->n_kv_heads * nKB * sizeof(float));
+  L.selected = off; off = align_up(off + (size_t)s->batch * s->n_kv_heads * p->top_k_blocks * sizeof(int32_t));
+  L.partial = off;  off = align_up(off + (size_t)s->batch * s->n_q_heads * ns * (s->head_dim + 2) * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+sa_status check_decode(const sa_shape* s, const sa_decode_params* p) {
+  sa_status st = check_shape_common(s);
+  if (st != SA_OK) return st;
+  if (!p) return SA_ERR_NULL;
+  if (s->seq_q != 1) return SA_ERR_SHAPE;
+  if (p->block_k < 1 || p->top_k_blocks < 1 || p->sink_tokens < 0 || p->local_tokens < 1 ||
+      p->n_splits < 0)
+    return SA_ERR_PARAM;
+  if (isnan(p->softmax_scale) || isinf(p->softmax_scale)) return SA_ERR_PARAM;
+  if (ceil_div(s->seq_k, p->block_k) > 8192) return SA_ERR_UNSUPPORTED;
+  if (!strides_ok(s->q_stride) || !strides_ok(s->k_stride) || !strides_ok(s->v_stride) ||
+      !strides_ok(s->o_stride))
+    return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_status_string(sa_status st) {
+  switch (st) {
+    case SA_OK: return "ok";
+    case SA_ERR_NULL: return "null pointer";
+    case SA_ERR_SHAPE: return "invalid shape, stride or alignment";
+    case SA_ERR_PARAM: return "invalid parameter";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_CAPACITY: return "list capacity too small";
+    case SA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+size_t sa_workspace_size(int op, const sa_shape* shape, const void* params) {
+  if (!shape || !params) return 0;
+  if (op == SA_OP_ESTIMATE) {
+    const sa_sparse_params* p = (const sa_sparse_params*)params;
+    if (check_prefill_shape(shape) != SA_OK || check_sparse_params(shape, p, true) != SA_OK) return 0;
+    return est_layout(shape, p).total;
+  }
+  if (op == SA_OP_DECODE) {
+    const sa_decode_params* p = (const sa_decode_params*)params;
+    if (check_decode(shape, p) != SA_OK) return 0;
+    return dec_layout(shape, p).total;
+  }
+  return 0;
+}
+
+sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params, const void* q,
+                           const void* k, const sa_lists* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  sa_status st = check_prefill_shape(shape);
+  if (st != SA_OK) return st;
+  st = check_sparse_params(shape, params, true);
+  if (st != SA_OK) return st;
+  if (!q || !k || !out || !out->counts || !out->idx) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k)) return SA_ERR_SHAPE;
+  const int N = shape->seq_q;
+  const int nKB = ceil_div(N, params->block_k), nQB = ceil_div(N, params->block_q);
+  if (out->stride < 1) return SA_ERR_CAPACITY;
+  if (params->granularity == SA_BLOCK && out->stride < nKB) return SA_ERR_CAPACITY;
+  const EstLayout L = est_layout(shape, params);
+  if (!ws) return SA_ERR_WORKSPACE;
+  if (ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0) return SA_ERR_WORKSPACE;
+
+  EstArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.qs0 = shape->q_stride[0]; a.qs1 = shape->q_stride[1]; a.qs2 = shape->q_stride[2];
+  a.ks0 = shape->k_stride[0]; a.ks1 = shape->k_stride[1]; a.ks2 = shape->k_stride[2];
+  a.B = shape->batch; a.Hq = shape->n_q_heads; a.Hkv = shape->n_kv_heads;
+  a.G = a.Hq / a.Hkv; a.D = shape->head_dim; a.N = N;
+  a.bq = params->block_q; a.bk = params->block_k;
+  a.sink = params->sink_tokens; a.local = params->local_tokens;
+  a.nQB = nQB; a.nKB = nKB;
+  a.c = resolve_scale(params->softmax_scale, a.D);
+  char* base = (char*)ws;
+  a.kq = (int8_t*)(base + L.kq);
+  a.sk = (float*)(base + L.sk);
+  a.qq = (int8_t*)(base + L.qq);
+  a.sq = (float*)(base + L.sq);
+  a.abar = (float*)(base + L.abar);
+  a.bits = (uint32_t*)(base + L.bits);
+  a.W = L.W;
+  a.counts = out->counts;
+  a.idx = out->idx;
+  a.stride = out->stride;
+  a.margins = out->margins;
+  for (int h = 0; h < a.Hq; ++h) a.theta[h] = params->theta[h];
+  if (launch_estimate(a, params->granularity, stream) != hipSuccess) return SA_ERR_DEVICE;
+  return SA_OK;
+}
+
+sa_status sa_sparse_prefill(const sa_shape* shape, const sa_sparse_params* params, const void* q,
+                            const void* k, const void* v, const sa_lists* lists, void* o,
+                            float* lse, hipStream_t stream) {
+  sa_status st = check_prefill_shape(shape);
+  if (st != SA_OK) return st;
+  st = check_sparse_params(shape, params, false);
+  if (st != SA_OK) return st;
+  if (!q || !k || !v || !o || !lists || !lists->counts || !lists->idx) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SA_ERR_SHAPE;
+  const int N = shape->seq_q;
+  const int nKB = ceil_div(N, params->block_k), nQB = ceil_div(N, params->block_q);
+  if (lists->stride < 1) return SA_ERR_CAPACITY;
+  if (params->granularity == SA_BLOCK && lists->stride < nKB) return SA_ERR_CAPACITY;
+
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o; a.lse = lse;
+  a.qs0 = shape->q_stride[0]; a.qs1 = shape->q_stride[1]; a.qs2 = shape->q_stride[2];
+  a.ks0 = shape->k_stride[0]; a.ks1 = shape->k_stride[1]; a.ks2 = shape->k_stride[2];
+  a.vs0 = shape->v_stride[0]; a.vs1 = shape->v_stride[1]; a.vs2 = shape->v_stride[2];
+  a.os0 = shape->o_stride[0]; a.os1 = shape->o_stride[1]; a.os2 = shape->o_stride[2];
+  a.counts = lists->counts; a.idx = lists->idx; a.stride = lists->stride;
+  a.B = shape->batch; a.Hq = shape->n_q_heads; a.Hkv = shape->n_kv_heads;
+  a.G = a.Hq / a.Hkv; a.N = N; a.bq = params->block_q; a.nQB = nQB;
+  a.tpb = params->block_q / 64;
+  a.scale_log2 = resolve_scale(params->softmax_scale, shape->head_dim) * 1.4426950408889634f;
+  if (launch_prefill(a, shape->head_dim, params->granularity, stream) != hipSuccess)
+    return SA_ERR_DEVICE;
+  return SA_OK;
+}
+
+static void fill_dec_args(DecArgs& a, const sa_shape* s, int block_k) {
+  memset(&a, 0, sizeof(a));
+  a.qs0 = s->q_stride[0]; a.qs2 = s->q_stride[2];
+  a.ks0 = s->k_stride[0]; a.ks1 = s->k_stride[1]; a.ks2 = s->k_stride[2];
+  a.vs0 = s->v_stride[0]; a.vs1 = s->v_stride[1]; a.vs2 = s->v_stride[2];
+  a.os0 = s->o_stride[0]; a.os2 = s->o_stride[2];
+  a.B = s->batch; a.Hq = s->n_q_heads; a.Hkv = s->n_kv_heads; a.G = a.Hq / a.Hkv;
+  a.D = s->head_dim; a.L = s->seq_k; a.bk = block_k;
+  a.nKB = ceil_div(s->seq_k, block_k);
+}
+
+sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k, const void* k_cache,
+                                 const int32_t* cache_len, void* k_summary, hipStream_t stream) {
+  sa_status st = check_shape_common(shape);
+  if (st != SA_OK) return st;
+  if (!k_cache || !cache_len || !k_summary) return SA_ERR_NULL;
+  if (block_k < 1) return SA_ERR_PARAM;
+  if (!strides_ok(shape->k_stride)) return SA_ERR_SHAPE;
+  if (!aligned16(k_cache) || !aligned16(k_summary)) return SA_ERR_SHAPE;
+  DecArgs a;
+  fill_dec_args(a, shape, block_k);
+  a.kc = (const uint16_t*)k_cache;
+  a.cache_len = cache_len;
+  a.ksum = (const uint16_t*)k_summary;
+  if (launch_block_summary(a, stream) != hipSuccess) return SA_ERR_DEVICE;
+  return SA_OK;
+}
+
+sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params, const void* q,
+                           const void* k_cache, const void* v_cache, const void* k_summary,
+                           const int32_t* cache_len, void* o, float* lse, int32_t* selected,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  sa_status st = check_decode(shape, params);
+  if (st != SA_OK) return st;
+  if (!q || !k_cache || !v_cache || !k_summary || !cache_len || !o) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_summary) ||
+      !aligned16(o))
+    return SA_ERR_SHAPE;
+  const DecLayout L = dec_layout(shape, params);
+  if (!ws) return SA_ERR_WORKSPACE;
+  if (ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0) return SA_ERR_WORKSPACE;
+  DecArgs a;
+  fill_dec_args(a, shape, params->block_k);
+  char* base = (char*)ws;
+  a.q = (const uint16_t*)q;
+  a.kc = (const uint16_t*)k_cache;
+  a.vc = (const uint16_t*)v_cache;
+  a.ksum = (const uint16_t*)k_summary;
+  a.cache_len = cache_len;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.scores = (float*)(base + L.scores);
+  a.selected = selected ? selected : (int32_t*)(base + L.selected);
+  a.partial = (float*)(base + L.partial);
+  a.top_k = params->top_k_blocks;
+  a.sink = params->sink_tokens;
+  a.local = params->local_tokens;
+  a.n_splits = decode_splits(shape, params);
+  a.c = resolve_scale(params->softmax_scale, shape->head_dim);
+  if (launch_decode(a, stream) != hipSuccess) return SA_ERR_DEVICE;
+  return SA_OK;
+}
+
+}  // extern "C"

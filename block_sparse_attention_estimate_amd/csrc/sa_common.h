@@ -1,0 +1,75 @@
+// Shared device types and small helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define SA_DEV static __device__ __forceinline__
+
+// 32x32x16 bf16 MFMA: A lane l holds A[l%32][(l/32)*8 .. +8]; B lane l holds
+// B[(l/32)*8 .. +8][l%32]; C lane l holds C[(l/32)*4 + 8*(r/4) + r%4][l%32], r = 0..15.
+SA_DEV f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x32 int8 MFMA, same lane pattern with 16 int8 (4 dwords) per lane along k.
+SA_DEV i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+SA_DEV float bf16_bits_to_float(unsigned short u) {
+  return __uint_as_float(((unsigned int)u) << 16);
+}
+
+SA_DEV double bf16_bits_to_double(unsigned short u) {
+  return (double)__uint_as_float(((unsigned int)u) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+SA_DEV unsigned short float_to_bf16_bits(float f) {
+  unsigned int u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+SA_DEV float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+SA_DEV double wave_sum_d(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+SA_DEV int wave_sum_i(int v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Exchange a value with lane ^ 32 (the other half of a wave64).
+SA_DEV float swap_halves(float v) {
+  return __shfl_xor(v, 32);
+}
+
+SA_DEV int swap_halves_i(int v) {
+  return __shfl_xor(v, 32);
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger unsigned).
+SA_DEV unsigned int float_order_key(float f) {
+  unsigned int u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}

@@ -1,0 +1,66 @@
+// Host-side launch interface between the C ABI (sa_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa.h"
+
+// Everything the estimation kernels read, passed by value (theta included).
+struct EstArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2;
+  int B, Hq, Hkv, G, D, N, bq, bk, sink, local, nQB, nKB;
+  float c;                 // softmax scale, fp32
+  // workspace carve-out
+  int8_t* kq;              // [B, Hkv, nKB * bk, D] int8 keys
+  float* sk;               // [B, Hkv, nKB] key-tile scales
+  int8_t* qq;              // [B, Hkv, nQB, G, D] int8 pooled queries
+  float* sq;               // [B, Hkv, nQB, G] pooled-query scales
+  float* abar;             // [B, Hkv, nQB, G] block-averaged anchors
+  uint32_t* bits;          // [B, Hkv, nQB, W] keep bits
+  int W;                   // words per bit row
+  // outputs
+  int32_t* counts;
+  int32_t* idx;
+  int32_t stride;
+  float* margins;
+  float theta[SA_MAX_Q_HEADS];
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
+  const int32_t* counts;
+  const int32_t* idx;
+  int stride;
+  int B, Hq, Hkv, G, N, bq, nQB, tpb, n_hp;
+  float scale_log2;
+  int total;
+};
+
+struct DecArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const uint16_t* ksum;
+  const int32_t* cache_len;
+  uint16_t* o;
+  float* lse;
+  int32_t* selected;
+  float* scores;           // [B, Hkv, nKBmax]
+  float* partial;          // [B, Hq, n_splits, D + 2]
+  int64_t qs0, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os2;
+  int B, Hq, Hkv, G, D, L, bk, nKB, top_k, sink, local, n_splits;
+  float c;
+};
+
+hipError_t launch_estimate(const EstArgs& a, int granularity, hipStream_t s);
+hipError_t launch_prefill(const AttnArgs& a, int D, int granularity, hipStream_t s);
+hipError_t launch_block_summary(const DecArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecArgs& a, hipStream_t s);

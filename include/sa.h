@@ -1,0 +1,173 @@
+/*
+ * sa.h -- C ABI of the MI355X (gfx950) sparse-attention library (libsa.so).
+ *
+ * Training-free block/stripe-sparse attention for long-context prefill, and top-K
+ * block-sparse decode.  The operations follow the review pages:
+ *
+ *  - AnchorAttention: Difference-Aware Sparse Attention with Stripe Granularity
+ *    (arXiv 2505.23520): Eq. (1) anchor = max score over the initial and local key regions;
+ *    Eq. (2) mask = I(avgpool(x_a) - avgpool(Q) K^T / sqrt(d) <= theta); Eq. (3) the index
+ *    set I per query block; "Core claim": stripe granularity and discrete K/V loading.
+ *  - SALE: Low-bit Estimation for Efficient Sparse Attention in Long-context LLM Prefilling
+ *    (arXiv 2505.24179): low-precision Q.K^T estimate, sink (32 tokens) and local (256
+ *    tokens) areas, block skipping, log-domain compare; drop-in replacement of the
+ *    attention module (inputs Q, K, V; output O).
+ *  - SpotAttention: Plug-In Block-Sparse Routing for Pretrained Long-Context Transformers
+ *    (arXiv 2606.22874), Figure 2: decode attends to a sink prefix, a recency window and the
+ *    top-scoring blocks, gathered from the cache.
+ *  - KVpop (arXiv 2607.05061), referee minor comment 4: query heads sharing a KV head are
+ *    aggregated with max.
+ *
+ * Conventions shared by every entry point
+ *  - Memory: every tensor pointer is DEVICE memory owned by the caller (the library never
+ *    allocates or frees on these paths and keeps no mutable global state; calls on
+ *    different streams are independent).  `sa_shape`, `sa_sparse_params`,
+ *    `sa_decode_params` and `sa_lists` themselves are HOST structs read during the call.
+ *  - Layout: Q, K, V, O are bf16 with head_dim contiguous; the (batch, token, head)
+ *    strides are given in ELEMENTS and must be multiples of 8 (16-byte rows); base
+ *    pointers must be 16-byte aligned.  Query head h uses KV head h / (Hq / Hkv).
+ *  - Execution: asynchronous on `stream`.  All validation happens on the host before any
+ *    launch; on an error nothing is launched and no output is touched.
+ *  - Errors: returned as `sa_status`; no exception or abort crosses the ABI.  A HIP launch
+ *    failure is reported as SA_ERR_DEVICE.
+ *  - Supported (v1): head_dim in {64, 128}; block_q in {64, 128}; block_k == 64;
+ *    n_q_heads <= 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8}.
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,         /* a required pointer is NULL                                   */
+  SA_ERR_SHAPE = 2,        /* inconsistent sizes, strides or alignment                     */
+  SA_ERR_PARAM = 3,        /* bad parameter value (theta NaN, negative sink, ...)          */
+  SA_ERR_UNSUPPORTED = 4,  /* valid but not implemented (head_dim, block sizes, group size)*/
+  SA_ERR_CAPACITY = 5,     /* list stride too small for a block list                       */
+  SA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than sa_workspace_size()           */
+  SA_ERR_DEVICE = 7        /* a HIP call or kernel launch failed                           */
+} sa_status;
+
+enum { SA_BLOCK = 0, SA_STRIPE = 1 };
+enum { SA_OP_ESTIMATE = 0, SA_OP_PREFILL = 1, SA_OP_DECODE = 2 };
+
+#define SA_MAX_Q_HEADS 128
+
+/* Problem statement: batch, heads, head_dim, query/key lengths and element strides of
+ * the (batch, token, head) dimensions of each tensor.  For decode, seq_q is 1 and seq_k is
+ * the cache capacity (tokens per sequence in the cache buffers); q/o strides use the token
+ * stride slot unused. */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim, seq_q, seq_k;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+} sa_shape;
+
+/* Sparse prefill parameters.  `theta` (HOST array [n_q_heads], logit units) is the Eq. (2)
+ * threshold per query head: +inf keeps every causal block (dense causal attention), -inf
+ * keeps only the forced sink and local blocks; NaN is rejected.  softmax_scale <= 0 means
+ * 1/sqrt(head_dim) (rounded once to fp32).  sink_tokens >= 0 and local_tokens >= 1. */
+typedef struct {
+  int32_t block_q, block_k, sink_tokens, local_tokens;
+  int32_t granularity;            /* SA_BLOCK or SA_STRIPE */
+  const float* theta;             /* host [n_q_heads] */
+  float softmax_scale;
+} sa_sparse_params;
+
+/* Per-row kept lists (the index set I of Eq. (3)), one row per (batch, KV head, query
+ * block), rows ordered (b, g, i).  Row r holds counts[r] ascending key-block ids (block
+ * granularity) or key-column ids (stripe granularity) in idx[r*stride ...].  Forced sink and
+ * local entries are included.  counts always receives the true count; entries past
+ * `stride` are dropped (stripe lists only -- block lists require stride >= ceil(seq_k /
+ * block_k)), so a caller detects stripe overflow as counts[r] > stride after the call.
+ * margins (nullable, DEVICE float [rows * n_cand], n_cand = ceil(seq_k/block_k) for blocks or
+ * seq_k for stripes) receives, for each causal candidate, max over the group's heads of
+ * (score - (anchor - theta)); entries of non-candidates are left untouched. */
+typedef struct {
+  int32_t* counts;                /* device [B * Hkv * nQB]           */
+  int32_t* idx;                   /* device [B * Hkv * nQB * stride]  */
+  int32_t stride;
+  float* margins;                 /* device, nullable                 */
+} sa_lists;
+
+/* Decode parameters: key-block size of the summaries and of the selection, number of
+ * selected blocks K (forced blocks count toward K), sink and local (recency) sizes in
+ * tokens, number of split-K partitions (0 = library choice), softmax scale as above. */
+typedef struct {
+  int32_t block_k, top_k_blocks, sink_tokens, local_tokens, n_splits;
+  float softmax_scale;
+} sa_decode_params;
+
+/* Workspace bytes an operation needs (op = SA_OP_ESTIMATE with sa_sparse_params, or
+ * SA_OP_DECODE with sa_decode_params; SA_OP_PREFILL needs none).  Returns 0 for an
+ * invalid request. */
+size_t sa_workspace_size(int op, const sa_shape* shape, const void* params);
+
+/* Estimation pass (AnchorAttention Eq. (1)-(3); SALE low-precision estimate):
+ *  1. anchor x_a[r] = max over keys j <= r with j < sink or j > r - local of
+ *     c * q_r . k_j (bf16 MFMA, fp32 accumulate), averaged over the query block;
+ *  2. pooled query avgpool(Q) (fp64 sum, one rounding to fp32, fp32 divide), quantised to
+ *     int8 with one symmetric scale per vector; keys quantised per block_k-key tile;
+ *  3. exact int32 score D = qbar_q . k_q; s = fp32(D) * fp32(fp32(s_q * s_k) * c);
+ *     block granularity takes the max over the block's causal columns;
+ *  4. keep when max over the group's heads of s - (anchor - theta_h) >= 0 (ties keep), or
+ *     when the block/column is forced (overlaps [0, sink) or the query block's local
+ *     windows); compact into ascending lists.
+ * q: device bf16 [B, seq, Hq, d]; k: device bf16 [B, seq, Hkv, d]; seq_q == seq_k.
+ * ws: device scratch of at least sa_workspace_size(SA_OP_ESTIMATE, ...) bytes, 256-byte
+ * aligned, owned by the caller, may be reused after the stream passes this call. */
+sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params,
+                           const void* q, const void* k, const sa_lists* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Computation pass (SALE "Computation-Pass"; AnchorAttention discrete K/V loading): for
+ * every query row r of head h in query block i, attention over the tokens named by the
+ * list of (b, h / (Hq/Hkv), i) with j <= r, online softmax on bf16 MFMA.  Block lists name
+ * key blocks; stripe lists name key columns (gathered row by row).  o: device bf16
+ * [B, seq, Hq, d] (o_stride); lse: nullable device fp32 [B, Hq, seq], natural log.  A row
+ * with no visible key gets O = 0 and LSE = -inf.  Only the first min(counts, stride)
+ * entries of a row are read. */
+sa_status sa_sparse_prefill(const sa_shape* shape, const sa_sparse_params* params /* theta unused, may be NULL */,
+                            const void* q, const void* k, const void* v,
+                            const sa_lists* lists, void* o, float* lse, hipStream_t stream);
+
+/* Block summaries for decode (SALE "The reading": one representative per key block):
+ * kbar[b, J, g, :] = mean of the cached keys of block J (fp64 sum and divide, rounded to
+ * fp32 then to bf16); blocks at or past cache_len[b] are written as zeros.
+ * k_cache: device bf16 [B, seq_k, Hkv, d] (k_stride); cache_len: device int32 [B] with
+ * cache_len[b] in [1, seq_k] (values outside are clamped on the device); k_summary:
+ * device bf16 [B, ceil(seq_k/block_k), Hkv, d],
+ * contiguous. */
+sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k,
+                                 const void* k_cache, const int32_t* cache_len,
+                                 void* k_summary, hipStream_t stream);
+
+/* Sparse decode (SpotAttention Figure 2 with a training-free block score): per (b, g)
+ * score every block J < ceil(cache_len[b]/block_k) by max over the group's heads of
+ * c * q_h . kbar_J; select the forced blocks (overlapping [0, sink) or
+ * [cache_len-local, cache_len-1]) plus the highest-scoring others (ties to the lower
+ * block) up to top_k_blocks; then split-K attention of the single query (position
+ * cache_len-1, seeing every cached token) over the selected blocks and an LSE merge.
+ * q: device bf16 [B, Hq, d] (q_stride[0] = batch stride, q_stride[2] = head stride);
+ * o: device bf16 [B, Hq, d] likewise (o_stride); lse: nullable device fp32 [B, Hq];
+ * selected: nullable device int32 [B, Hkv, top_k_blocks], ascending, padded with -1.
+ * ws: at least sa_workspace_size(SA_OP_DECODE, ...) bytes. */
+sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params,
+                           const void* q, const void* k_cache, const void* v_cache,
+                           const void* k_summary, const int32_t* cache_len,
+                           void* o, float* lse, int32_t* selected,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* sa_status_string(sa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SA_H_ */

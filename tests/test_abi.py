@@ -1,0 +1,129 @@
+"""The C ABI library loads, exports every entry point include/sa.h declares, and rejects
+invalid calls on the host before any launch (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+from block_sparse_attention_estimate_amd import _lib  # noqa: E402
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libsa.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(sa_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        assert lib.sa_status_string(st)
+    assert lib.sa_status_string(0) == b"ok"
+
+
+def _shape(B=1, Hq=4, Hkv=1, D=128, N=256):
+    s = _lib.SaShape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.seq_q, s.seq_k = B, Hq, Hkv, D, N, N
+    s.q_stride[:] = (N * Hq * D, Hq * D, D)
+    s.k_stride[:] = (N * Hkv * D, Hkv * D, D)
+    s.v_stride[:] = (N * Hkv * D, Hkv * D, D)
+    s.o_stride[:] = (N * Hq * D, Hq * D, D)
+    return s
+
+
+def _params(theta, Hq=4, bq=128, bk=64, gran=0):
+    p = _lib.SaSparseParams()
+    p.block_q, p.block_k, p.sink_tokens, p.local_tokens, p.granularity = bq, bk, 32, 256, gran
+    arr = (ctypes.c_float * Hq)(*([theta] * Hq))
+    p.theta = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    p.softmax_scale = 0.0
+    return p, arr
+
+
+FAKE = 0x7F0000000000   # never dereferenced: every call below fails validation first
+
+
+def _est(lib, s, p, ws_bytes=0, stride=4, counts=FAKE, idx=FAKE, ws=FAKE, q=FAKE, k=FAKE):
+    ls = _lib.SaLists()
+    ls.counts, ls.idx, ls.stride, ls.margins = counts, idx, stride, None
+    return lib.sa_estimate_mask(ctypes.byref(s), ctypes.byref(p), q, k, ctypes.byref(ls), ws,
+                                ws_bytes, None)
+
+
+def test_validation_codes(lib):
+    s = _shape()
+    p, keep = _params(4.0)
+    need = lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(p))
+    assert need > 256 * 1024 // 8
+    assert _est(lib, s, p, q=None) == _lib.SA_ERR_NULL
+    assert _est(lib, s, p, stride=3) == _lib.SA_ERR_CAPACITY          # 4 key blocks
+    assert _est(lib, s, p, ws_bytes=need - 1) == _lib.SA_ERR_WORKSPACE
+    assert _est(lib, s, p, ws=None, ws_bytes=need) == _lib.SA_ERR_WORKSPACE
+    assert _est(lib, s, p, q=FAKE + 8, ws_bytes=need) == _lib.SA_ERR_SHAPE   # misaligned
+    pn, keep2 = _params(float("nan"))
+    assert _est(lib, s, pn, ws_bytes=need) == _lib.SA_ERR_PARAM
+    pu, keep3 = _params(4.0, bk=32)
+    assert _est(lib, s, pu, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
+    pq, keep4 = _params(4.0, bq=96)
+    assert _est(lib, s, pq, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
+    bad = _shape(Hq=6, Hkv=4)
+    assert _est(lib, bad, p, ws_bytes=need) == _lib.SA_ERR_SHAPE
+    d96 = _shape(D=96)
+    assert _est(lib, d96, p, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
+    g3 = _shape(Hq=3, Hkv=1)
+    p3, keep5 = _params(4.0, Hq=3)
+    assert _est(lib, g3, p3, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
+    st = _shape()
+    st.q_stride[1] = 4 * 128 + 4     # not a multiple of 8 elements
+    assert _est(lib, st, p, ws_bytes=need) == _lib.SA_ERR_SHAPE
+    neq = _shape()
+    neq.seq_k = 200
+    assert _est(lib, neq, p, ws_bytes=need) == _lib.SA_ERR_SHAPE
+    # prefill validation
+    ls = _lib.SaLists()
+    ls.counts, ls.idx, ls.stride, ls.margins = FAKE, FAKE, 3, None
+    assert lib.sa_sparse_prefill(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE,
+                                 ctypes.byref(ls), FAKE, None, None) == _lib.SA_ERR_CAPACITY
+    ls.stride = 4
+    assert lib.sa_sparse_prefill(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, None,
+                                 ctypes.byref(ls), FAKE, None, None) == _lib.SA_ERR_NULL
+    # decode validation
+    ds = _shape(B=2, N=1000)
+    ds.seq_q = 1
+    dp = _lib.SaDecodeParams()
+    dp.block_k, dp.top_k_blocks, dp.sink_tokens, dp.local_tokens, dp.n_splits = 64, 8, 32, 256, 0
+    dneed = lib.sa_workspace_size(_lib.SA_OP_DECODE, ctypes.byref(ds), ctypes.byref(dp))
+    assert dneed > 0
+    args = [ctypes.byref(ds), ctypes.byref(dp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None]
+    assert lib.sa_sparse_decode(*args, FAKE, dneed - 1, None) == _lib.SA_ERR_WORKSPACE
+    dp.top_k_blocks = 0
+    assert lib.sa_sparse_decode(*args, FAKE, dneed, None) == _lib.SA_ERR_PARAM
+    dp.top_k_blocks = 8
+    ds.seq_q = 2
+    assert lib.sa_sparse_decode(*args, FAKE, dneed, None) == _lib.SA_ERR_SHAPE
+    ds.seq_q = 1
+    assert lib.sa_build_block_summary(ctypes.byref(ds), 0, FAKE, FAKE, FAKE, None) == _lib.SA_ERR_PARAM
+    assert lib.sa_build_block_summary(ctypes.byref(ds), 64, None, FAKE, FAKE, None) == _lib.SA_ERR_NULL
+    assert lib.sa_workspace_size(_lib.SA_OP_PREFILL, ctypes.byref(s), ctypes.byref(p)) == 0

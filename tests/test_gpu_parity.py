@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle on seeded inputs.
+
+Sizes here run in seconds on the oracle yet span several tiles and a ragged tail; the
+full-size workloads are in test_gpu_fullsize.py.  Bars: kept lists bit-exact except
+entries whose oracle margin lies within 1e-3 of the threshold; attention output under the
+oracle's lists within max-abs 2e-2 and mean-abs 2e-3 of the fp64 oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import (compare_lists, compare_outputs, log, lists_from_ref, oracle_estimate_for,
+                     to_dev, upload_lists)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sa.load_library()
+    return torch.device("cuda:0")
+
+
+def _run_prefill_case(dev, x, theta, *, check_attention=True, stride=None):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    B, N, Hq, D = x.q.shape
+    Hkv = x.k.shape[2]
+    log(f"case {x.name} N={N} Hq={Hq} Hkv={Hkv} d={D} gran={x.granularity} theta={list(np.unique(theta))}")
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    lists = sa.estimate_mask(q, k, theta, granularity=x.granularity, margins=True, stride=stride,
+                             **kw)
+    torch.cuda.synchronize()
+    ref = oracle_estimate_for(x, theta)
+    rows, entries, flips = compare_lists(lists, ref)
+    # margins agree with the oracle's within the band on every candidate
+    mg = lists.margins.cpu().numpy()
+    worst = 0.0
+    for (b, g, i), r in ref.items():
+        m_ref = r["margin"]
+        m_gpu = mg[b, g, i, :m_ref.size]
+        fin = np.isfinite(m_ref)
+        assert np.array_equal(np.isfinite(m_gpu), fin)
+        if fin.any():
+            worst = max(worst, float(np.abs(m_gpu[fin] - m_ref[fin]).max()))
+    assert worst < 1e-3, worst
+    log(f"  lists ok: rows={rows} entries={entries} ambiguous flips={flips} max|dmargin|={worst:.1e}")
+    if not check_attention:
+        return
+    nqb = -(-N // x.block_q)
+    st = lists.stride
+    dl = upload_lists(ref, (B, Hkv, nqb), dev, x.granularity, st)
+    o, lse = sa.sparse_prefill(q, k, v, dl, **kw)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_all(x.q, x.k, x.v, lists_from_ref(ref), block_q=x.block_q,
+                                  block_k=x.block_k, granularity=x.granularity)
+    mx, mean, lmax = compare_outputs(o, lse, O, LSE)
+    log(f"  attention ok: max|dO|={mx:.2e} mean={mean:.2e} max|dLSE|={lmax:.2e}")
+
+
+def test_tiny_workload_and_theta_sweep(dev):
+    x = synth.make_prefill("tiny_4k")
+    for th in [4.0, 1.5, 2.0, 2.5, np.inf, -np.inf]:
+        _run_prefill_case(dev, x, np.full(1, th, np.float32), check_attention=th in (4.0, 2.5, -np.inf))
+
+
+@pytest.mark.parametrize("seq,hq,hkv,d,bq", [(4000, 8, 2, 128, 128), (1500, 16, 2, 128, 128),
+                                             (1000, 4, 2, 64, 64), (777, 2, 2, 128, 128),
+                                             (2100, 4, 1, 64, 128)])
+def test_llama_recipe_reduced(dev, seq, hq, hkv, d, bq):
+    x = synth.make_prefill("llama8b_32k", seq=seq, hq=hq, hkv=hkv, head_dim=d)
+    x.block_q = bq
+    grp = hq // hkv
+    theta = np.repeat(np.array([2.0, 3.0, 4.0, 6.0] * 8, np.float32)[:hkv], grp)
+    _run_prefill_case(dev, x, theta)
+
+
+def test_edge_lengths(dev):
+    for seq in [1, 63, 64, 65, 129, 200]:
+        x = synth.make_prefill("llama8b_32k", seq=seq, hq=4, hkv=1)
+        _run_prefill_case(dev, x, np.full(4, 3.0, np.float32))
+
+
+@pytest.mark.parametrize("seq,theta", [(3000, 3.0), (2500, 5.0)])
+def test_stripe_reduced(dev, seq, theta):
+    x = synth.make_prefill("stripe_64k", seq=seq, hq=8, hkv=2)
+    _run_prefill_case(dev, x, np.full(8, theta, np.float32))
+
+
+def test_stripe_capacity_overflow_reported(dev):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill("stripe_64k", seq=1000, hq=4, hkv=1)
+    q, k = to_dev(x.q, dev), to_dev(x.k, dev)
+    lists = sa.estimate_mask(q, k, np.inf, granularity="stripe", stride=300,
+                             block_q=128, block_k=64, sink=32, local=256)
+    torch.cuda.synchronize()
+    counts = lists.counts.cpu().numpy()
+    # theta = +inf keeps every causal column: the true counts are reported
+    want = [min(1000, (i + 1) * 128) for i in range(counts.shape[2])]
+    assert counts[0, 0].tolist() == want
+    assert lists.overflowed()
+    # the prefill reads only the first `stride` entries of an overflowed row (no fault)
+    v = to_dev(x.v, dev)
+    o, _ = sa.sparse_prefill(q, k, v, lists, block_q=128, block_k=64, sink=32, local=256)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
+def test_determinism(dev):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill("llama8b_32k", seq=3000, hq=8, hkv=2)
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=128, block_k=64, sink=32, local=256)
+    outs = []
+    for _ in range(2):
+        l = sa.estimate_mask(q, k, np.full(8, 6.0, np.float32), **kw)
+        o, lse = sa.sparse_prefill(q, k, v, l, **kw)
+        torch.cuda.synchronize()
+        outs.append((l.counts.cpu(), l.idx.cpu(), o.cpu(), lse.cpu()))
+    c0, i0, o0, l0 = outs[0]
+    c1, i1, o1, l1 = outs[1]
+    assert torch.equal(c0, c1)
+    for r in range(c0.numel()):
+        n = int(c0.view(-1)[r])
+        assert torch.equal(i0.view(-1, i0.shape[-1])[r, :n], i1.view(-1, i1.shape[-1])[r, :n])
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l0, l1)
+
+
+@pytest.mark.parametrize("batch,seq,hq,hkv,d,top_k", [(3, 5000, 8, 2, 128, 24), (2, 3000, 4, 1, 64, 8),
+                                                     (2, 2000, 16, 2, 128, 64)])
+def test_decode_reduced(dev, batch, seq, hq, hkv, d, top_k):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_decode(batch=batch, seq=seq, hq=hq, hkv=hkv, head_dim=d, top_k=top_k)
+    if batch >= 2:
+        x.cache_len[1] = seq - 937          # ragged cache lengths
+    log(f"decode B={batch} L={seq} Hq={hq} Hkv={hkv} d={d} K={top_k} lens={x.cache_len.tolist()}")
+    q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=64)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=64, top_k=top_k, sink=32, local=256)
+    torch.cuda.synchronize()
+    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, 64)
+    kb = kbar.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(batch):
+        nb = -(-int(x.cache_len[b]) // 64)
+        np.testing.assert_array_equal(kb[b, :nb], kbar_ref[b, :nb])
+    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=64, top_k=top_k, sink=32, local=256)
+    s = sel.cpu().numpy()
+    used = {}
+    flips = 0
+    for (b, g), r in ref.items():
+        k_ = min(top_k, -(-int(x.cache_len[b]) // 64))
+        got = s[b, g, :k_]
+        assert (s[b, g, k_:] == -1).all()
+        assert np.all(np.diff(got) > 0)
+        diff = set(got.tolist()) ^ set(r["selected"].tolist())
+        assert diff <= set(r["ambiguous"].tolist()), ((b, g), sorted(diff))
+        flips += len(diff)
+        used[(b, g)] = got
+    O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used, block_k=64)
+    err = np.abs(o.float().cpu().numpy() - O)
+    assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
+    assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
+    log(f"  decode ok: flips={flips} max|dO|={err.max():.2e} mean={err.mean():.2e}")
