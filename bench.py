@@ -1,0 +1,247 @@
+"""Benchmark: one step = the whole sparse-prefill hot path (estimation pass + block-sparse
+attention) of one attention layer on seeded synthetic inputs already resident in HBM.
+
+Default workload: Llama-3.1-8B-shaped layer at 128K (batch 1, 32 query / 8 KV heads,
+head_dim 128, bf16, block 128x64, sink 32, local 256, per-KV-head theta from {2, 3, 4, 6}).
+Prints one JSON line.  --workload selects the other configurations for manual runs
+(llama8b_32k, stripe_64k, decode_b16_128k).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+PREFILL = ("llama8b_128k", "llama8b_32k", "stripe_64k")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def cpu_baseline_prefill(x, dense_flops, n_est_rows=128, n_attn_rows=128, seed=1):
+    """The oracle (numpy fp64) on a bounded random sample of the same workload: estimate
+    rows (b, g, i) and attention query blocks (b, h, i) drawn uniformly, timed separately and
+    scaled by total rows / sampled rows to a whole-layer time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    B, N, Hq, D = x.q.shape
+    Hkv = x.k.shape[2]
+    G = Hq // Hkv
+    nqb = -(-N // x.block_q)
+    rng = np.random.default_rng(seed)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local,
+              granularity=x.granularity)
+    # estimate sample, grouped by KV head so each group's key tiles are quantised once
+    gs = rng.integers(0, Hkv, n_est_rows)
+    is_ = rng.integers(0, nqb, n_est_rows)
+    rows = sorted((0, int(g), int(i)) for g, i in zip(gs, is_))
+    t0 = time.perf_counter()
+    ref = oracle.estimate_rows(x.q, x.k, x.theta, rows=rows, keep_margins=False, **kw)
+    t_est = time.perf_counter() - t0
+    # attention sample: lists from the oracle's own estimate of those rows
+    arows = []
+    for (b, g, i) in rows[:n_attn_rows]:
+        arows.append((b, g * G + int(rng.integers(0, G)), i))
+    lists = {key: r["kept"] for key, r in ref.items()}
+    t0 = time.perf_counter()
+    oracle.attention_rows(x.q, x.k, x.v, lists, rows=arows, block_q=x.block_q,
+                          block_k=x.block_k, granularity=x.granularity)
+    t_att = time.perf_counter() - t0
+    full = t_est * (B * Hkv * nqb) / len(rows) + t_att * (B * Hq * nqb) / len(arows)
+    return {"value": dense_flops / full / 1e12, "unit": "TFLOP/s (dense-equivalent)",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} random estimate rows (b,g,i) in {t_est:.1f}s and "
+                      f"{len(arows)} random attention query blocks (b,h,i) in {t_att:.1f}s, "
+                      f"scaled by rows to the whole layer ({full:.0f}s)",
+            "est_s": t_est, "attn_s": t_att, "extrapolated_layer_s": full}
+
+
+def bench_prefill(args, dev):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    import synth
+    log(f"generating {args.workload}")
+    x = synth.make_prefill(args.workload, seed=args.seed)
+    B, N, Hq, D = x.q.shape
+    Hkv = x.k.shape[2]
+    G = Hq // Hkv
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    stride = None
+    if x.granularity == "stripe":
+        stride = args.stripe_capacity
+    lists = sa.alloc_lists(q, k, block_q=x.block_q, block_k=x.block_k,
+                           granularity=x.granularity, stride=stride)
+    ws = torch.empty(sa.workspace_size(sa.SA_OP_ESTIMATE, q=q, k=k, granularity=x.granularity,
+                                       **kw), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sa.estimate_mask(q, k, x.theta, granularity=x.granularity, workspace=ws, out=lists, **kw)
+        if ev is not None:
+            ev[1].record(stream)
+        sa.sparse_prefill(q, k, v, lists, out=o, lse=False, **kw)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if x.granularity == "stripe" and lists.overflowed():
+        raise SystemExit("stripe list capacity exceeded; raise --stripe-capacity")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    est_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    att_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = wall * 1e3 / args.steps
+    counts = lists.counts.cpu().numpy().astype(np.int64)
+    nqb = counts.shape[2]
+    ends = np.minimum(N, (np.arange(nqb) + 1) * x.block_q) - 1
+    if x.granularity == "block":
+        cands = (ends // x.block_k + 1).astype(np.int64)
+        kept_units = int(counts.sum()) * G                       # kept (head, 128x64 tile)
+        flops_per_unit = 4.0 * x.block_q * x.block_k * D
+        density = float(counts.sum() / (cands.sum() * B * Hkv))
+    else:
+        cands = (ends + 1).astype(np.int64)
+        kept_units = int(counts.sum()) * G                       # kept (head, column)
+        flops_per_unit = 4.0 * x.block_q * D
+        density = float(counts.sum() / (cands.sum() * B * Hkv))
+    kept_flops = kept_units * flops_per_unit
+    dense_flops = 2.0 * N * N * D * Hq * B
+    att_avg = float(np.mean(att_ms))
+    est_avg = float(np.mean(est_ms))
+    achieved = kept_flops / (att_avg * 1e-3) / 1e12
+    per_group = (counts.sum(axis=(0, 2)) / (cands.sum() * B)).round(4).tolist()
+    out = {
+        "metric": "ms/layer & dense-equiv TFLOP/s (fraction of MFMA peak) for sparse prefill @128K",
+        "value": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: batch {B}, {Hq}/{Hkv} heads, d {D}, "
+                               f"seq {N}, block {x.block_q}x{x.block_k}, sink {x.sink}, "
+                               f"local {x.local}, {x.granularity}, theta per query head "
+                               f"{sorted(set(np.round(x.theta, 3).tolist()))}",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "ms_per_layer": round(ms_step, 3),
+        "estimate_ms": round(est_avg, 3), "attention_ms": round(att_avg, 3),
+        "estimate_over_attention": round(est_avg / att_avg, 4),
+        "kept_density": round(density, 5), "kept_density_per_kv_head": per_group,
+        "kept_tile_tflops": round(achieved, 2),
+        "kept_tile_frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "attn_sparse (sa_sparse_prefill)",
+                     "units": f"{kept_units} kept (head, {x.block_q}x{x.block_k} tile) x "
+                              f"{flops_per_unit / 1e6:.3f} MFLOP"},
+    }
+    if args.cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        out["cpu_baseline"] = cpu_baseline_prefill(x, dense_flops)
+    return out
+
+
+def bench_decode(args, dev):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    import synth
+    log("generating decode workload")
+    x = synth.make_decode(args.workload, seed=args.seed)
+    B, Hq, D = x.q.shape
+    L, Hkv = x.k_cache.shape[1], x.k_cache.shape[2]
+    q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=x.block_k)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    kw = dict(block_k=x.block_k, top_k=x.top_k, sink=x.sink, local=x.local)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
+    for _ in range(args.warmup):
+        sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    nkb = -(-L // x.block_k)
+    sel_bytes = B * Hkv * x.top_k * x.block_k * D * 2 * 2
+    sum_bytes = B * Hkv * nkb * D * 2
+    gbs = (sel_bytes + sum_bytes) / (us * 1e-6) / 1e9
+    return {"metric": "sparse decode step time and achieved HBM GB/s",
+            "value": round(gbs, 1), "unit": "GB/s (algorithmic)", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"{args.workload}: batch {B}, {Hq}/{Hkv} heads, d {D}, "
+                                   f"cache {L}, top-{x.top_k} blocks of {x.block_k}",
+                       "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
+            "us_per_step": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_128k",
+                    choices=list(PREFILL) + ["decode_b16_128k"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--stripe-capacity", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the workload "
+              "would shard by KV head with no exchange); run with --gpus 1", file=sys.stderr)
+        raise SystemExit(2)
+    import torch
+    dev = torch.device("cuda:0")
+    import block_sparse_attention_estimate_amd as sa
+    sa.load_library()
+    if args.workload in PREFILL:
+        out = bench_prefill(args, dev)
+    else:
+        out = bench_decode(args, dev)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

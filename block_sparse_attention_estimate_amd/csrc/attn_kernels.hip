@@ -53,10 +53,14 @@ __global__ __launch_bounds__(64 * HPW * 2 / NT) void attn_sparse(AttnArgs a) {
   int rest = w / a.tpb;
   const int hp = rest % a.n_hp;
   rest /= a.n_hp;
-  const int g = rest % a.Hkv;
-  rest /= a.Hkv;
-  const int b = rest % a.B;
-  rest /= a.B;
+  // rest = i_rev * (B * Hkv) + r2; rotating (b, g) with i_rev spreads every KV head (and so
+  // every threshold) over all XCDs instead of pinning one head to one XCD
+  const int BG = a.B * a.Hkv;
+  const int i_rev = rest / BG;
+  const int gb = (rest % BG + i_rev) % BG;
+  const int g = gb % a.Hkv;
+  const int b = gb / a.Hkv;
+  rest = i_rev;
   const int iq = a.nQB - 1 - rest;
   const int r0 = iq * a.bq + tsub * 64;
   if (iq < 0 || r0 >= a.N) return;
@@ -97,38 +101,59 @@ __global__ __launch_bounds__(64 * HPW * 2 / NT) void attn_sparse(AttnArgs a) {
   u32x4 kreg[PK];
   u32x4 vreg[PV][4];
   int kidv = 0;
-
-  auto tok_of = [&](int it, int kk, int Jb) -> int {
-    if (STRIPE) {
-      const int e = it * 64 + kk;
-      return e < n ? min(max(list[e], 0), a.N - 1) : 0;
-    }
-    return min(max(Jb * 64 + kk, 0), a.N - 1);
-  };
+  // per-thread staging coordinates (fixed for the whole loop)
+  int k_row[PK], k_dc[PK], v_row[PV], v_dc[PV];
+#pragma unroll
+  for (int c = 0; c < PK; ++c) {
+    const int ch = c * T + tid;
+    k_row[c] = ch / CPR;
+    k_dc[c] = (ch % CPR) * 8;
+  }
+#pragma unroll
+  for (int u = 0; u < PV; ++u) {
+    const int un = u * T + tid;
+    v_row[u] = (un / CPR) * 4;
+    v_dc[u] = (un % CPR) * 8;
+  }
 
   auto load_tile = [&](int it) {
-    const int Jb = STRIPE ? 0 : list[it];
+    if (!STRIPE) {
+      const int t0 = list[it] * 64;
+      if (t0 >= 0 && t0 + 63 < a.N) {
+        const uint16_t* kt = kg + (int64_t)t0 * a.ks1;
+        const uint16_t* vt = vg + (int64_t)t0 * a.vs1;
 #pragma unroll
-    for (int c = 0; c < PK; ++c) {
-      const int ch = c * T + tid;
-      if (ch < KCH) {
-        const int kk = ch / CPR, dc = (ch % CPR) * 8;
-        const int tok = tok_of(it, kk, Jb);
-        kreg[c] = *(const u32x4*)(kg + (int64_t)tok * a.ks1 + dc);
+        for (int c = 0; c < PK; ++c)
+          if (c * T + tid < KCH) kreg[c] = *(const u32x4*)(kt + (int64_t)k_row[c] * a.ks1 + k_dc[c]);
+#pragma unroll
+        for (int u = 0; u < PV; ++u)
+          if (u * T + tid < VU) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              vreg[u][j] = *(const u32x4*)(vt + (int64_t)(v_row[u] + j) * a.vs1 + v_dc[u]);
+          }
+        return;
       }
     }
-#pragma unroll
-    for (int u = 0; u < PV; ++u) {
-      const int un = u * T + tid;
-      if (un < VU) {
-        const int kq = (un / CPR) * 4, dc = (un % CPR) * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tok = tok_of(it, kq + j, Jb);
-          vreg[u][j] = *(const u32x4*)(vg + (int64_t)tok * a.vs1 + dc);
-        }
+    // ragged last block or gathered (stripe) rows: per-row token ids, clamped in range
+    auto tok_of = [&](int kk) -> int {
+      if (STRIPE) {
+        const int e = it * 64 + kk;
+        return e < n ? min(max(list[e], 0), a.N - 1) : 0;
       }
-    }
+      return min(max(list[it] * 64 + kk, 0), a.N - 1);
+    };
+#pragma unroll
+    for (int c = 0; c < PK; ++c)
+      if (c * T + tid < KCH)
+        kreg[c] = *(const u32x4*)(kg + (int64_t)tok_of(k_row[c]) * a.ks1 + k_dc[c]);
+#pragma unroll
+    for (int u = 0; u < PV; ++u)
+      if (u * T + tid < VU) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vreg[u][j] = *(const u32x4*)(vg + (int64_t)tok_of(v_row[u] + j) * a.vs1 + v_dc[u]);
+      }
     if (STRIPE && tid < 64) {
       const int e = it * 64 + tid;
       kidv = e < n ? list[e] : 0x7FFFFFFF;
@@ -137,29 +162,26 @@ __global__ __launch_bounds__(64 * HPW * 2 / NT) void attn_sparse(AttnArgs a) {
 
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < PK; ++c) {
-      const int ch = c * T + tid;
-      if (ch < KCH) {
-        const int kk = ch / CPR, dc = (ch % CPR) * 8;
-        *(u32x4*)&k_lds[buf][kk * KP + dc] = kreg[c];
-      }
-    }
+    for (int c = 0; c < PK; ++c)
+      if (c * T + tid < KCH) *(u32x4*)&k_lds[buf][k_row[c] * KP + k_dc[c]] = kreg[c];
 #pragma unroll
     for (int u = 0; u < PV; ++u) {
-      const int un = u * T + tid;
-      if (un < VU) {
-        const int kq = (un / CPR) * 4, dc = (un % CPR) * 8;
+      if (u * T + tid < VU) {
+        const int kq = v_row[u], dc = v_dc[u];
         // 4-key chunk c of a 16-key group moves to chunk {0, 2, 1, 3}[c]
         const int cq = (kq & 15) >> 2;
         const int pos = (kq & ~15) + (((cq & 1) << 1) | (cq >> 1)) * 4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = 16 * (e & 1);
-          const unsigned int x0 = (vreg[u][0][e >> 1] >> sh) & 0xFFFFu;
-          const unsigned int x1 = (vreg[u][1][e >> 1] >> sh) & 0xFFFFu;
-          const unsigned int x2 = (vreg[u][2][e >> 1] >> sh) & 0xFFFFu;
-          const unsigned int x3 = (vreg[u][3][e >> 1] >> sh) & 0xFFFFu;
-          *(u32x2*)&v_lds[buf][(dc + e) * VP + pos] = (u32x2){x0 | (x1 << 16), x2 | (x3 << 16)};
+        for (int e2 = 0; e2 < 4; ++e2) {
+          // dims dc + 2*e2 (low halves) and dc + 2*e2 + 1 (high halves) of the 4 keys
+          const unsigned int w0 = vreg[u][0][e2], w1 = vreg[u][1][e2];
+          const unsigned int w2 = vreg[u][2][e2], w3 = vreg[u][3][e2];
+          const unsigned int lo01 = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+          const unsigned int lo23 = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+          const unsigned int hi01 = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+          const unsigned int hi23 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+          *(u32x2*)&v_lds[buf][(dc + 2 * e2) * VP + pos] = (u32x2){lo01, lo23};
+          *(u32x2*)&v_lds[buf][(dc + 2 * e2 + 1) * VP + pos] = (u32x2){hi01, hi23};
         }
       }
     }
@@ -178,6 +200,9 @@ __global__ __launch_bounds__(64 * HPW * 2 / NT) void attn_sparse(AttnArgs a) {
     l_run[nt] = 0.f;
   }
   const float sl2 = a.scale_log2;
+  // bf16 pair (1.0, 1.0) for row sums with v_dot2
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   if (n_tiles > 0) {
     load_tile(0);
@@ -230,40 +255,55 @@ __global__ __launch_bounds__(64 * HPW * 2 / NT) void attn_sparse(AttnArgs a) {
         }
     }
 
-    // online softmax (log2 domain), P^T in bf16 for the PV product
+    // online softmax in the log2 domain.  The running max moves only when a row's new max
+    // exceeds it by more than 8 (a factor 256), so O is rescaled rarely; otherwise the
+    // probabilities are taken against the stale max (<= 2^8, exact in the final ratio).
+    float mx[NT];
+    bool grow = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float v = NEG_INF;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][nt][r]);
+      v = fmaxf(v, swap_halves(v)) * sl2;
+      mx[nt] = v;
+      grow |= v > m_run[nt] + 8.0f;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float mnew = fmaxf(m_run[nt], mx[nt]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mnew);
+        m_run[nt] = mnew;
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
+      }
+    }
     bf16x8 pf[NT][4];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float mx = NEG_INF;
+      const float mneg = -m_run[nt];
+      float ls = l_run[nt];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = fmaxf(m_run[nt], mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mnew);
-      m_run[nt] = mnew;
-      float ls = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], sl2, -mnew));
-          sacc[mt][nt][r] = p;
-          ls += p;
-        }
-      l_run[nt] = fmaf(l_run[nt], alpha, ls);
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm) oacc[dm][nt] *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s2 = 0; s2 < 2; ++s2) {
           f32x8 t;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) t[e] = sacc[mt][nt][8 * s + e];
-          pf[nt][mt * 2 + s] = __builtin_convertvector(t, bf16x8);
+          for (int e = 0; e < 8; ++e)
+            t[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][8 * s2 + e], sl2, mneg));
+          const bf16x8 pb = __builtin_convertvector(t, bf16x8);
+          pf[nt][mt * 2 + s2] = pb;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pb[e], pb[e + 1]};
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
+          }
         }
+      l_run[nt] = ls;
     }
 
     // O^T += V^T P^T
@@ -321,7 +361,7 @@ template <int D, bool STRIPE>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   static const int nt_pref = [] {
     const char* e = getenv("SA_ATTN_NT");
-    return (e && atoi(e) == 1) ? 1 : 2;
+    return (e && atoi(e) == 2) ? 2 : 1;
   }();
   if (a.G >= 4) {
     if (nt_pref == 1) return launch_one<D, 1, 4, STRIPE>(a, s);
