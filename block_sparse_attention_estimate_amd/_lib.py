@@ -50,11 +50,13 @@ class SaDecodeParams(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libsa.so once; raise if it is missing (there is no fallback path)."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libsa.so once; raise if it is missing (there is no fallback path).
+    SA_LIB_PATH may name another build of the same library (kernel variants)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("SA_LIB_PATH") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"libsa.so not found at {path}: build it with "
                            f"__graft_entry__.build() (hipcc --offload-arch=gfx950)")

@@ -64,6 +64,19 @@ SA_DEV float swap_halves(float v) {
   return __shfl_xor(v, 32);
 }
 
+// max / sum of a value and its copy in lane ^ 32, with v_permlane32_swap (no LDS traffic).
+// The swap leaves lanes 0-31 of the first result and lanes 32-63 of the second untouched and
+// exchanges the others, so for every lane the pair holds {v[l], v[l ^ 32]} in some order.
+SA_DEV float half_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+SA_DEV float half_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 SA_DEV int swap_halves_i(int v) {
   return __shfl_xor(v, 32);
 }

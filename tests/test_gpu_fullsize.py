@@ -1,0 +1,136 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The oracle recomputes sampled rows one by one (every row at 32K); attention parity is
+checked on sampled query blocks whose GPU list equals the oracle's list (the oracle's list
+is the attention input; rows whose lists differ only by ambiguous entries are counted)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import MAX_ABS, MEAN_ABS, compare_lists, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sa.load_library()
+    return torch.device("cuda:0")
+
+
+def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    log(f"generating {name}")
+    x = synth.make_prefill(name, seed=seed)
+    B, N, Hq, D = x.q.shape
+    Hkv = x.k.shape[2]
+    G = Hq // Hkv
+    nqb = -(-N // x.block_q)
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    stride = 8192 if x.granularity == "stripe" else None
+    lists = sa.estimate_mask(q, k, x.theta, granularity=x.granularity, stride=stride, **kw)
+    o, lse = sa.sparse_prefill(q, k, v, lists, **kw)
+    torch.cuda.synchronize()
+    assert not lists.overflowed()
+    rng = np.random.default_rng(seed + 7)
+    if n_rows is None:
+        rows = [(0, g, i) for g in range(Hkv) for i in range(nqb)]
+    else:
+        gi = set()
+        for g in range(Hkv):                     # first, last and random query blocks
+            gi.add((g, 0))
+            gi.add((g, nqb - 1))
+        while len(gi) < n_rows:
+            gi.add((int(rng.integers(0, Hkv)), int(rng.integers(0, nqb))))
+        rows = sorted((0, g, i) for g, i in gi)
+    log(f"oracle estimate of {len(rows)} rows")
+    ref = oracle.estimate_rows(x.q, x.k, x.theta, rows=rows, keep_margins=False,
+                               block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local,
+                               granularity=x.granularity)
+    nrows, entries, flips = compare_lists(lists, ref)
+    log(f"  lists ok: rows={nrows} entries={entries} ambiguous flips={flips}")
+    counts = lists.counts.cpu().numpy()
+    idx = lists.idx.cpu().numpy()
+    same = [key for key, r in ref.items()
+            if np.array_equal(idx[key][:counts[key]], r["kept"])]
+    pick = [same[j] for j in rng.permutation(len(same))[:n_attn]]
+    # always include the last query block of some group (longest lists)
+    last = [key for key in same if key[2] == nqb - 1]
+    if last and last[0] not in pick:
+        pick[-1] = last[0]
+    arows = [(b, g * G + int(rng.integers(0, G)), i) for (b, g, i) in pick]
+    log(f"oracle attention of {len(arows)} query blocks")
+    res = oracle.attention_rows(x.q, x.k, x.v, {key: ref[key]["kept"] for key in pick},
+                                rows=arows, block_q=x.block_q, block_k=x.block_k,
+                                granularity=x.granularity)
+    og = o.float().cpu()
+    lg = lse.cpu().numpy()
+    errs, lerrs = [], []
+    for (b, h, i), (oref, lref) in res.items():
+        r0 = i * x.block_q
+        r1 = min(N, r0 + x.block_q)
+        errs.append(np.abs(og[b, r0:r1, h, :].numpy() - oref).ravel())
+        lerrs.append(np.abs(lg[b, h, r0:r1] - lref))
+    err = np.concatenate(errs)
+    lerr = np.concatenate(lerrs)
+    log(f"  attention: max|dO|={err.max():.2e} mean={err.mean():.2e} max|dLSE|={lerr.max():.2e}")
+    assert err.max() < MAX_ABS and err.mean() < MEAN_ABS and lerr.max() < 1e-2
+    assert flips <= max(2, entries // 1000)
+
+
+def test_llama8b_32k_every_row(dev):
+    _prefill_parity(dev, "llama8b_32k", n_rows=None, n_attn=16)
+
+
+def test_llama8b_128k_sampled(dev):
+    _prefill_parity(dev, "llama8b_128k", n_rows=40, n_attn=12)
+
+
+def test_stripe_64k_sampled(dev):
+    _prefill_parity(dev, "stripe_64k", n_rows=24, n_attn=10)
+
+
+def test_decode_b16_128k(dev):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    log("generating decode_b16_128k")
+    x = synth.make_decode("decode_b16_128k")
+    B, Hq, D = x.q.shape
+    q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=x.block_k)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=x.block_k, top_k=x.top_k,
+                                   sink=x.sink, local=x.local)
+    torch.cuda.synchronize()
+    log("oracle block summaries")
+    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, x.block_k)
+    kb = kbar.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(kb, kbar_ref)
+    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=x.block_k, top_k=x.top_k,
+                               sink=x.sink, local=x.local)
+    s = sel.cpu().numpy()
+    flips = 0
+    same = {}
+    for (b, g), r in ref.items():
+        got = s[b, g]
+        diff = set(got.tolist()) ^ set(r["selected"].tolist())
+        assert diff <= set(r["ambiguous"].tolist()), ((b, g), sorted(diff))
+        flips += len(diff)
+        if not diff:
+            same[(b, g)] = r["selected"]
+    log(f"  selection ok: flips={flips}")
+    keep_b = [b for b in range(B) if all((b, g) in same for g in range(kc.shape[2]))]
+    assert keep_b
+    sub = {(j, g): same[(b, g)] for j, b in enumerate(keep_b) for g in range(kc.shape[2])}
+    O, LSE = oracle.decode_attention(x.q[keep_b], x.k_cache[keep_b], x.v_cache[keep_b],
+                                     x.cache_len[keep_b], sub, block_k=x.block_k)
+    err = np.abs(o.float().cpu().numpy()[keep_b] - O)
+    log(f"  decode attention over {len(keep_b)} sequences: max|dO|={err.max():.2e} mean={err.mean():.2e}")
+    assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
+    assert np.abs(lse.cpu().numpy()[keep_b] - LSE).max() < 1e-2
