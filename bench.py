@@ -23,6 +23,82 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 PREFILL = ("llama8b_128k", "llama8b_32k", "stripe_64k")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_estimate_amd", "csrc", "attn_kernels.hip")
+DEC_SRC = os.path.join(ROOT, "block_sparse_attention_estimate_amd", "csrc", "decode_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30          # plain device copy used to calibrate the byte counters
+
+
+def source_hash(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(name, src):
+    """HBM bytes per launch recorded in profiles/<name>.txt, or None when missing or taken
+    on a different kernel source."""
+    path = os.path.join(PROFILES, name + ".txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_hash(src):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_pmc(fetch_dir, write_dir, kernel, workload, src, command):
+    """Text summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB per
+    dispatch) for `kernel`, scaled by the same counters on a plain copy of COPY_BYTES."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals, copy = [], []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                if kernel in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+                elif "copyBuffer" in r["Kernel_Name"]:
+                    copy.append(float(r["Counter_Value"]))
+        # the calibration copy is by far the largest copy dispatch of the run
+        return (sum(vals) / len(vals) if vals else float("nan"),
+                max(copy) if copy else float("nan"), len(vals))
+
+    f_k, f_c, n_f = per_dispatch(fetch_dir, "FETCH_SIZE")
+    w_k, w_c, n_w = per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (f_c * 1024.0)
+    w_scale = COPY_BYTES / (w_c * 1024.0)
+    total = f_k * 1024.0 * f_scale + w_k * 1024.0 * w_scale
+    lines = [f"# HBM traffic of {kernel} on {workload}",
+             f"command: {command}",
+             f"kernel_source_sha256_16: {source_hash(src)}",
+             f"dispatches: fetch {n_f}, write {n_w}",
+             f"fetch_kib_per_dispatch: {f_k:.1f}",
+             f"write_kib_per_dispatch: {w_k:.1f}",
+             f"copy_fetch_kib ({COPY_BYTES} B copy): {f_c:.1f}",
+             f"copy_write_kib ({COPY_BYTES} B copy): {w_c:.1f}",
+             f"fetch_scale: {f_scale:.4f}",
+             f"write_scale: {w_scale:.4f}",
+             f"hbm_bytes_per_launch: {total:.0f}"]
+    return "\n".join(lines)
+
+
+def copy_calibration(dev):
+    import torch
+    n = COPY_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def log(msg):
@@ -164,7 +240,7 @@ def bench_prefill(args, dev):
         "kept_tile_frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": traffic_from_profile(f"attn_sparse_{args.workload}_traffic", ATTN_SRC),
                      "kernel": "attn_sparse (sa_sparse_prefill)",
                      "units": f"{kept_units} kept (head, {x.block_q}x{x.block_k} tile) x "
                               f"{flops_per_unit / 1e6:.3f} MFLOP"},
@@ -214,7 +290,8 @@ def bench_decode(args, dev):
                        "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
             "us_per_step": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_from_profile(f"dec_splitk_{args.workload}_traffic", DEC_SRC)}}
 
 
 def main():
@@ -227,7 +304,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--stripe-capacity", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (byte-counter scale)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--kernel", default="attn_sparse")
+    ap.add_argument("--command", default="")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        src = DEC_SRC if args.kernel.startswith("dec_") else ATTN_SRC
+        print(summarize_pmc(*args.summarize_pmc, args.kernel, args.workload, src, args.command))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the workload "
               "would shard by KV head with no exchange); run with --gpus 1", file=sys.stderr)
@@ -240,6 +327,8 @@ def main():
         out = bench_prefill(args, dev)
     else:
         out = bench_decode(args, dev)
+    if args.copy_calibration:
+        copy_calibration(dev)
     print(json.dumps(out), flush=True)
 
 

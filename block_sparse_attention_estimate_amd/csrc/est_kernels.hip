@@ -112,18 +112,35 @@ __global__ __launch_bounds__(256) void est_anchor_pool(EstArgs a) {
     const int lo = max(0, ra - a.local + 1);
     const int win_start = max((lo / 32) * 32, sink_tiles_end);
     const uint16_t* kb = a.k + b * a.ks0 + g * a.ks2 + half * 8;
-    for (int pass = 0; pass < 2; ++pass) {
-      const int t_begin = pass == 0 ? 0 : win_start;
-      const int t_end = pass == 0 ? sink_tiles_end : hi + 1;
-      for (int ts = t_begin; ts < t_end; ts += 32) {
-        const int kr = min(ts + l32, a.N - 1);
-        const uint16_t* kp = kb + (int64_t)kr * a.ks1;
-        f32x16 acc = {};
+    // key tiles: the sink tiles, then the window tiles; fragments of the next tile are
+    // loaded before the current tile's MFMAs
+    const int n_sink_t = sink_tiles_end / 32;
+    const int n_win_t = win_start <= hi ? (hi - win_start) / 32 + 1 : 0;
+    const int n_t = n_sink_t + n_win_t;
+    auto tile_start = [&](int t) { return t < n_sink_t ? t * 32 : win_start + (t - n_sink_t) * 32; };
+    bf16x8 kf[KS], kn[KS];
+    if (n_t > 0) {
+      const uint16_t* kp = kb + (int64_t)min(tile_start(0) + l32, a.N - 1) * a.ks1;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          bf16x8 kf = *(const bf16x8*)(kp + ks * 16);
-          acc = mfma_bf16(kf, qf[ks], acc);
-        }
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const bf16x8*)(kp + ks * 16);
+    }
+    for (int t = 0; t < n_t; ++t) {
+      const int ts = tile_start(t);
+      if (t + 1 < n_t) {
+        const uint16_t* kp = kb + (int64_t)min(tile_start(t + 1) + l32, a.N - 1) * a.ks1;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kn[ks] = *(const bf16x8*)(kp + ks * 16);
+      }
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(kf[ks], qf[ks], acc);
+      // a tile whose 32 keys are visible to all 32 rows of this n-tile needs no mask
+      const bool all_sink = ts + 31 < a.sink && ts + 31 <= ra;
+      const bool all_win = ts >= ra + 31 - a.local + 1 && ts + 31 <= ra;
+      if (all_sink || all_win) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+      } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
@@ -131,19 +148,42 @@ __global__ __launch_bounds__(256) void est_anchor_pool(EstArgs a) {
           if (ok) mx = fmaxf(mx, acc[r]);
         }
       }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
     }
     mx = fmaxf(mx, swap_halves(mx));
     if (half == 0 && row < r1) xa_s[hg][row - r0] = __fmul_rn(mx, a.c);
   }
 
   // Pooled query: fp64 sum over the block's rows, one rounding to fp32, fp32 division.
-  for (int p = tid; p < G * D; p += 256) {
-    const int hg = p / D, dd = p % D;
+  // Each thread owns two adjacent dims of one head (one 4-byte load per row); four
+  // independent fp64 partial sums keep several loads in flight.  Sums of bf16 values are
+  // exact in fp64 here, so the split does not change the result.
+  for (int p = tid; p < G * D / 2; p += 256) {
+    const int hg = p / (D / 2), d2 = (p % (D / 2)) * 2;
     const int h = g * G + hg;
-    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r0 * a.qs1 + h * a.qs2 + dd;
-    double s = 0.0;
-    for (int r = 0; r < nrows; ++r) s += bf16_bits_to_double(qp[(int64_t)r * a.qs1]);
-    qbar_s[hg][dd] = __fdiv_rn((float)s, (float)nrows);
+    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r0 * a.qs1 + h * a.qs2 + d2;
+    double s0[4] = {0.0, 0.0, 0.0, 0.0}, s1[4] = {0.0, 0.0, 0.0, 0.0};
+    int r = 0;
+    for (; r + 8 <= nrows; r += 8) {
+      unsigned int u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = *(const unsigned int*)(qp + (int64_t)(r + j) * a.qs1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        s0[j & 3] += bf16_bits_to_double((unsigned short)(u[j] & 0xFFFFu));
+        s1[j & 3] += bf16_bits_to_double((unsigned short)(u[j] >> 16));
+      }
+    }
+    for (; r < nrows; ++r) {
+      const unsigned int u = *(const unsigned int*)(qp + (int64_t)r * a.qs1);
+      s0[0] += bf16_bits_to_double((unsigned short)(u & 0xFFFFu));
+      s1[0] += bf16_bits_to_double((unsigned short)(u >> 16));
+    }
+    const double t0 = (s0[0] + s0[1]) + (s0[2] + s0[3]);
+    const double t1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+    qbar_s[hg][d2] = __fdiv_rn((float)t0, (float)nrows);
+    qbar_s[hg][d2 + 1] = __fdiv_rn((float)t1, (float)nrows);
   }
   __syncthreads();
 
@@ -220,22 +260,35 @@ __global__ __launch_bounds__(256) void est_score_block(EstArgs a, int n_rt, int 
   const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
   unsigned int bits[NT] = {0u, 0u};
 
+  i32x4 kf[2][KS], kn[2][KS];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[mt][ks] = *(const i32x4*)(kbase + (int64_t)(J0 * 64 + mt * 32 + l32) * D + ks * 32);
   for (int J = J0; J < J_end; ++J) {
+    if (J + 1 < J_end) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kn[mt][ks] = *(const i32x4*)(kbase + (int64_t)((J + 1) * 64 + mt * 32 + l32) * D + ks * 32);
+    }
     i32x16 acc[2][NT];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (i32x16){};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int8_t* kp = kbase + (int64_t)(J * 64 + mt * 32 + l32) * D;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const i32x4 kf = *(const i32x4*)(kp + ks * 32);
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_i8(kf, qf[nt][ks], acc[mt][nt]);
-      }
-    }
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_i8(kf[mt][ks], qf[nt][ks], acc[mt][nt]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = kn[mt][ks];
     const float skv = a.sk[(int64_t)bg * a.nKB + J];
     const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
 #pragma unroll
@@ -286,7 +339,7 @@ __global__ __launch_bounds__(256) void est_score_block(EstArgs a, int n_rt, int 
 // ballot that holds, per row pair, the keep bits of 32 consecutive columns.
 // Workgroup = 4 waves x 64 rows, 32 key tiles of 64 columns.
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool MARGINS>
 __global__ __launch_bounds__(256) void est_score_stripe(EstArgs a, int n_rt, int n_jc) {
   constexpr int KS = D / 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -297,28 +350,28 @@ __global__ __launch_bounds__(256) void est_score_stripe(EstArgs a, int n_rt, int
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.G;
   const int rows_total = a.nQB * G;
-  const int R_last = min(rt * 256 + 255, rows_total - 1);
+  const int R_last = min(rt * 128 + 127, rows_total - 1);
   const int e_last = min(a.N, (R_last / G + 1) * a.bq) - 1;
   const int J0 = jc * 32;
   if (J0 * 64 > e_last) return;
   const int J_end = min(J0 + 32, e_last / 64 + 1);
   const int64_t row_base = (int64_t)bg * a.nQB * G;
-  const int Rw = rt * 256 + wave * 64;                  // first row of this wave
+  const int Rw = rt * 128 + wave * 32;                  // first row of this wave
   if (Rw >= rows_total) return;
 
   // A operand: pooled query rows Rw + mt*32 + l32
-  i32x4 qf[2][KS];
-  for (int mt = 0; mt < 2; ++mt) {
+  i32x4 qf[1][KS];
+  for (int mt = 0; mt < 1; ++mt) {
     const int Rc = min(Rw + mt * 32 + l32, rows_total - 1);
     const int8_t* qp = a.qq + (row_base + Rc) * D + half * 16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[mt][ks] = *(const i32x4*)(qp + ks * 32);
   }
   // Per-register row data: register r of m-tile mt holds row Rw + mt*32 + half*4 + 8(r/4) + r%4
-  float thr[2][16], sqv[2][16];
-  int erow[2][16];
+  float thr[1][16], sqv[1][16];
+  int erow[1][16];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 1; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int R = Rw + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
@@ -329,82 +382,119 @@ __global__ __launch_bounds__(256) void est_score_stripe(EstArgs a, int n_rt, int
       erow[mt][r] = R < rows_total ? min(a.N, (Rc / G + 1) * a.bq) - 1 : -1;
     }
   const int e_min = min(a.N, (Rw / G + 1) * a.bq) - 1;
-  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
-  for (int J = J0; J < J_end; ++J) {
-    i32x16 acc[2][2];
+  // rows past the end never pass: their threshold is +inf
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 1; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (erow[mt][r] < 0) thr[mt][r] = __builtin_huge_valf();
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
+  i32x4 kf[2][KS], kn[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[nt][ks] = *(const i32x4*)(kbase + (int64_t)(J0 * 64 + nt * 32 + l32) * D + ks * 32);
+  for (int J = J0; J < J_end; ++J) {
+    if (J + 1 < J_end) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kn[nt][ks] = *(const i32x4*)(kbase + (int64_t)((J + 1) * 64 + nt * 32 + l32) * D + ks * 32);
+    }
+    i32x16 acc[1][2];
+#pragma unroll
+    for (int mt = 0; mt < 1; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (i32x16){};
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int8_t* kp = kbase + (int64_t)(J * 64 + nt * 32 + l32) * D;
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const i32x4 kf = *(const i32x4*)(kp + ks * 32);
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma_i8(qf[mt][ks], kf, acc[mt][nt]);
-      }
-    }
+        for (int mt = 0; mt < 1; ++mt) acc[mt][nt] = mfma_i8(qf[mt][ks], kf[nt][ks], acc[mt][nt]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[nt][ks] = kn[nt][ks];
     const float skv = a.sk[(int64_t)bg * a.nKB + J];
+    // keep <=> fp32(fp32(D) * m) - (abar - theta) >= 0 <=> fp32(fp32(D) * m) >= (abar - theta)
+    float mult[1][16];
+#pragma unroll
+    for (int mt = 0; mt < 1; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mult[mt][r] = __fmul_rn(__fmul_rn(sqv[mt][r], skv), a.c);
     const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int key = J * 64 + nt * 32 + l32;
       const int wi = J * 2 + nt;                         // bit word of columns [key - l32, +32)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 1; ++mt) {
         // register r = 4*ag + bb of this m-tile is row Rw + mt*32 + half*4 + 8*ag + bb
 #pragma unroll
         for (int ag = 0; ag < 4; ++ag) {
-          float mv[4];
+          unsigned long long bal[4];
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
             const int r = 4 * ag + bb;
-            const float mult = __fmul_rn(__fmul_rn(sqv[mt][r], skv), a.c);
-            float margin = __fmul_rn((float)acc[mt][nt][r], mult) - thr[mt][r];
-            if ((need_mask && key > erow[mt][r]) || erow[mt][r] < 0) margin = NEG_INF;
-            mv[bb] = margin;
+            const float y = __fmul_rn((float)acc[mt][nt][r], mult[mt][r]);
+            bool keep = y >= thr[mt][r];
+            if (need_mask) keep = keep && key <= erow[mt][r];
+            bal[bb] = __ballot(keep);
           }
           const int Rg = Rw + mt * 32 + 8 * ag;        // first row of this 8-row group
-          if (G <= 4) {
-            // G consecutive rows (same half) form one query block: OR their ballots
-            unsigned long long word = 0ull;
-            float mg = NEG_INF;
+          if (lane == 0) {
+            if (G <= 4) {
+              // G consecutive rows (same half) form one query block: OR their ballots
+              unsigned long long word = 0ull;
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-              word |= __ballot(mv[bb] >= 0.f);
-              mg = fmaxf(mg, mv[bb]);
-              if (((bb + 1) % G) == 0) {
-                const int b0 = bb + 1 - G;
-                const int R_lo = Rg + b0, R_hi = Rg + 4 + b0;
-                if (lane == 0) {
+              for (int bb = 0; bb < 4; ++bb) {
+                word |= bal[bb];
+                if (((bb + 1) % G) == 0) {
+                  const int R_lo = Rg + bb + 1 - G, R_hi = R_lo + 4;
                   if (R_lo < rows_total) a.bits[(row_base / G + R_lo / G) * a.W + wi] = (unsigned int)word;
                   if (R_hi < rows_total) a.bits[(row_base / G + R_hi / G) * a.W + wi] = (unsigned int)(word >> 32);
+                  word = 0ull;
                 }
-                if (a.margins) {
+              }
+            } else {
+              // G == 8: rows Rg .. Rg+7 (both halves) are one query block
+              const unsigned long long word = bal[0] | bal[1] | bal[2] | bal[3];
+              if (Rg < rows_total)
+                a.bits[(row_base / G + Rg / G) * a.W + wi] = (unsigned int)word | (unsigned int)(word >> 32);
+            }
+          }
+          if (MARGINS) {
+            // diagnostic output: max over the group's heads of score - (anchor - theta)
+            float mv[4];
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              const int r = 4 * ag + bb;
+              float m = __fmul_rn((float)acc[mt][nt][r], mult[mt][r]) - thr[mt][r];
+              if (key > erow[mt][r] || erow[mt][r] < 0) m = NEG_INF;
+              mv[bb] = m;
+            }
+            if (G <= 4) {
+              float mg = NEG_INF;
+#pragma unroll
+              for (int bb = 0; bb < 4; ++bb) {
+                mg = fmaxf(mg, mv[bb]);
+                if (((bb + 1) % G) == 0) {
+                  const int b0 = bb + 1 - G;
                   const int R = Rg + half * 4 + b0;
                   if (R < rows_total && key <= erow[mt][4 * ag + b0])
                     a.margins[((int64_t)bg * a.nQB + R / G) * a.N + key] = mg;
+                  mg = NEG_INF;
                 }
-                word = 0ull;
-                mg = NEG_INF;
               }
+            } else {
+              float mg = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));
+              mg = fmaxf(mg, swap_halves(mg));
+              if (half == 0 && Rg < rows_total && key <= erow[mt][4 * ag])
+                a.margins[((int64_t)bg * a.nQB + Rg / G) * a.N + key] = mg;
             }
-          } else {
-            // G == 8: rows Rg .. Rg+7 (both halves) are one query block
-            unsigned long long word = 0ull;
-            float mg = NEG_INF;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-              word |= __ballot(mv[bb] >= 0.f);
-              mg = fmaxf(mg, mv[bb]);
-            }
-            mg = fmaxf(mg, swap_halves(mg));
-            if (lane == 0 && Rg < rows_total)
-              a.bits[(row_base / G + Rg / G) * a.W + wi] = (unsigned int)word | (unsigned int)(word >> 32);
-            if (a.margins && half == 0 && Rg < rows_total && key <= erow[mt][4 * ag])
-              a.margins[((int64_t)bg * a.nQB + Rg / G) * a.N + key] = mg;
           }
         }
       }
@@ -484,7 +574,14 @@ static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream
   const int n_jc = (a.nKB + 31) / 32;
   const int grid = a.B * a.Hkv * n_rt * n_jc;
   if (granularity == SA_STRIPE) {
-    hipLaunchKernelGGL(est_score_stripe<D>, dim3(grid), dim3(256), 0, s, a, n_rt, n_jc);
+    const int n_rt_s = (rows_total + 127) / 128;
+    // the instance without the diagnostic margins output keeps its registers for the hot loop
+    if (a.margins)
+      hipLaunchKernelGGL((est_score_stripe<D, true>), dim3(a.B * a.Hkv * n_rt_s * n_jc), dim3(256), 0,
+                         s, a, n_rt_s, n_jc);
+    else
+      hipLaunchKernelGGL((est_score_stripe<D, false>), dim3(a.B * a.Hkv * n_rt_s * n_jc), dim3(256), 0,
+                         s, a, n_rt_s, n_jc);
     hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, 1);
   } else {
     hipLaunchKernelGGL(est_score_block<D>, dim3(grid), dim3(256), 0, s, a, n_rt, n_jc);
