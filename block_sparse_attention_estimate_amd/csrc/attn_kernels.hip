@@ -398,6 +398,260 @@ __global__ __launch_bounds__(128 * HPW) void attn_sparse(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Block lists: K/V tiles go HBM -> LDS with direct loads (global_load_lds_dwordx4), no
+// staging registers.  Four LDS stages: tile t is consumed while tiles t+1..t+3 are in flight.
+//  * K rows keep head_dim order with a 16-byte pad per row (pitch 272 B for d = 128), so the
+//    A-operand reads of S^T = K Q^T (16 rows x 16 B per lane group) hit distinct banks.
+//  * V rows are stored as they are (pitch 320 B for d = 128); the A operand of O^T += V^T P^T
+//    is read with ds_read_b64_tr_b16: within a 16-lane group, lane j addresses the 4 dims
+//    [d0 + 4(j%4), +4) of key row k0 + j/4, and the read returns to lane i the 4 keys
+//    k0..k0+3 of dim d0 + i -- exactly the 4 keys the P^T register layout pairs with that lane.
+// ---------------------------------------------------------------------------------------
+// s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at their maxima)
+#define VMCNT_IMM(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+template <int D, int HPW>
+__global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
+  constexpr int NWV = 2 * HPW;             // waves: 2 slices of 32 rows per head
+  constexpr int KS = D / 16;               // k-steps of S^T
+  constexpr int DM = D / 32;               // d tiles of O^T
+  constexpr int ROWB = D * 2;              // bytes of one K/V row
+  constexpr int KPITCH = D == 128 ? 272 : 144;
+  constexpr int VPITCH = D == 128 ? 320 : 192;
+  constexpr int KREG = 64 * KPITCH, VREG = 64 * VPITCH;
+  constexpr int KWIN = KREG / 1024, VWIN = VREG / 1024, NWIN = KWIN + VWIN;
+  constexpr int STAGE = KREG + VREG;
+  constexpr int SLOTS = (NWIN + NWV - 1) / NWV;      // DMA windows per wave per tile
+  static_assert(KREG % 1024 == 0 && VREG % 1024 == 0, "DMA windows must tile the stage");
+  // four stages as distinct objects, so the compiler can tell a load into one stage from
+  // reads of another; windows past NWIN (to give every wave the same count) go to `spare`
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st3[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char spare[1024];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+
+  // ---- work item (longest first; both halves of a query block on one XCD) ----
+  int w = blockIdx.x;
+  if (a.tpb == 2) {
+    const int full = (a.total / 16) * 16;
+    if (w < full) w = (w / 16) * 16 + (w % 8) * 2 + ((w / 8) & 1);
+  }
+  const int tsub = w % a.tpb;
+  int rest = w / a.tpb;
+  const int hp = rest % a.n_hp;
+  rest /= a.n_hp;
+  const int BG = a.B * a.Hkv;
+  const int i_rev = rest / BG;
+  const int gb = (rest % BG + i_rev) % BG;
+  const int g = gb % a.Hkv;
+  const int b = gb / a.Hkv;
+  const int iq = a.nQB - 1 - i_rev;
+  const int r0 = iq * a.bq + tsub * 64;
+  if (iq < 0 || r0 >= a.N) return;
+  const int r_last = min(r0 + 63, a.N - 1);
+  const int h = g * a.G + hp * HPW + (wave >> 1);
+  const int rw = r0 + (wave & 1) * 32;
+  const int row = rw + l32;
+
+  // the lists are read-only here: read them through the constant address space (scalar loads)
+  const int64_t lrow = (int64_t)(b * a.Hkv + g) * a.nQB + iq;
+  const __attribute__((address_space(4))) int32_t* list =
+      (const __attribute__((address_space(4))) int32_t*)(a.idx + lrow * a.stride);
+  int n = min(((const __attribute__((address_space(4))) int32_t*)a.counts)[lrow], a.stride);
+  while (n > 0 && list[n - 1] * 64 > r_last) --n;
+  int n_main = n;
+  while (n_main > 0 && (list[n_main - 1] * 64 + 63 > r0 || list[n_main - 1] * 64 + 63 >= a.N)) --n_main;
+
+  bf16x8 qf[KS];
+  {
+    const int rowc = min(row, a.N - 1);
+    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + h * a.qs2 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
+  }
+
+  // ---- DMA slots of this wave: window j = wave + k * NWV of each stage ----
+  const uint16_t* kg = a.k + b * a.ks0 + g * a.ks2;
+  const uint16_t* vg = a.v + b * a.vs0 + g * a.vs2;
+  int s_row[SLOTS], s_off[SLOTS];
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    const int j = min(wave + k * NWV, NWIN - 1);
+    const bool isv = j >= KWIN;
+    const int o = (isv ? j - KWIN : j) * 1024 + lane * 16;
+    const int pitch = isv ? VPITCH : KPITCH;
+    const int r = o / pitch;
+    const int cb = o % pitch;
+    const int c = cb < ROWB ? cb / 16 : 0;          // pad bytes receive a harmless copy
+    s_row[k] = r;
+    s_off[k] = r * (int)(isv ? a.vs1 : a.ks1) + c * 8;
+  }
+  // Issue the DMA of tile t (clamped to the list) into stage S.  Every wave issues exactly
+  // SLOTS loads per call, so the vmcnt waits below are compile-time constants.
+  auto issue = [&]<int S>(int t) {
+    unsigned char* stb = S == 0 ? st0 : S == 1 ? st1 : S == 2 ? st2 : st3;
+    const int t0 = list[min(t, n - 1)] * 64;
+    const bool fast = t0 + 63 < a.N;
+    const int64_t kb = (int64_t)t0 * a.ks1, vb = (int64_t)t0 * a.vs1;
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+      const int j = wave + k * NWV;
+      const bool isv = min(j, NWIN - 1) >= KWIN;
+      const uint16_t* src;
+      if (fast) {
+        src = isv ? vg + vb + s_off[k] : kg + kb + s_off[k];
+      } else {
+        const int tok = min(t0 + s_row[k], a.N - 1);
+        const int coff = s_off[k] - s_row[k] * (int)(isv ? a.vs1 : a.ks1);
+        src = isv ? vg + (int64_t)tok * a.vs1 + coff : kg + (int64_t)tok * a.ks1 + coff;
+      }
+      if (j < NWIN) {
+        unsigned char* dst = stb + (isv ? KREG + (j - KWIN) * 1024 : j * 1024);
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, dst), 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, spare), 16, 0, 0);
+      }
+    }
+  };
+
+  // per-lane LDS read offsets within a stage
+  const int k_rd = l32 * KPITCH + half * 16;
+  const int grp = lane >> 4, jj = lane & 15;
+  const int v_rd = KREG + (4 * (grp >> 1) + (jj >> 2)) * VPITCH + (16 * (grp & 1) + 4 * (jj & 3)) * 2;
+
+  f32x16 oacc[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) oacc[dm] = (f32x16){};
+  float m_run = -1e30f, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // one tile: S^T = K Q^T, mask (tail tiles), online softmax (log2 domain, lazy rescale as in
+  // attn_sparse), O^T += V^T P^T with transposing V reads; then the DMA of tile t+3, the wait
+  // for tile t+1 and the barrier
+  auto step = [&]<int S>(int t) {
+    unsigned char* sb = S == 0 ? st0 : S == 1 ? st1 : S == 2 ? st2 : st3;
+    f32x16 sacc[2];
+    sacc[0] = (f32x16){};
+    sacc[1] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 kf = *(const bf16x8*)(sb + k_rd + mt * 32 * KPITCH + ks * 32);
+        sacc[mt] = mfma_bf16(kf, qf[ks], sacc[mt]);
+      }
+    if (t >= n_main) {
+      const int Jb = list[t];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = Jb * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+          if (tok > row || tok >= a.N) sacc[mt][r] = NEG_INF;
+        }
+    }
+    {
+      float v = NEG_INF;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][r]);
+      v = half_pair_max(v) * sl2;
+      if (__any(v > m_run + 8.0f)) {
+        const float mnew = fmaxf(m_run, v);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+        m_run = mnew;
+        l_run *= alpha;
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+      }
+    }
+    bf16x8 pf[4];
+    {
+      const float mneg = -m_run;
+      float ls = l_run;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          f32x8 tt;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * s2 + e], sl2, mneg));
+          const bf16x8 pb = __builtin_convertvector(tt, bf16x8);
+          pf[mt * 2 + s2] = pb;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pb[e], pb[e + 1]};
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
+          }
+        }
+      l_run = ls;
+    }
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        const unsigned char* vp = sb + v_rd + 16 * s4 * VPITCH + dm * 64;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp + 8 * VPITCH));
+        const v4i16 both[2] = {lo, hi};
+        bf16x8 vf;
+        __builtin_memcpy(&vf, both, 16);
+        oacc[dm] = mfma_bf16(vf, pf[s4], oacc[dm]);
+      }
+    issue.template operator()<(S + 3) & 3>(t + 3);
+    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(2 * SLOTS));
+    __syncthreads();
+  };
+
+  if (n > 0) {
+    issue.template operator()<0>(0);
+    issue.template operator()<1>(1);
+    issue.template operator()<2>(2);
+    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(2 * SLOTS));
+    __syncthreads();
+    int t = 0;
+    for (; t + 4 <= n; t += 4) {
+      step.template operator()<0>(t);
+      step.template operator()<1>(t + 1);
+      step.template operator()<2>(t + 2);
+      step.template operator()<3>(t + 3);
+    }
+    if (t < n) step.template operator()<0>(t);
+    if (t + 1 < n) step.template operator()<1>(t + 1);
+    if (t + 2 < n) step.template operator()<2>(t + 2);
+    // no DMA may still be writing this workgroup's LDS when it exits
+    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+  }
+
+  const float lt = half_pair_sum(l_run);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (row < a.N) {
+    uint16_t* op = a.o + b * a.os0 + (int64_t)row * a.os1 + h * a.os2 + half * 4;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const unsigned int lo = float_to_bf16_bits(oacc[dm][4 * q4 + 0] * inv) |
+                                ((unsigned int)float_to_bf16_bits(oacc[dm][4 * q4 + 1] * inv) << 16);
+        const unsigned int hi = float_to_bf16_bits(oacc[dm][4 * q4 + 2] * inv) |
+                                ((unsigned int)float_to_bf16_bits(oacc[dm][4 * q4 + 3] * inv) << 16);
+        *(u32x2*)(op + dm * 32 + 8 * q4) = (u32x2){lo, hi};
+      }
+    if (a.lse && half == 0)
+      a.lse[((int64_t)b * a.Hq + h) * a.N + row] =
+          lt > 0.f ? (m_run + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 template <int D, int HPW, bool STRIPE>
 static hipError_t launch_one(const AttnArgs& a0, hipStream_t s) {
   AttnArgs a = a0;
@@ -408,8 +662,23 @@ static hipError_t launch_one(const AttnArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int HPW>
+static hipError_t launch_block(const AttnArgs& a0, hipStream_t s) {
+  AttnArgs a = a0;
+  a.n_hp = a.G / HPW;
+  a.total = a.B * a.Hkv * a.n_hp * a.nQB * a.tpb;
+  if (a.total == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_block<D, HPW>), dim3(a.total), dim3(128 * HPW), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, bool STRIPE>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+  if (!STRIPE) {
+    if (a.G >= 4) return launch_block<D, 4>(a, s);
+    if (a.G == 2) return launch_block<D, 2>(a, s);
+    return launch_block<D, 1>(a, s);
+  }
   if (a.G >= 4) return launch_one<D, 4, STRIPE>(a, s);
   if (a.G == 2) return launch_one<D, 2, STRIPE>(a, s);
   return launch_one<D, 1, STRIPE>(a, s);
