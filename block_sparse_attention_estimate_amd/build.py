@@ -13,7 +13,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsa.so")
 SOURCES = ["sa_api.hip", "est_kernels.hip", "attn_kernels.hip", "decode_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-ffp-contract=fast",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=fast",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
          # packed fp32 VALU instructions stay disabled in all device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

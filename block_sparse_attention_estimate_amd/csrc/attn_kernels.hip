@@ -414,6 +414,8 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 template <int D, int HPW>
 __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
+  // The host pass only needs this kernel's signature (for its launch stub).
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NWV = 2 * HPW;             // waves: 2 slices of 32 rows per head
   constexpr int KS = D / 16;               // k-steps of S^T
   constexpr int DM = D / 32;               // d tiles of O^T
@@ -423,7 +425,11 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   constexpr int KREG = 64 * KPITCH, VREG = 64 * VPITCH;
   constexpr int KWIN = KREG / 1024, VWIN = VREG / 1024, NWIN = KWIN + VWIN;
   constexpr int STAGE = KREG + VREG;
-  constexpr int SLOTS = (NWIN + NWV - 1) / NWV;      // DMA windows per wave per tile
+  // DMA: the first half of the waves loads the K windows of a stage, the second half the V
+  // windows; every wave issues SLOTS loads per tile (surplus slots go to `spare`)
+  constexpr int HW = NWV / 2;
+  constexpr int SLOTS = (KWIN + HW - 1) / HW > (VWIN + HW - 1) / HW ? (KWIN + HW - 1) / HW
+                                                                      : (VWIN + HW - 1) / HW;
   static_assert(KREG % 1024 == 0 && VREG % 1024 == 0, "DMA windows must tile the stage");
   // four stages as distinct objects, so the compiler can tell a load into one stage from
   // reads of another; windows past NWIN (to give every wave the same count) go to `spare`
@@ -433,7 +439,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st3[STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char spare[1024];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
 
   // ---- work item (longest first; both halves of a query block on one XCD) ----
   int w = blockIdx.x;
@@ -475,46 +482,46 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
   }
 
-  // ---- DMA slots of this wave: window j = wave + k * NWV of each stage ----
-  const uint16_t* kg = a.k + b * a.ks0 + g * a.ks2;
-  const uint16_t* vg = a.v + b * a.vs0 + g * a.vs2;
-  int s_row[SLOTS], s_off[SLOTS];
+  // ---- DMA slots of this wave ----
+  const bool dma_v = wave >= HW;                       // this wave loads V windows
+  const int wbase = (dma_v ? wave - HW : wave) * SLOTS;  // first window of this wave
+  const int nwin = dma_v ? VWIN : KWIN;
+  const int pitch_b = dma_v ? VPITCH : KPITCH;
+  const int64_t tstride = dma_v ? a.vs1 : a.ks1;       // elements between key rows
+  const uint16_t* gbase = dma_v ? a.v + b * a.vs0 + g * a.vs2 : a.k + b * a.ks0 + g * a.ks2;
+  const int region = dma_v ? KREG : 0;
+  int s_off[SLOTS];                                    // element offset in a full tile
 #pragma unroll
   for (int k = 0; k < SLOTS; ++k) {
-    const int j = min(wave + k * NWV, NWIN - 1);
-    const bool isv = j >= KWIN;
-    const int o = (isv ? j - KWIN : j) * 1024 + lane * 16;
-    const int pitch = isv ? VPITCH : KPITCH;
-    const int r = o / pitch;
-    const int cb = o % pitch;
-    const int c = cb < ROWB ? cb / 16 : 0;          // pad bytes receive a harmless copy
-    s_row[k] = r;
-    s_off[k] = r * (int)(isv ? a.vs1 : a.ks1) + c * 8;
+    const int o = min(wbase + k, nwin - 1) * 1024 + lane * 16;
+    const int r = o / pitch_b, cb = o % pitch_b;
+    s_off[k] = r * (int)tstride + (cb < ROWB ? cb / 16 : 0) * 8;   // pads get a harmless copy
   }
-  // Issue the DMA of tile t (clamped to the list) into stage S.  Every wave issues exactly
+  // Issue the DMA of tile t (clamped to the list) into the stage at stb.  Every wave issues exactly
   // SLOTS loads per call, so the vmcnt waits below are compile-time constants.
-  auto issue = [&]<int S>(int t) {
-    unsigned char* stb = S == 0 ? st0 : S == 1 ? st1 : S == 2 ? st2 : st3;
+  auto issue = [&](unsigned char* stb, int t) {
     const int t0 = list[min(t, n - 1)] * 64;
-    const bool fast = t0 + 63 < a.N;
-    const int64_t kb = (int64_t)t0 * a.ks1, vb = (int64_t)t0 * a.vs1;
+    if (t0 + 63 < a.N) {
+      const uint16_t* tb = gbase + (int64_t)t0 * tstride;
 #pragma unroll
-    for (int k = 0; k < SLOTS; ++k) {
-      const int j = wave + k * NWV;
-      const bool isv = min(j, NWIN - 1) >= KWIN;
-      const uint16_t* src;
-      if (fast) {
-        src = isv ? vg + vb + s_off[k] : kg + kb + s_off[k];
-      } else {
-        const int tok = min(t0 + s_row[k], a.N - 1);
-        const int coff = s_off[k] - s_row[k] * (int)(isv ? a.vs1 : a.ks1);
-        src = isv ? vg + (int64_t)tok * a.vs1 + coff : kg + (int64_t)tok * a.ks1 + coff;
+      for (int k = 0; k < SLOTS; ++k) {
+        if (wbase + k < nwin)
+          __builtin_amdgcn_global_load_lds(tb + s_off[k], LDS_PTR(void, stb + region + (wbase + k) * 1024), 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(tb + s_off[k], LDS_PTR(void, spare), 16, 0, 0);
       }
-      if (j < NWIN) {
-        unsigned char* dst = stb + (isv ? KREG + (j - KWIN) * 1024 : j * 1024);
-        __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, dst), 16, 0, 0);
-      } else {
-        __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, spare), 16, 0, 0);
+    } else {
+      // ragged last block: rows past the end read the last row
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k) {
+        const int o = min(wbase + k, nwin - 1) * 1024 + lane * 16;
+        const int r = o / pitch_b;
+        const int tok = min(t0 + r, a.N - 1);
+        const uint16_t* src = gbase + (int64_t)tok * tstride + (s_off[k] - r * (int)tstride);
+        if (wbase + k < nwin)
+          __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, stb + region + (wbase + k) * 1024), 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, spare), 16, 0, 0);
       }
     }
   };
@@ -532,12 +539,9 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // one tile: S^T = K Q^T, mask (tail tiles), online softmax (log2 domain, lazy rescale as in
-  // attn_sparse), O^T += V^T P^T with transposing V reads; then the DMA of tile t+3, the wait
-  // for tile t+1 and the barrier
-  auto step = [&]<int S>(int t) {
-    unsigned char* sb = S == 0 ? st0 : S == 1 ? st1 : S == 2 ? st2 : st3;
-    f32x16 sacc[2];
+  // ---- the three phases of a tile ----
+  // S^T = K Q^T from the stage at sb
+  auto qk = [&](const unsigned char* sb, f32x16* sacc) {
     sacc[0] = (f32x16){};
     sacc[1] = (f32x16){};
 #pragma unroll
@@ -547,6 +551,10 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
         const bf16x8 kf = *(const bf16x8*)(sb + k_rd + mt * 32 * KPITCH + ks * 32);
         sacc[mt] = mfma_bf16(kf, qf[ks], sacc[mt]);
       }
+  };
+  // mask (tail tiles), online softmax in the log2 domain with lazy rescale (the running max
+  // moves only when a row's max exceeds it by more than 8), P^T in bf16 and the row sums
+  auto softmax = [&](int t, f32x16* sacc, bf16x8* pf) {
     if (t >= n_main) {
       const int Jb = list[t];
 #pragma unroll
@@ -557,43 +565,41 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
           if (tok > row || tok >= a.N) sacc[mt][r] = NEG_INF;
         }
     }
-    {
-      float v = NEG_INF;
+    float v = NEG_INF;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][r]);
-      v = half_pair_max(v) * sl2;
-      if (__any(v > m_run + 8.0f)) {
-        const float mnew = fmaxf(m_run, v);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-        m_run = mnew;
-        l_run *= alpha;
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][r]);
+    v = half_pair_max(v) * sl2;
+    if (__any(v > m_run + 8.0f)) {
+      const float mnew = fmaxf(m_run, v);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      m_run = mnew;
+      l_run *= alpha;
 #pragma unroll
-        for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
-      }
+      for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
     }
-    bf16x8 pf[4];
-    {
-      const float mneg = -m_run;
-      float ls = l_run;
+    const float mneg = -m_run;
+    float ls = l_run;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          f32x8 tt;
+      for (int s2 = 0; s2 < 2; ++s2) {
+        f32x8 tt;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * s2 + e], sl2, mneg));
-          const bf16x8 pb = __builtin_convertvector(tt, bf16x8);
-          pf[mt * 2 + s2] = pb;
+        for (int e = 0; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * s2 + e], sl2, mneg));
+        const bf16x8 pb = __builtin_convertvector(tt, bf16x8);
+        pf[mt * 2 + s2] = pb;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pr = {pb[e], pb[e + 1]};
-            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
-          }
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pb[e], pb[e + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
         }
-      l_run = ls;
-    }
+      }
+    l_run = ls;
+  };
+  // O^T += V^T P^T with transposing V reads from the stage at sb
+  auto pv = [&](const unsigned char* sb, const bf16x8* pf) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
@@ -606,27 +612,64 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
         __builtin_memcpy(&vf, both, 16);
         oacc[dm] = mfma_bf16(vf, pf[s4], oacc[dm]);
       }
-    issue.template operator()<(S + 3) & 3>(t + 3);
-    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(2 * SLOTS));
-    __syncthreads();
   };
 
+  // Two wave groups one phase apart.  Group A (waves 0..NWV/2-1) runs S(t), softmax(t),
+  // PV(t) in step t; group B runs PV(t-1), S(t), softmax(t), so one group's exponentials
+  // overlap the other group's MFMAs on the same SIMD.  Every step ends with the DMA of tile
+  // t+2 into stage (t+2)%4, the wait for tile t+1 and one barrier; group B still reads stage
+  // (t-1)%4 in step t, which no DMA of step t touches.
+  const bool grp_b = wave >= NWV / 2;
   if (n > 0) {
-    issue.template operator()<0>(0);
-    issue.template operator()<1>(1);
-    issue.template operator()<2>(2);
-    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(2 * SLOTS));
+    issue(st0, 0);
+    issue(st1, 1);
+    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(SLOTS));
     __syncthreads();
-    int t = 0;
-    for (; t + 4 <= n; t += 4) {
-      step.template operator()<0>(t);
-      step.template operator()<1>(t + 1);
-      step.template operator()<2>(t + 2);
-      step.template operator()<3>(t + 3);
+    f32x16 sacc[2];
+    bf16x8 pf[4];
+    if (!grp_b) {
+      auto step = [&](unsigned char* sb, unsigned char* sd, int t) {
+        qk(sb, sacc);
+        softmax(t, sacc, pf);
+        pv(sb, pf);
+        issue(sd, t + 2);
+        __builtin_amdgcn_s_waitcnt(VMCNT_IMM(SLOTS));
+        __syncthreads();
+      };
+      int t = 0;
+      for (; t + 4 <= n; t += 4) {
+        step(st0, st2, t);
+        step(st1, st3, t + 1);
+        step(st2, st0, t + 2);
+        step(st3, st1, t + 3);
+      }
+      if (t < n) step(st0, st2, t);
+      if (t + 1 < n) step(st1, st3, t + 1);
+      if (t + 2 < n) step(st2, st0, t + 2);
+    } else {
+      auto step = [&](const unsigned char* sp, unsigned char* sb, unsigned char* sd, int t) {
+        if (t > 0) pv(sp, pf);
+        qk(sb, sacc);
+        softmax(t, sacc, pf);
+        issue(sd, t + 2);
+        __builtin_amdgcn_s_waitcnt(VMCNT_IMM(SLOTS));
+        __syncthreads();
+      };
+      int t = 0;
+      for (; t + 4 <= n; t += 4) {
+        step(st3, st0, st2, t);
+        step(st0, st1, st3, t + 1);
+        step(st1, st2, st0, t + 2);
+        step(st2, st3, st1, t + 3);
+      }
+      if (t < n) step(st3, st0, st2, t);
+      if (t + 1 < n) step(st0, st1, st3, t + 1);
+      if (t + 2 < n) step(st1, st2, st0, t + 2);
+      // the last tile's PV (its stage is not overwritten: the remaining DMAs are clamped
+      // re-loads of the last tile into the two stages after it)
+      const int lst = (n - 1) & 3;
+      pv(lst == 0 ? st0 : lst == 1 ? st1 : lst == 2 ? st2 : st3, pf);
     }
-    if (t < n) step.template operator()<0>(t);
-    if (t + 1 < n) step.template operator()<1>(t + 1);
-    if (t + 2 < n) step.template operator()<2>(t + 2);
     // no DMA may still be writing this workgroup's LDS when it exits
     __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
   }
@@ -649,6 +692,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
       a.lse[((int64_t)b * a.Hq + h) * a.N + row] =
           lt > 0.f ? (m_run + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 // ---------------------------------------------------------------------------------------

@@ -81,6 +81,12 @@ SA_DEV int swap_halves_i(int v) {
   return __shfl_xor(v, 32);
 }
 
+// Wave-uniform copy of a value that is uniform across the wave (lets the compiler keep it in
+// scalar registers and branch on it without exec-mask handling).
+SA_DEV int wave_uniform(int v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger unsigned).
 SA_DEV unsigned int float_order_key(float f) {
   unsigned int u = __float_as_uint(f);
