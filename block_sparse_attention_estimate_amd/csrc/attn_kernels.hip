@@ -409,6 +409,22 @@ __global__ __launch_bounds__(128 * HPW) void attn_sparse(AttnArgs a) {
 // ---------------------------------------------------------------------------------------
 // s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at their maxima)
 #define VMCNT_IMM(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+// the same with lgkmcnt = 0 as well (every LDS read and scalar load of this wave returned)
+#define VMCNT_LGKM0_IMM(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
+
+// Workgroup barrier for the DMA pipeline.  __syncthreads() carries a workgroup release fence,
+// and since the direct-to-LDS loads write LDS the fence makes the compiler wait for every one
+// of them (vmcnt(0)) -- including the prefetch just issued.  Here the wait is explicit: this
+// wave's DMAs older than the newest n are complete and its LDS reads have returned; after the
+// barrier the same holds for every wave.  The empty asm statements keep the compiler from
+// moving memory operations across the barrier.
+#define DMA_BARRIER(n)                                   \
+  do {                                                   \
+    __builtin_amdgcn_s_waitcnt(VMCNT_LGKM0_IMM(n));      \
+    asm volatile("" ::: "memory");                       \
+    __builtin_amdgcn_s_barrier();                        \
+    asm volatile("" ::: "memory");                       \
+  } while (0)
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -499,8 +515,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   }
   // Issue the DMA of tile t (clamped to the list) into the stage at stb.  Every wave issues exactly
   // SLOTS loads per call, so the vmcnt waits below are compile-time constants.
-  auto issue = [&](unsigned char* stb, int t) {
-    const int t0 = list[min(t, n - 1)] * 64;
+  auto issue = [&](unsigned char* stb, int jb) {
+    const int t0 = jb * 64;
     if (t0 + 63 < a.N) {
       const uint16_t* tb = gbase + (int64_t)t0 * tstride;
 #pragma unroll
@@ -539,7 +555,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // ---- the three phases of a tile ----
+  // ---- the phases of a tile ----
   // S^T = K Q^T from the stage at sb
   auto qk = [&](const unsigned char* sb, f32x16* sacc) {
     sacc[0] = (f32x16){};
@@ -552,35 +568,21 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
         sacc[mt] = mfma_bf16(kf, qf[ks], sacc[mt]);
       }
   };
-  // mask (tail tiles), online softmax in the log2 domain with lazy rescale (the running max
-  // moves only when a row's max exceeds it by more than 8), P^T in bf16 and the row sums
-  auto softmax = [&](int t, f32x16* sacc, bf16x8* pf) {
-    if (t >= n_main) {
-      const int Jb = list[t];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = Jb * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
-          if (tok > row || tok >= a.N) sacc[mt][r] = NEG_INF;
-        }
-    }
-    float v = NEG_INF;
+  // entries of tile t past the diagonal or the end of the sequence
+  auto mask = [&](int t, f32x16* sacc) {
+    const int Jb = list[t];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][r]);
-    v = half_pair_max(v) * sl2;
-    if (__any(v > m_run + 8.0f)) {
-      const float mnew = fmaxf(m_run, v);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-      m_run = mnew;
-      l_run *= alpha;
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int tok = Jb * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+        if (tok > row || tok >= a.N) sacc[mt][r] = NEG_INF;
+      }
+  };
+  // P^T = exp2(S^T scale - m) in bf16; returns this lane's sum of the rounded values
+  auto expo = [&](const f32x16* sacc, bf16x8* pf) -> float {
     const float mneg = -m_run;
-    float ls = l_run;
+    float ls = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -596,7 +598,28 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
           ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
         }
       }
-    l_run = ls;
+    return ls;
+  };
+  // The running max m stays fixed while every P value of a tile is at most 2^16 (checked on the
+  // lane's partial row sum, which bounds each value).  A tile that breaks the bound (scores more
+  // than 16 above m in the log2 domain, or the first tile, while m is still -1e30) moves m to
+  // the tile's row max, rescales O and l and recomputes P.  No per-tile row max is taken.
+  auto settle = [&](const f32x16* sacc, bf16x8* pf, float ts) {
+    if (__any(!(ts <= 65536.0f))) {
+      float v = NEG_INF;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][r]);
+      const float mnew = fmaxf(m_run, half_pair_max(v) * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      m_run = mnew;
+      l_run *= alpha;
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+      ts = expo(sacc, pf);
+    }
+    l_run += ts;
   };
   // O^T += V^T P^T with transposing V reads from the stage at sb
   auto pv = [&](const unsigned char* sb, const bf16x8* pf) {
@@ -614,61 +637,65 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
       }
   };
 
-  // Two wave groups one phase apart.  Group A (waves 0..NWV/2-1) runs S(t), softmax(t),
-  // PV(t) in step t; group B runs PV(t-1), S(t), softmax(t), so one group's exponentials
-  // overlap the other group's MFMAs on the same SIMD.  Every step ends with the DMA of tile
-  // t+2 into stage (t+2)%4, the wait for tile t+1 and one barrier; group B still reads stage
-  // (t-1)%4 in step t, which no DMA of step t touches.
-  const bool grp_b = wave >= NWV / 2;
+  // Software pipeline over the list.  On entry to step t, S(t) is in `cur` (masked).  Step t
+  // computes P(t) while the MFMAs of S(t+1) run, then P V(t), issues the DMA of tile t+3 into
+  // the stage of tile t-1 and waits for tile t+2, so at every barrier only the newest tile is
+  // in flight.
   if (n > 0) {
-    issue(st0, 0);
-    issue(st1, 1);
-    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(SLOTS));
-    __syncthreads();
-    f32x16 sacc[2];
-    bf16x8 pf[4];
-    if (!grp_b) {
-      auto step = [&](unsigned char* sb, unsigned char* sd, int t) {
-        qk(sb, sacc);
-        softmax(t, sacc, pf);
-        pv(sb, pf);
-        issue(sd, t + 2);
-        __builtin_amdgcn_s_waitcnt(VMCNT_IMM(SLOTS));
-        __syncthreads();
-      };
-      int t = 0;
-      for (; t + 4 <= n; t += 4) {
-        step(st0, st2, t);
-        step(st1, st3, t + 1);
-        step(st2, st0, t + 2);
-        step(st3, st1, t + 3);
-      }
-      if (t < n) step(st0, st2, t);
-      if (t + 1 < n) step(st1, st3, t + 1);
-      if (t + 2 < n) step(st2, st0, t + 2);
+    issue(st0, list[0]);
+    issue(st1, list[min(1, n - 1)]);
+    issue(st2, list[min(2, n - 1)]);
+    DMA_BARRIER(SLOTS);
+    f32x16 sa[2], sbb[2];
+    qk(st0, sa);
+    if (n_main == 0) mask(0, sa);
+    auto step = [&](unsigned char* sc, unsigned char* sn, unsigned char* sd, int t,
+                    f32x16* cur, f32x16* nxt, bool may_mask) {
+      const int jd = list[min(t + 3, n - 1)];
+      bf16x8 pf[4];
+      const float ts = expo(cur, pf);
+      qk(sn, nxt);
+      settle(cur, pf, ts);
+      pv(sc, pf);
+      if (may_mask && t + 1 >= n_main) mask(t + 1, nxt);
+      issue(sd, jd);
+      DMA_BARRIER(SLOTS);
+    };
+    auto last = [&](unsigned char* sc, f32x16* cur) {
+      bf16x8 pf[4];
+      const float ts = expo(cur, pf);
+      settle(cur, pf, ts);
+      pv(sc, pf);
+    };
+    int t = 0;
+    for (; t + 4 < n_main; t += 4) {          // the next tile of every step needs no mask
+      step(st0, st1, st3, t, sa, sbb, false);
+      step(st1, st2, st0, t + 1, sbb, sa, false);
+      step(st2, st3, st1, t + 2, sa, sbb, false);
+      step(st3, st0, st2, t + 3, sbb, sa, false);
+    }
+    for (; t + 4 < n; t += 4) {
+      step(st0, st1, st3, t, sa, sbb, true);
+      step(st1, st2, st0, t + 1, sbb, sa, true);
+      step(st2, st3, st1, t + 2, sa, sbb, true);
+      step(st3, st0, st2, t + 3, sbb, sa, true);
+    }
+    // steps t .. n-2 (at most three) and the last tile n-1 <= t+3
+    if (t + 1 >= n) {
+      last(st0, sa);
     } else {
-      auto step = [&](const unsigned char* sp, unsigned char* sb, unsigned char* sd, int t) {
-        if (t > 0) pv(sp, pf);
-        qk(sb, sacc);
-        softmax(t, sacc, pf);
-        issue(sd, t + 2);
-        __builtin_amdgcn_s_waitcnt(VMCNT_IMM(SLOTS));
-        __syncthreads();
-      };
-      int t = 0;
-      for (; t + 4 <= n; t += 4) {
-        step(st3, st0, st2, t);
-        step(st0, st1, st3, t + 1);
-        step(st1, st2, st0, t + 2);
-        step(st2, st3, st1, t + 3);
+      step(st0, st1, st3, t, sa, sbb, true);
+      if (t + 2 >= n) {
+        last(st1, sbb);
+      } else {
+        step(st1, st2, st0, t + 1, sbb, sa, true);
+        if (t + 3 >= n) {
+          last(st2, sa);
+        } else {
+          step(st2, st3, st1, t + 2, sa, sbb, true);
+          last(st3, sbb);
+        }
       }
-      if (t < n) step(st3, st0, st2, t);
-      if (t + 1 < n) step(st0, st1, st3, t + 1);
-      if (t + 2 < n) step(st1, st2, st0, t + 2);
-      // the last tile's PV (its stage is not overwritten: the remaining DMAs are clamped
-      // re-loads of the last tile into the two stages after it)
-      const int lst = (n - 1) & 3;
-      pv(lst == 0 ? st0 : lst == 1 ? st1 : lst == 2 ? st2 : st3, pf);
     }
     // no DMA may still be writing this workgroup's LDS when it exits
     __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
