@@ -110,7 +110,7 @@ def to_dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def cpu_baseline_prefill(x, dense_flops, n_est_rows=128, n_attn_rows=128, seed=1):
+def cpu_baseline_prefill(x, dense_flops, n_est_rows=512, n_attn_rows=512, seed=1):
     """The oracle (numpy fp64) on a bounded random sample of the same workload: estimate
     rows (b, g, i) and attention query blocks (b, h, i) drawn uniformly, timed separately and
     scaled by total rows / sampled rows to a whole-layer time."""
@@ -219,6 +219,8 @@ def bench_prefill(args, dev):
     est_avg = float(np.mean(est_ms))
     achieved = kept_flops / (att_avg * 1e-3) / 1e12
     per_group = (counts.sum(axis=(0, 2)) / (cands.sum() * B)).round(4).tolist()
+    # the attention kernel the library launches for these lists
+    kernel = "attn_block" if x.granularity == "block" else "attn_sparse"
     out = {
         "metric": "ms/layer & dense-equiv TFLOP/s (fraction of MFMA peak) for sparse prefill @128K",
         "value": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
@@ -240,8 +242,8 @@ def bench_prefill(args, dev):
         "kept_tile_frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(f"attn_sparse_{args.workload}_traffic", ATTN_SRC),
-                     "kernel": "attn_sparse (sa_sparse_prefill)",
+                     "traffic": traffic_from_profile(f"{kernel}_{args.workload}_traffic", ATTN_SRC),
+                     "kernel": f"{kernel} (sa_sparse_prefill)",
                      "units": f"{kept_units} kept (head, {x.block_q}x{x.block_k} tile) x "
                               f"{flops_per_unit / 1e6:.3f} MFLOP"},
     }
@@ -308,7 +310,7 @@ def main():
                     help="after timing, run one plain 1 GiB device copy (byte-counter scale)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--kernel", default="attn_sparse")
+    ap.add_argument("--kernel", default="attn_block")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.summarize_pmc:

@@ -470,7 +470,9 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   rest /= a.n_hp;
   const int BG = a.B * a.Hkv;
   const int i_rev = rest / BG;
-  const int gb = (rest % BG + i_rev) % BG;
+  // the KV group rotates every 16 query blocks: the ~16 work items an XCD runs at a time share
+  // one group's K/V in that XCD's L2, while over the launch every XCD sees every group
+  const int gb = (rest % BG + i_rev / 16) % BG;
   const int g = gb % a.Hkv;
   const int b = gb / a.Hkv;
   const int iq = a.nQB - 1 - i_rev;
