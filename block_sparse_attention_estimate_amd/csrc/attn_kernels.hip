@@ -407,10 +407,6 @@ __global__ __launch_bounds__(128 * HPW) void attn_sparse(AttnArgs a) {
 //    [d0 + 4(j%4), +4) of key row k0 + j/4, and the read returns to lane i the 4 keys
 //    k0..k0+3 of dim d0 + i -- exactly the 4 keys the P^T register layout pairs with that lane.
 // ---------------------------------------------------------------------------------------
-// s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at their maxima)
-#define VMCNT_IMM(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
-// the same with lgkmcnt = 0 as well (every LDS read and scalar load of this wave returned)
-#define VMCNT_LGKM0_IMM(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
 
 // Workgroup barrier for the DMA pipeline.  __syncthreads() carries a workgroup release fence,
 // and since the direct-to-LDS loads write LDS the fence makes the compiler wait for every one
@@ -425,8 +421,6 @@ __global__ __launch_bounds__(128 * HPW) void attn_sparse(AttnArgs a) {
     __builtin_amdgcn_s_barrier();                        \
     asm volatile("" ::: "memory");                       \
   } while (0)
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 template <int D, int HPW>
 __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {

@@ -9,10 +9,14 @@
 //
 // Kernels:
 //   dec_block_summary  kbar[b, J, g, :] = mean of the block's cached keys (fp64 -> fp32 -> bf16)
-//   dec_score          score[b, g, J] = max over the group's heads of c * q_h . kbar_J
-//   dec_select         forced blocks + top (K - |F|) others by (score desc, block asc),
-//                      bitonic sort of 64-bit keys in LDS, ascending output list
-//   dec_splitk         per (b, g, split): 16-lane groups stream the split's selected keys
+//   dec_score_rows     score[b, g, J] = max over the group's heads of c * q_h . kbar_J, one
+//                      coalesced summary row per 16-lane group, DPP reductions
+//   dec_select_radix   forced blocks + top (K - |F|) others by (score desc, block asc): radix
+//                      select of the K-th key (8 bits per pass), ascending output list
+//   dec_splitk_mfma    64-key blocks: per (b, g, split), each wave takes whole blocks; the G
+//                      heads are the 32-wide row dimension of S^T = K Q^T and O^T = V^T P^T
+//                      on bf16 MFMA, K/V go HBM -> LDS by direct loads; one partial per split
+//   dec_splitk         other block sizes: 16-lane groups stream the split's selected keys
 //                      (one 16-byte K and V slice per lane), online softmax for the G packed
 //                      heads, merged in-wave then across waves into one partial (m, l, acc)
 //   dec_combine        LSE merge of the partials -> O (bf16) and LSE
@@ -41,93 +45,166 @@ __global__ __launch_bounds__(D) void dec_block_summary(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void dec_score(DecArgs a) {
+// Sum of a value over each 16-lane row of the wave with DPP (the result in every lane).
+SA_DEV float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // half mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // mirror
+  return v;
+}
+
+// score[b, g, J] = c * max over the G heads of q_h . kbar[b, J, g].  A 16-lane group reads one
+// summary row (d bf16 values) with one load per lane and reduces the per-head dot products
+// over the group with DPP; each workgroup covers 64 blocks (4 per group, loaded up front).
+template <int D, int G>
+__global__ __launch_bounds__(256) void dec_score_rows(DecArgs a) {
+  constexpr int DPL = D / 16;              // dims per lane (8 or 4)
+  constexpr int RPG = 4;                   // rows per group
   const int g = blockIdx.y, b = blockIdx.z;
-  const int J = blockIdx.x * 256 + threadIdx.x;
-  __shared__ float qs[8][D];
-  for (int p = threadIdx.x; p < a.G * D; p += 256) {
-    const int hg = p / D, d = p % D;
-    qs[hg][d] = bf16_bits_to_float(a.q[b * a.qs0 + (g * a.G + hg) * a.qs2 + d]);
-  }
-  __syncthreads();
-  if (J >= a.nKB) return;
+  const int tid = threadIdx.x, sub = tid & 15, grp = tid >> 4;
   const int nb = (min(max(a.cache_len[b], 0), a.L) + a.bk - 1) / a.bk;
-  float score = NEG_INF;
-  if (J < nb) {
-    const uint16_t* kp = a.ksum + (((int64_t)b * a.nKB + J) * a.Hkv + g) * D;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int d0 = 0; d0 < D; d0 += 8) {
-      const u16x8 kv = *(const u16x8*)(kp + d0);
+  float qv[G][DPL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = bf16_bits_to_float(kv[e]);
+  for (int hg = 0; hg < G; ++hg) {
+    const uint16_t* qp = a.q + b * a.qs0 + (g * G + hg) * a.qs2 + sub * DPL;
 #pragma unroll
-        for (int hg = 0; hg < 8; ++hg)
-          if (hg < a.G) acc[hg] = fmaf(qs[hg][d0 + e], x, acc[hg]);
-      }
-    }
-    float mx = acc[0];
-#pragma unroll
-    for (int hg = 1; hg < 8; ++hg)
-      if (hg < a.G) mx = fmaxf(mx, acc[hg]);
-    score = mx * a.c;
+    for (int e = 0; e < DPL; ++e) qv[hg][e] = bf16_bits_to_float(qp[e]);
   }
-  a.scores[((int64_t)b * a.Hkv + g) * a.nKB + J] = score;
+  const int J0 = blockIdx.x * 16 * RPG + grp;
+  float kx[RPG][DPL];
+#pragma unroll
+  for (int r = 0; r < RPG; ++r) {
+    const int J = min(J0 + 16 * r, a.nKB - 1);
+    const uint16_t* kp = a.ksum + (((int64_t)b * a.nKB + J) * a.Hkv + g) * D + sub * DPL;
+    if (DPL == 8) {
+      const u16x8 u = *(const u16x8*)kp;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) kx[r][e] = bf16_bits_to_float(u[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) kx[r][e] = bf16_bits_to_float(kp[e]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPG; ++r) {
+    const int J = J0 + 16 * r;
+    float mx = NEG_INF;
+#pragma unroll
+    for (int hg = 0; hg < G; ++hg) {
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) p = fmaf(qv[hg][e], kx[r][e], p);
+      mx = fmaxf(mx, row16_sum(p));
+    }
+    if (sub == 0 && J < a.nKB)
+      a.scores[((int64_t)b * a.Hkv + g) * a.nKB + J] = J < nb ? mx * a.c : NEG_INF;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
-// NP = power of two >= nKB (<= 8192).  One workgroup of 1024 threads per (b, g).
-template <int NP>
-__global__ __launch_bounds__(1024) void dec_select(DecArgs a) {
+// Top-K by radix select.  One workgroup per (b, g).  Each candidate block j < nb gets the
+// order-preserving 32-bit key of its score (forced blocks: the maximum key); the K-th largest
+// key T is found 8 bits at a time from per-digit histograms, then the output takes every key
+// above T and, among keys equal to T, the smallest block ids (the order (key desc, block asc)
+// of the sort it replaces), written in ascending block order.
+__global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  __shared__ unsigned long long keys[NP];
-  __shared__ unsigned char flag[NP];
-  __shared__ int wsum[16];
+  extern __shared__ unsigned int skey[];          // [nKB]
+  __shared__ unsigned int hist[256];
+  __shared__ unsigned int s_prefix, s_need;
+  __shared__ int wsum[4];
   const int lb = min(max(a.cache_len[b], 0), a.L);
   const int nb = (lb + a.bk - 1) / a.bk;
   const float* sc = a.scores + ((int64_t)b * a.Hkv + g) * a.nKB;
-  for (int j = tid; j < NP; j += 1024) {
-    unsigned long long key = 0ull;
-    if (j < nb) {
-      const bool forced = (j * a.bk < a.sink) || ((j + 1) * a.bk - 1 >= lb - a.local);
-      const unsigned int hi = forced ? 0xFFFFFFFFu : float_order_key(sc[j]);
-      key = ((unsigned long long)hi << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned int)j);
-    }
-    keys[j] = key;
-    flag[j] = 0;
+  for (int j = tid; j < nb; j += 256) {
+    const bool forced = (j * a.bk < a.sink) || ((j + 1) * a.bk - 1 >= lb - a.local);
+    skey[j] = forced ? 0xFFFFFFFFu : float_order_key(sc[j]);
   }
   __syncthreads();
-  // bitonic sort, descending
-  for (int k = 2; k <= NP; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < NP; i += 1024) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = keys[i], y = keys[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            keys[i] = y;
-            keys[ixj] = x;
+  const int kk = min(a.top_k, nb);
+  unsigned int prefix = 0, need = (unsigned int)kk;   // keys matching prefix on the digits so far
+  if (kk < nb) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      const unsigned int hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      for (int j = tid; j < nb; j += 256) {
+        const unsigned int k = skey[j];
+        if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // counts of digits >= d, scanned from the top: lane l owns digits 4l .. 4l+3
+        unsigned int c[4], tot = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c[e] = hist[4 * tid + e];
+          tot += c[e];
+        }
+        // suffix sum over lanes (digits above this lane's)
+        unsigned int above = tot;
+        for (int o = 1; o < 64; o <<= 1) {
+          const unsigned int t = __shfl_down(above, o);
+          if (tid + o < 64) above += t;
+        }
+        above -= tot;                                   // keys with a larger digit
+        unsigned int run = above;
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          if (run < need && run + c[e] >= need) {       // the K-th key has digit 4l+e
+            s_prefix = prefix | ((unsigned int)(4 * tid + e) << shift);
+            s_need = need - run;
           }
+          run += c[e];
         }
       }
       __syncthreads();
+      prefix = s_prefix;
+      need = s_need;
     }
   }
-  const int kk = min(a.top_k, nb);
-  for (int p = tid; p < kk; p += 1024) {
-    const unsigned int j = 0xFFFFFFFFu - (unsigned int)(keys[p] & 0xFFFFFFFFull);
-    flag[j] = 1;
-  }
-  __syncthreads();
-  // ascending compaction of the flags
-  constexpr int PER = NP / 1024 > 0 ? NP / 1024 : 1;
-  const int j0 = tid * PER;
-  int cnt = 0;
-  for (int j = j0; j < j0 + PER && j < NP; ++j) cnt += flag[j];
+  // flags: key > T, or key == T among the first `need` equal keys by block id
+  constexpr int MAXPER = 32;                          // nKB <= 8192 = 256 * 32
+  const int per = (nb + 255) / 256;
+  const int j0 = tid * per;
+  int eq = 0;
+  if (kk < nb)
+    for (int e = 0; e < per && j0 + e < nb; ++e) eq += skey[j0 + e] == prefix;
+  // exclusive prefix of equal keys over the threads (block order)
   const int lane = tid & 63, wave = tid >> 6;
-  int incl = cnt;
+  int incl = eq;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int eq_before = incl - eq;
+  for (int w = 0; w < wave; ++w) eq_before += wsum[w];
+  __syncthreads();
+  unsigned int sel_bits = 0;                           // bit e: block j0 + e selected
+  int cnt = 0;
+  for (int e = 0; e < per && e < MAXPER && j0 + e < nb; ++e) {
+    const unsigned int k = skey[j0 + e];
+    bool take;
+    if (kk >= nb) {
+      take = true;
+    } else if (k > prefix) {
+      take = true;
+    } else if (k == prefix) {
+      take = (unsigned int)eq_before < need;
+      ++eq_before;
+    } else {
+      take = false;
+    }
+    if (take) {
+      sel_bits |= 1u << e;
+      ++cnt;
+    }
+  }
+  // ascending compaction
+  incl = cnt;
   for (int o = 1; o < 64; o <<= 1) {
     const int t = __shfl_up(incl, o);
     if (lane >= o) incl += t;
@@ -137,9 +214,9 @@ __global__ __launch_bounds__(1024) void dec_select(DecArgs a) {
   int pos = incl - cnt;
   for (int w = 0; w < wave; ++w) pos += wsum[w];
   int32_t* out = a.selected + ((int64_t)b * a.Hkv + g) * a.top_k;
-  for (int j = j0; j < j0 + PER && j < NP; ++j)
-    if (flag[j]) out[pos++] = j;
-  for (int p = kk + tid; p < a.top_k; p += 1024) out[p] = -1;
+  for (int e = 0; e < per && e < MAXPER; ++e)
+    if (sel_bits & (1u << e)) out[pos++] = j0 + e;
+  for (int p = kk + tid; p < a.top_k; p += 256) out[p] = -1;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -289,6 +366,187 @@ __global__ __launch_bounds__(256) void dec_splitk(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Split-K attention for 64-key blocks on MFMA.  The G query heads of a KV head play the role
+// of the query rows of the prefill kernel: S^T = K Q^T with Q^T's 32 columns holding the G
+// heads (zero beyond G), so each lane owns one head and 16 keys of each 32-key half and the
+// softmax statistics stay in-lane (plus one exchange with lane ^ 32); P^T stays in registers
+// as the B operand of O^T += V^T P^T.  Each wave of the workgroup takes the split's blocks
+// w, w + 4, ...: the block's K rows are loaded straight into registers in the A-operand
+// layout, its V rows go HBM -> the wave's LDS region by direct loads (320-byte rows for
+// d = 128) and V^T is read with transposing LDS reads, so S and the softmax run while V is
+// still arriving.  80 KB of LDS per workgroup lets two workgroups share a CU.  The four
+// waves' (m, l, O) are merged through LDS into one partial per (b, head, split).  MFMA work
+// is 8x the useful work for G = 4 and still far below the time the K/V bytes take to arrive.
+template <int D>
+__global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
+  // The host pass only needs this kernel's signature (for its launch stub).
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KS = D / 16, DM = D / 32, ROWB = D * 2;
+  constexpr int VPITCH = D == 128 ? 320 : 192;
+  constexpr int VREG = 64 * VPITCH;
+  constexpr int VWIN = VREG / 1024;
+  static_assert(VREG % 1024 == 0, "DMA windows must tile the region");
+  static_assert(4 * VREG >= (2 * 4 * 32 + 4 * 32 * D) * 4, "merge buffers must fit the regions");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * VREG];
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
+  unsigned char* reg = lds + wave * VREG;
+  const int lb = min(max(a.cache_len[b], 0), a.L);
+  const int nb = (lb + 63) / 64;
+  const int nsel = min(a.top_k, nb);
+  const int bps = (nsel + a.n_splits - 1) / a.n_splits;
+  const int blk0 = s * bps, blk1 = min(nsel, blk0 + bps);
+  const __attribute__((address_space(4))) int32_t* sel =
+      (const __attribute__((address_space(4))) int32_t*)(a.selected + ((int64_t)b * a.Hkv + g) * a.top_k);
+  const float sl2 = a.c * 1.4426950408889634f;
+
+  // Q^T as the B operand: lane l holds head l % 32 of the group (zero beyond G)
+  bf16x8 qf[KS];
+  {
+    const int hc = min(l32, a.G - 1);
+    const uint16_t* qp = a.q + b * a.qs0 + (g * a.G + hc) * a.qs2 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = *(const bf16x8*)(qp + ks * 16);
+      if (l32 >= a.G) qf[ks] = (bf16x8){};
+    }
+  }
+  const uint16_t* kbase = a.kc + b * a.ks0 + g * a.ks2 + half * 8;
+  const uint16_t* vbase = a.vc + b * a.vs0 + g * a.vs2;
+  const int grp = lane >> 4, jj = lane & 15;
+  const int v_rd = (4 * (grp >> 1) + (jj >> 2)) * VPITCH + (16 * (grp & 1) + 4 * (jj & 3)) * 2;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+  f32x16 oacc[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) oacc[dm] = (f32x16){};
+  float m_run = -1e30f, l_run = 0.f;
+
+  for (int blk = blk0 + wave; blk < blk1; blk += 4) {
+    const int t0 = sel[blk] * 64;
+    // K rows in the A-operand layout: lane l holds key 32 mt + l % 32, dims 16 ks + 8 (l / 32)
+    // (rows past the cache end re-read the last cached row; their scores are masked below)
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int tok = min(t0 + mt * 32 + l32, lb - 1);
+      const uint16_t* kp = kbase + (int64_t)tok * a.ks1;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = *(const bf16x8*)(kp + ks * 16);
+    }
+    // V rows -> this wave's LDS region
+#pragma unroll
+    for (int w = 0; w < VWIN; ++w) {
+      const int o = w * 1024 + lane * 16;
+      const int r = o / VPITCH, cb = o % VPITCH;
+      const int tok = min(t0 + r, lb - 1);
+      __builtin_amdgcn_global_load_lds(vbase + (int64_t)tok * a.vs1 + (cb < ROWB ? cb / 2 : 0),
+                                       LDS_PTR(void, reg + w * 1024), 16, 0, 0);
+    }
+    // S^T = K Q^T (the compiler waits for the K loads only; V is still in flight)
+    f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma_bf16(kf[mt][ks], qf[ks], sacc[mt]);
+    if (t0 + 63 >= lb) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = t0 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+          if (tok >= lb) sacc[mt][r] = NEG_INF;
+        }
+    }
+    // online softmax over the block (log2 domain)
+    float v = NEG_INF;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][r]);
+    const float mnew = fmaxf(m_run, half_pair_max(v) * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+    m_run = mnew;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+    float ls = l_run * alpha;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        f32x8 tt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * s2 + e], sl2, -mnew));
+        const bf16x8 pb = __builtin_convertvector(tt, bf16x8);
+        pf[mt * 2 + s2] = pb;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pb[e], pb[e + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
+        }
+      }
+    l_run = ls;
+    // O^T += V^T P^T once this wave's V rows have landed
+    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        const unsigned char* vp = reg + v_rd + 16 * s4 * VPITCH + dm * 64;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp + 8 * VPITCH));
+        const v4i16 both[2] = {lo, hi};
+        bf16x8 vf;
+        __builtin_memcpy(&vf, both, 16);
+        oacc[dm] = mfma_bf16(vf, pf[s4], oacc[dm]);
+      }
+    // every LDS read of the region has returned before the next block's loads overwrite it
+    __builtin_amdgcn_s_waitcnt(LGKM0_IMM);
+  }
+
+  // ---- merge the four waves through LDS (the regions are free once every wave is here) ----
+  __syncthreads();
+  float* mo = (float*)lds;                     // [4][32] running max per wave and head
+  float* lo = mo + 4 * 32;                     // [4][32] row sum
+  float* ao = lo + 4 * 32;                     // [4][32][D] O per wave and head
+  const float lt = half_pair_sum(l_run);
+  if (l32 < a.G) {
+    if (half == 0) {
+      mo[wave * 32 + l32] = m_run;
+      lo[wave * 32 + l32] = lt;
+    }
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ao[(wave * 32 + l32) * D + dm * 32 + half * 4 + 8 * (r >> 2) + (r & 3)] = oacc[dm][r];
+  }
+  __syncthreads();
+  for (int p = tid; p < a.G * D; p += 256) {
+    const int hg = p / D, d = p % D;
+    float mx = mo[hg];
+    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, mo[w * 32 + hg]);
+    float ltot = 0.f, at = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float f = __builtin_amdgcn_exp2f(mo[w * 32 + hg] - mx);
+      ltot += lo[w * 32 + hg] * f;
+      at += ao[(w * 32 + hg) * D + d] * f;
+    }
+    float* part = a.partial + (((int64_t)b * a.Hq + g * a.G + hg) * a.n_splits + s) * (D + 2);
+    part[d] = at;
+    if (d == 0) {
+      part[D] = mx;
+      part[D + 1] = ltot;
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(D) void dec_combine(DecArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
@@ -322,18 +580,18 @@ hipError_t launch_block_summary(const DecArgs& a, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(dec_score<D>, dim3((a.nKB + 255) / 256, a.Hkv, a.B), dim3(256), 0, s, a);
-  const int nkb = a.nKB;
-  if (nkb <= 1024)
-    hipLaunchKernelGGL(dec_select<1024>, dim3(a.Hkv, a.B), dim3(1024), 0, s, a);
-  else if (nkb <= 2048)
-    hipLaunchKernelGGL(dec_select<2048>, dim3(a.Hkv, a.B), dim3(1024), 0, s, a);
-  else if (nkb <= 4096)
-    hipLaunchKernelGGL(dec_select<4096>, dim3(a.Hkv, a.B), dim3(1024), 0, s, a);
-  else
-    hipLaunchKernelGGL(dec_select<8192>, dim3(a.Hkv, a.B), dim3(1024), 0, s, a);
-  const dim3 grid(a.n_splits, a.Hkv, a.B);
+  const dim3 sgrid((a.nKB + 63) / 64, a.Hkv, a.B);
   switch (a.G) {
+    case 1: hipLaunchKernelGGL((dec_score_rows<D, 1>), sgrid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dec_score_rows<D, 2>), sgrid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((dec_score_rows<D, 4>), sgrid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((dec_score_rows<D, 8>), sgrid, dim3(256), 0, s, a); break;
+  }
+  hipLaunchKernelGGL(dec_select_radix, dim3(a.Hkv, a.B), dim3(256), a.nKB * sizeof(unsigned int), s, a);
+  const dim3 grid(a.n_splits, a.Hkv, a.B);
+  if (a.bk == 64) {
+    hipLaunchKernelGGL(dec_splitk_mfma<D>, grid, dim3(256), 0, s, a);
+  } else switch (a.G) {
     case 1: hipLaunchKernelGGL((dec_splitk<D, 1>), grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((dec_splitk<D, 2>), grid, dim3(256), 0, s, a); break;
     case 4: hipLaunchKernelGGL((dec_splitk<D, 4>), grid, dim3(256), 0, s, a); break;

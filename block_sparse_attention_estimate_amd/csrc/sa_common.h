@@ -15,6 +15,18 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// generic pointer -> LDS (address space 3) pointer, for the LDS-only builtins
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+// wait for vmcnt <= n only (expcnt and lgkmcnt at their maxima)
+#define VMCNT_IMM(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+// wait for vmcnt <= n and lgkmcnt = 0 (every LDS read and scalar load of this wave returned)
+#define VMCNT_LGKM0_IMM(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
+// wait for lgkmcnt = 0 only
+#define LGKM0_IMM (15 | (3 << 14) | (7 << 4))
 
 #define SA_DEV static __device__ __forceinline__
 

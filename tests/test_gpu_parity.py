@@ -134,31 +134,34 @@ def test_determinism(dev):
     assert torch.equal(l0, l1)
 
 
-@pytest.mark.parametrize("batch,seq,hq,hkv,d,top_k", [(3, 5000, 8, 2, 128, 24), (2, 3000, 4, 1, 64, 8),
-                                                     (2, 2000, 16, 2, 128, 64)])
-def test_decode_reduced(dev, batch, seq, hq, hkv, d, top_k):
+@pytest.mark.parametrize("batch,seq,hq,hkv,d,top_k,bk", [(3, 5000, 8, 2, 128, 24, 64),
+                                                        (2, 3000, 4, 1, 64, 8, 64),
+                                                        (2, 2000, 16, 2, 128, 64, 64),
+                                                        (2, 3000, 2, 2, 64, 12, 64),
+                                                        (2, 3000, 8, 2, 128, 24, 32)])
+def test_decode_reduced(dev, batch, seq, hq, hkv, d, top_k, bk):
     import torch
     import block_sparse_attention_estimate_amd as sa
     x = synth.make_decode(batch=batch, seq=seq, hq=hq, hkv=hkv, head_dim=d, top_k=top_k)
     if batch >= 2:
         x.cache_len[1] = seq - 937          # ragged cache lengths
-    log(f"decode B={batch} L={seq} Hq={hq} Hkv={hkv} d={d} K={top_k} lens={x.cache_len.tolist()}")
+    log(f"decode B={batch} L={seq} Hq={hq} Hkv={hkv} d={d} K={top_k} bk={bk} lens={x.cache_len.tolist()}")
     q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
     cl = torch.from_numpy(x.cache_len).to(dev)
-    kbar = sa.build_block_summary(kc, cl, block_k=64)
-    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=64, top_k=top_k, sink=32, local=256)
+    kbar = sa.build_block_summary(kc, cl, block_k=bk)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=bk, top_k=top_k, sink=32, local=256)
     torch.cuda.synchronize()
-    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, 64)
+    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, bk)
     kb = kbar.view(torch.int16).cpu().numpy().view(np.uint16)
     for b in range(batch):
-        nb = -(-int(x.cache_len[b]) // 64)
+        nb = -(-int(x.cache_len[b]) // bk)
         np.testing.assert_array_equal(kb[b, :nb], kbar_ref[b, :nb])
-    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=64, top_k=top_k, sink=32, local=256)
+    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=bk, top_k=top_k, sink=32, local=256)
     s = sel.cpu().numpy()
     used = {}
     flips = 0
     for (b, g), r in ref.items():
-        k_ = min(top_k, -(-int(x.cache_len[b]) // 64))
+        k_ = min(top_k, -(-int(x.cache_len[b]) // bk))
         got = s[b, g, :k_]
         assert (s[b, g, k_:] == -1).all()
         assert np.all(np.diff(got) > 0)
@@ -166,7 +169,7 @@ def test_decode_reduced(dev, batch, seq, hq, hkv, d, top_k):
         assert diff <= set(r["ambiguous"].tolist()), ((b, g), sorted(diff))
         flips += len(diff)
         used[(b, g)] = got
-    O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used, block_k=64)
+    O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used, block_k=bk)
     err = np.abs(o.float().cpu().numpy() - O)
     assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
     assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
