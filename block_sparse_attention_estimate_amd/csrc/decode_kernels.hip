@@ -12,10 +12,12 @@
 //   dec_score_rows     score[b, g, J] = max over the group's heads of c * q_h . kbar_J, one
 //                      coalesced summary row per 16-lane group, DPP reductions
 //   dec_select_radix   forced blocks + top (K - |F|) others by (score desc, block asc): radix
-//                      select of the K-th key (8 bits per pass), ascending output list
+//                      select of the K-th key (8 bits per pass, LDS histograms), ascending
+//                      output list
 //   dec_splitk_mfma    64-key blocks: per (b, g, split), each wave takes whole blocks; the G
 //                      heads are the 32-wide row dimension of S^T = K Q^T and O^T = V^T P^T
-//                      on bf16 MFMA, K/V go HBM -> LDS by direct loads; one partial per split
+//                      on bf16 MFMA, K in registers, V -> LDS by direct loads; one partial per
+//                      split
 //   dec_splitk         other block sizes: 16-lane groups stream the split's selected keys
 //                      (one 16-byte K and V slice per lane), online softmax for the G packed
 //                      heads, merged in-wave then across waves into one partial (m, l, acc)
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
   constexpr int VREG = 64 * VPITCH;
   constexpr int VWIN = VREG / 1024;
   static_assert(VREG % 1024 == 0, "DMA windows must tile the region");
-  static_assert(4 * VREG >= (2 * 4 * 32 + 4 * 32 * D) * 4, "merge buffers must fit the regions");
+  static_assert(4 * VREG >= (2 * 4 * 32 + 4 * 32 * D + 1) * 4, "merge buffers must fit the regions");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * VREG];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -543,25 +545,49 @@ __global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
       part[D + 1] = ltot;
     }
   }
+
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
 // ---------------------------------------------------------------------------------------
+// One workgroup per (b, head), one thread per dimension.  The (m, l) of every split are read
+// up front (independent loads, chunks of 16), so the merge waits for memory about twice rather
+// than once per split.
 template <int D>
 __global__ __launch_bounds__(D) void dec_combine(DecArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const float* part = a.partial + ((int64_t)b * a.Hq + h) * a.n_splits * (D + 2);
+  constexpr int CH = 16;
   float mx = -1e30f;
-  for (int s = 0; s < a.n_splits; ++s)
-    if (part[s * (D + 2) + D + 1] > 0.f) mx = fmaxf(mx, part[s * (D + 2) + D]);
-  float lt = 0.f, at = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float ls = part[s * (D + 2) + D + 1];
-    if (ls > 0.f) {
-      const float f = __builtin_amdgcn_exp2f(part[s * (D + 2) + D] - mx);
-      lt += ls * f;
-      at += part[s * (D + 2) + d] * f;
+  for (int s0 = 0; s0 < a.n_splits; s0 += CH) {
+    float ms[CH], ls[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int sp = min(s0 + e, a.n_splits - 1);
+      ms[e] = part[sp * (D + 2) + D];
+      ls[e] = part[sp * (D + 2) + D + 1];
     }
+#pragma unroll
+    for (int e = 0; e < CH; ++e)
+      if (ls[e] > 0.f) mx = fmaxf(mx, ms[e]);
+  }
+  float lt = 0.f, at = 0.f;
+  for (int s0 = 0; s0 < a.n_splits; s0 += CH) {
+    float ms[CH], ls[CH], vs[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int sp = min(s0 + e, a.n_splits - 1);
+      ms[e] = part[sp * (D + 2) + D];
+      ls[e] = s0 + e < a.n_splits ? part[sp * (D + 2) + D + 1] : 0.f;
+      vs[e] = part[sp * (D + 2) + d];
+    }
+#pragma unroll
+    for (int e = 0; e < CH; ++e)
+      if (ls[e] > 0.f) {
+        const float f = __builtin_amdgcn_exp2f(ms[e] - mx);
+        lt += ls[e] * f;
+        at += vs[e] * f;
+      }
   }
   const float o = lt > 0.f ? at / lt : 0.f;
   ((uint16_t*)a.o)[b * a.os0 + h * a.os2 + d] = float_to_bf16_bits(o);
@@ -591,11 +617,13 @@ static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
   const dim3 grid(a.n_splits, a.Hkv, a.B);
   if (a.bk == 64) {
     hipLaunchKernelGGL(dec_splitk_mfma<D>, grid, dim3(256), 0, s, a);
-  } else switch (a.G) {
-    case 1: hipLaunchKernelGGL((dec_splitk<D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dec_splitk<D, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((dec_splitk<D, 4>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((dec_splitk<D, 8>), grid, dim3(256), 0, s, a); break;
+  } else {
+    switch (a.G) {
+      case 1: hipLaunchKernelGGL((dec_splitk<D, 1>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((dec_splitk<D, 2>), grid, dim3(256), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((dec_splitk<D, 4>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((dec_splitk<D, 8>), grid, dim3(256), 0, s, a); break;
+    }
   }
   hipLaunchKernelGGL(dec_combine<D>, dim3(a.Hq, a.B), dim3(D), 0, s, a);
   return hipGetLastError();

@@ -138,7 +138,8 @@ def test_determinism(dev):
                                                         (2, 3000, 4, 1, 64, 8, 64),
                                                         (2, 2000, 16, 2, 128, 64, 64),
                                                         (2, 3000, 2, 2, 64, 12, 64),
-                                                        (2, 3000, 8, 2, 128, 24, 32)])
+                                                        (2, 3000, 8, 2, 128, 24, 32),
+                                                        (1, 140000, 4, 1, 64, 32, 64)])
 def test_decode_reduced(dev, batch, seq, hq, hkv, d, top_k, bk):
     import torch
     import block_sparse_attention_estimate_amd as sa
