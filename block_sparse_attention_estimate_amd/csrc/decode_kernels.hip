@@ -12,7 +12,7 @@
 //   dec_score_rows     score[b, g, J] = max over the group's heads of c * q_h . kbar_J, one
 //                      coalesced summary row per 16-lane group, DPP reductions
 //   dec_select_radix   forced blocks + top (K - |F|) others by (score desc, block asc): radix
-//                      select of the K-th key (8 bits per pass, LDS histograms), ascending
+//                      select of the K-th key (11 bits per pass, LDS histograms), ascending
 //                      output list
 //   dec_splitk_mfma    64-key blocks: per (b, g, split), each wave takes whole blocks; the G
 //                      heads are the 32-wide row dimension of S^T = K Q^T and O^T = V^T P^T
@@ -105,16 +105,36 @@ __global__ __launch_bounds__(256) void dec_score_rows(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Top-K by radix select.  One workgroup per (b, g).  Each candidate block j < nb gets the
-// order-preserving 32-bit key of its score (forced blocks: the maximum key); the K-th largest
-// key T is found 8 bits at a time from per-digit histograms, then the output takes every key
-// above T and, among keys equal to T, the smallest block ids (the order (key desc, block asc)
-// of the sort it replaces), written in ascending block order.
+// Exclusive sum over the 256 threads of a workgroup (4 waves) of a non-negative count, in
+// thread order (reverse = true: over the threads after this one).  Two barriers.
+SA_DEV int block_excl_sum(int v, bool reverse, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = reverse ? __shfl_down(incl, o) : __shfl_up(incl, o);
+    if (reverse ? lane + o < 64 : lane >= o) incl += t;
+  }
+  __syncthreads();                                   // wsum free
+  if (reverse ? lane == 0 : lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int ex = incl - v;
+  for (int w = 0; w < 4; ++w)
+    if (reverse ? w > wave : w < wave) ex += wsum[w];
+  return ex;
+}
+
+// Top-K by radix select.  One workgroup (256 threads) per (b, g).  Each candidate block
+// j < nb gets the order-preserving 32-bit key of its score (forced blocks: the maximum key);
+// the K-th largest key is found 11 bits at a time (3 passes at most; it stops early once the
+// bin it falls in is taken whole), then the
+// output takes every key above the threshold T and, among keys equal to T on the resolved
+// bits, the smallest block ids -- the order (key desc, block asc) -- in ascending block order.
 __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
+  constexpr int BINS = 2048;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  extern __shared__ unsigned int skey[];          // [nKB]
-  __shared__ unsigned int hist[256];
-  __shared__ unsigned int s_prefix, s_need;
+  extern __shared__ unsigned int skey[];             // [nKB]
+  __shared__ unsigned int hist[BINS];
+  __shared__ unsigned int s_dig, s_need;
   __shared__ int wsum[4];
   const int lb = min(max(a.cache_len[b], 0), a.L);
   const int nb = (lb + a.bk - 1) / a.bk;
@@ -123,78 +143,62 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
     const bool forced = (j * a.bk < a.sink) || ((j + 1) * a.bk - 1 >= lb - a.local);
     skey[j] = forced ? 0xFFFFFFFFu : float_order_key(sc[j]);
   }
-  __syncthreads();
   const int kk = min(a.top_k, nb);
-  unsigned int prefix = 0, need = (unsigned int)kk;   // keys matching prefix on the digits so far
+  unsigned int T = 0, mask = 0;                      // threshold on the resolved bits
+  unsigned int need = (unsigned int)kk;
   if (kk < nb) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      const unsigned int hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    const int shifts[3] = {21, 10, 0};
+    for (int p = 0; p < 3; ++p) {
+      const int shift = shifts[p];
+      const unsigned int dmask = p == 2 ? 1023u : 2047u;
+      for (int e = tid; e < BINS; e += 256) hist[e] = 0;
+      __syncthreads();                                 // also: skey written
       for (int j = tid; j < nb; j += 256) {
         const unsigned int k = skey[j];
-        if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        if ((k & mask) == T) atomicAdd(&hist[(k >> shift) & dmask], 1u);
       }
       __syncthreads();
-      if (tid < 64) {
-        // counts of digits >= d, scanned from the top: lane l owns digits 4l .. 4l+3
-        unsigned int c[4], tot = 0;
+      // thread t owns the digits 8t .. 8t+7; counts of larger digits come from later threads
+      unsigned int c[8], tot = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          c[e] = hist[4 * tid + e];
-          tot += c[e];
-        }
-        // suffix sum over lanes (digits above this lane's)
-        unsigned int above = tot;
-        for (int o = 1; o < 64; o <<= 1) {
-          const unsigned int t = __shfl_down(above, o);
-          if (tid + o < 64) above += t;
-        }
-        above -= tot;                                   // keys with a larger digit
-        unsigned int run = above;
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * tid + e;
+        c[e] = hist[d];
+        tot += c[e];
+      }
+      unsigned int run = (unsigned int)block_excl_sum((int)tot, true, wsum);
 #pragma unroll
-        for (int e = 3; e >= 0; --e) {
-          if (run < need && run + c[e] >= need) {       // the K-th key has digit 4l+e
-            s_prefix = prefix | ((unsigned int)(4 * tid + e) << shift);
-            s_need = need - run;
-          }
-          run += c[e];
+      for (int e = 7; e >= 0; --e) {
+        if (run < need && run + c[e] >= need) {        // the K-th key has digit 8t+e
+          s_dig = (unsigned int)(8 * tid + e) | ((need - run == c[e]) ? 0x80000000u : 0u);
+          s_need = need - run;
         }
+        run += c[e];
       }
       __syncthreads();
-      prefix = s_prefix;
+      const unsigned int dg = s_dig;
       need = s_need;
+      T |= (dg & 0x7FFFFFFFu) << shift;
+      mask |= dmask << shift;
+      if (dg & 0x80000000u) break;                     // every key in that bin is taken
     }
   }
-  // flags: key > T, or key == T among the first `need` equal keys by block id
-  constexpr int MAXPER = 32;                          // nKB <= 8192 = 256 * 32
+  // flags: resolved key > T, or == T among the first `need` equal keys by block id
+  constexpr int MAXPER = 32;                           // nKB <= 8192 = 256 * 32
   const int per = (nb + 255) / 256;
   const int j0 = tid * per;
   int eq = 0;
   if (kk < nb)
-    for (int e = 0; e < per && j0 + e < nb; ++e) eq += skey[j0 + e] == prefix;
-  // exclusive prefix of equal keys over the threads (block order)
-  const int lane = tid & 63, wave = tid >> 6;
-  int incl = eq;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int eq_before = incl - eq;
-  for (int w = 0; w < wave; ++w) eq_before += wsum[w];
-  __syncthreads();
+    for (int e = 0; e < per && j0 + e < nb; ++e) eq += (skey[j0 + e] & mask) == T;
+  int eq_before = block_excl_sum(eq, false, wsum);
   unsigned int sel_bits = 0;                           // bit e: block j0 + e selected
   int cnt = 0;
   for (int e = 0; e < per && e < MAXPER && j0 + e < nb; ++e) {
-    const unsigned int k = skey[j0 + e];
+    const unsigned int k = skey[j0 + e] & mask;
     bool take;
-    if (kk >= nb) {
+    if (kk >= nb || k > T) {
       take = true;
-    } else if (k > prefix) {
-      take = true;
-    } else if (k == prefix) {
+    } else if (k == T) {
       take = (unsigned int)eq_before < need;
       ++eq_before;
     } else {
@@ -205,16 +209,7 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
       ++cnt;
     }
   }
-  // ascending compaction
-  incl = cnt;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int pos = incl - cnt;
-  for (int w = 0; w < wave; ++w) pos += wsum[w];
+  int pos = block_excl_sum(cnt, false, wsum);
   int32_t* out = a.selected + ((int64_t)b * a.Hkv + g) * a.top_k;
   for (int e = 0; e < per && e < MAXPER; ++e)
     if (sel_bits & (1u << e)) out[pos++] = j0 + e;
@@ -372,34 +367,41 @@ __global__ __launch_bounds__(256) void dec_splitk(DecArgs a) {
 // of the query rows of the prefill kernel: S^T = K Q^T with Q^T's 32 columns holding the G
 // heads (zero beyond G), so each lane owns one head and 16 keys of each 32-key half and the
 // softmax statistics stay in-lane (plus one exchange with lane ^ 32); P^T stays in registers
-// as the B operand of O^T += V^T P^T.  Each wave of the workgroup takes the split's blocks
-// w, w + 4, ...: the block's K rows are loaded straight into registers in the A-operand
-// layout, its V rows go HBM -> the wave's LDS region by direct loads (320-byte rows for
-// d = 128) and V^T is read with transposing LDS reads, so S and the softmax run while V is
-// still arriving.  80 KB of LDS per workgroup lets two workgroups share a CU.  The four
-// waves' (m, l, O) are merged through LDS into one partial per (b, head, split).  MFMA work
-// is 8x the useful work for G = 4 and still far below the time the K/V bytes take to arrive.
+// as the B operand of O^T += V^T P^T.  About one workgroup per CU: each wave streams its
+// share of the split's blocks (w, w + 4, ...) with the next block in flight -- its K rows go
+// straight into registers in the A-operand layout, its V rows HBM -> LDS by direct loads
+// (320-byte rows for d = 128, two buffers per wave) -- while the current block is computed;
+// V^T is read with transposing LDS reads.  The four waves' (m, l, O) are merged through LDS
+// into one partial per (b, head, split).  MFMA work is 8x the useful work for G = 4 and still
+// far below the time the K/V bytes take to arrive.
 template <int D>
-__global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
+__global__ __launch_bounds__(256, 1) void dec_splitk_mfma(DecArgs a) {
   // The host pass only needs this kernel's signature (for its launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KS = D / 16, DM = D / 32, ROWB = D * 2;
   constexpr int VPITCH = D == 128 ? 320 : 192;
   constexpr int VREG = 64 * VPITCH;
   constexpr int VWIN = VREG / 1024;
+  constexpr int LOADS = 2 * KS + VWIN;             // vector-memory ops per block
   static_assert(VREG % 1024 == 0, "DMA windows must tile the region");
-  static_assert(4 * VREG >= (2 * 4 * 32 + 4 * 32 * D + 1) * 4, "merge buffers must fit the regions");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * VREG];
+  static_assert(4 * VREG >= (2 * 4 * 32 + 4 * 32 * D) * 4, "merge buffers must fit the regions");
+  static_assert(LOADS < 64, "one block's loads must fit the vmcnt counter");
+  // two V buffers per wave, as distinct objects so the compiler can tell a load into one
+  // from reads of the other
+  __shared__ __attribute__((aligned(1024))) unsigned char vb0[4 * VREG];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb1[4 * VREG];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = wave_uniform(tid >> 6);
-  unsigned char* reg = lds + wave * VREG;
+  unsigned char* reg0 = vb0 + wave * VREG;
+  unsigned char* reg1 = vb1 + wave * VREG;
   const int lb = min(max(a.cache_len[b], 0), a.L);
   const int nb = (lb + 63) / 64;
   const int nsel = min(a.top_k, nb);
   const int bps = (nsel + a.n_splits - 1) / a.n_splits;
   const int blk0 = s * bps, blk1 = min(nsel, blk0 + bps);
+  const int nw = max(0, (blk1 - blk0 - wave + 3) / 4);   // this wave's blocks
   const __attribute__((address_space(4))) int32_t* sel =
       (const __attribute__((address_space(4))) int32_t*)(a.selected + ((int64_t)b * a.Hkv + g) * a.top_k);
   const float sl2 = a.c * 1.4426950408889634f;
@@ -427,11 +429,11 @@ __global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = (f32x16){};
   float m_run = -1e30f, l_run = 0.f;
 
-  for (int blk = blk0 + wave; blk < blk1; blk += 4) {
-    const int t0 = sel[blk] * 64;
-    // K rows in the A-operand layout: lane l holds key 32 mt + l % 32, dims 16 ks + 8 (l / 32)
-    // (rows past the cache end re-read the last cached row; their scores are masked below)
-    bf16x8 kf[2][KS];
+  // issue the loads of this wave's i-th block: K rows into kf in the A-operand layout (lane l:
+  // key 32 mt + l % 32, dims 16 ks + 8 (l / 32)), V rows into the LDS region; rows past the
+  // cache end re-read the last cached row (their scores are masked)
+  auto load = [&](int i, bf16x8 (*kf)[KS], unsigned char* reg) {
+    const int t0 = sel[blk0 + wave + 4 * i] * 64;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int tok = min(t0 + mt * 32 + l32, lb - 1);
@@ -439,7 +441,6 @@ __global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = *(const bf16x8*)(kp + ks * 16);
     }
-    // V rows -> this wave's LDS region
 #pragma unroll
     for (int w = 0; w < VWIN; ++w) {
       const int o = w * 1024 + lane * 16;
@@ -448,7 +449,10 @@ __global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
       __builtin_amdgcn_global_load_lds(vbase + (int64_t)tok * a.vs1 + (cb < ROWB ? cb / 2 : 0),
                                        LDS_PTR(void, reg + w * 1024), 16, 0, 0);
     }
-    // S^T = K Q^T (the compiler waits for the K loads only; V is still in flight)
+  };
+  // attention over the i-th block; `more`: the next block's loads are in flight behind it
+  auto compute = [&](int i, bf16x8 (*kf)[KS], const unsigned char* reg, bool more) {
+    const int t0 = sel[blk0 + wave + 4 * i] * 64;
     f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -492,8 +496,11 @@ __global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
         }
       }
     l_run = ls;
-    // O^T += V^T P^T once this wave's V rows have landed
-    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+    // this block's V rows have landed once only the next block's loads may be outstanding
+    if (more)
+      __builtin_amdgcn_s_waitcnt(VMCNT_IMM(LOADS));
+    else
+      __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
@@ -506,13 +513,24 @@ __global__ __launch_bounds__(256, 2) void dec_splitk_mfma(DecArgs a) {
         __builtin_memcpy(&vf, both, 16);
         oacc[dm] = mfma_bf16(vf, pf[s4], oacc[dm]);
       }
-    // every LDS read of the region has returned before the next block's loads overwrite it
+    // every LDS read of the region has returned before a later block's loads overwrite it
     __builtin_amdgcn_s_waitcnt(LGKM0_IMM);
+  };
+
+  bf16x8 ka[2][KS], kb[2][KS];
+  if (nw > 0) load(0, ka, reg0);
+  for (int i = 0; i < nw; i += 2) {
+    if (i + 1 < nw) load(i + 1, kb, reg1);
+    compute(i, ka, reg0, i + 1 < nw);
+    if (i + 1 < nw) {
+      if (i + 2 < nw) load(i + 2, ka, reg0);
+      compute(i + 1, kb, reg1, i + 2 < nw);
+    }
   }
 
   // ---- merge the four waves through LDS (the regions are free once every wave is here) ----
   __syncthreads();
-  float* mo = (float*)lds;                     // [4][32] running max per wave and head
+  float* mo = (float*)vb0;                     // [4][32] running max per wave and head
   float* lo = mo + 4 * 32;                     // [4][32] row sum
   float* ao = lo + 4 * 32;                     // [4][32][D] O per wave and head
   const float lt = half_pair_sum(l_run);

@@ -96,9 +96,11 @@ struct DecLayout {
 
 int decode_splits(const sa_shape* s, const sa_decode_params* p) {
   if (p->n_splits > 0) return p->n_splits;
-  // enough workgroups to cover the chip several times over
+  // 64-key blocks (MFMA kernel, each workgroup streams its blocks): about one workgroup per
+  // CU; other block sizes: enough workgroups to cover the chip several times over
+  const int64_t target = p->block_k == 64 ? 256 : 2048;
   int n = 1;
-  while ((int64_t)s->batch * s->n_kv_heads * n < 2048 && n < 64) n <<= 1;
+  while ((int64_t)s->batch * s->n_kv_heads * n < target && n < 64) n <<= 1;
   return n;
 }
 
