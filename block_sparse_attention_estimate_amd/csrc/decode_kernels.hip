@@ -58,22 +58,30 @@ SA_DEV float row16_sum(float v) {
 
 // score[b, g, J] = c * max over the G heads of q_h . kbar[b, J, g].  A 16-lane group reads one
 // summary row (d bf16 values) with one load per lane and reduces the per-head dot products
-// over the group with DPP; each workgroup covers 64 blocks (4 per group, loaded up front).
+// over the group with DPP; each workgroup covers 128 blocks (8 per group, loaded up front).
 template <int D, int G>
 __global__ __launch_bounds__(256) void dec_score_rows(DecArgs a) {
   constexpr int DPL = D / 16;              // dims per lane (8 or 4)
-  constexpr int RPG = 4;                   // rows per group
-  const int g = blockIdx.y, b = blockIdx.z;
+  constexpr int RPG = 8;                   // rows per group
+  // the KV head varies fastest over the grid: the workgroups of all heads of a block range
+  // run together and read each row group [b, J, 0..Hkv) of the summaries as a whole
+  const int g = blockIdx.x, b = blockIdx.z;
   const int tid = threadIdx.x, sub = tid & 15, grp = tid >> 4;
   const int nb = (min(max(a.cache_len[b], 0), a.L) + a.bk - 1) / a.bk;
   float qv[G][DPL];
 #pragma unroll
   for (int hg = 0; hg < G; ++hg) {
     const uint16_t* qp = a.q + b * a.qs0 + (g * G + hg) * a.qs2 + sub * DPL;
+    if (DPL == 8) {
+      const u16x8 u = *(const u16x8*)qp;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) qv[hg][e] = bf16_bits_to_float(qp[e]);
+      for (int e = 0; e < DPL; ++e) qv[hg][e] = bf16_bits_to_float(u[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) qv[hg][e] = bf16_bits_to_float(qp[e]);
+    }
   }
-  const int J0 = blockIdx.x * 16 * RPG + grp;
+  const int J0 = blockIdx.y * 16 * RPG + grp;
   float kx[RPG][DPL];
 #pragma unroll
   for (int r = 0; r < RPG; ++r) {
@@ -624,7 +632,7 @@ hipError_t launch_block_summary(const DecArgs& a, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
-  const dim3 sgrid((a.nKB + 63) / 64, a.Hkv, a.B);
+  const dim3 sgrid(a.Hkv, (a.nKB + 127) / 128, a.B);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((dec_score_rows<D, 1>), sgrid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((dec_score_rows<D, 2>), sgrid, dim3(256), 0, s, a); break;
