@@ -8,7 +8,8 @@
 // referee minor comment 4).
 //
 // Kernels:
-//   dec_block_summary  kbar[b, J, g, :] = mean of the block's cached keys (fp64 -> fp32 -> bf16)
+//   dec_block_summary  kbar[b, J, g, :] = mean of the block's cached keys (exact fp64 sum ->
+//                      fp32 -> bf16), all KV heads of a block per workgroup, coalesced
 //   dec_score_rows     score[b, g, J] = max over the group's heads of c * q_h . kbar_J, one
 //                      coalesced summary row per 16-lane group, DPP reductions
 //   dec_select_radix   forced blocks + top (K - |F|) others by (score desc, block asc): radix
@@ -28,22 +29,49 @@
 #define NEG_INF (-__builtin_huge_valf())
 
 // ---------------------------------------------------------------------------------------
+// kbar[b, J, g, :] for every KV head of one block: 256 threads cover the (g, d) elements of a
+// token row four at a time (8-byte loads, consecutive threads on consecutive elements), and
+// sum the block's tokens in fp64 -- exact, hence independent of the summation order, while
+// the block's values of one element span less than about 2^39 in magnitude (8-bit bf16
+// significands, at most 2^6 terms, 53-bit sum) -- then divide, round to fp32, then to bf16.
 template <int D>
-__global__ __launch_bounds__(D) void dec_block_summary(DecArgs a) {
-  const int J = blockIdx.x, g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+__global__ __launch_bounds__(256) void dec_block_summary(DecArgs a) {
+  const int J = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lb = min(max(a.cache_len[b], 0), a.L);
-  uint16_t* out = (uint16_t*)a.ksum + (((int64_t)b * a.nKB + J) * a.Hkv + g) * D + d;
-  const int t0 = J * a.bk;
-  if (t0 >= lb) {
-    *out = 0;
-    return;
+  const int t0 = J * a.bk, t1 = min(lb, t0 + a.bk);
+  for (int base = 0; base < a.Hkv * D; base += 1024) {
+    const int idx = base + tid * 4;
+    if (idx >= a.Hkv * D) break;
+    const int g = idx / D, d = idx % D;
+    uint16_t* out = (uint16_t*)a.ksum + (((int64_t)b * a.nKB + J) * a.Hkv + g) * D + d;
+    if (t0 >= lb) {
+      *(u32x2*)out = (u32x2){0u, 0u};
+      continue;
+    }
+    const uint16_t* kp = a.kc + b * a.ks0 + g * a.ks2 + d;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    auto add = [&](u32x2 u) {
+      s0 += bf16_bits_to_double((unsigned short)(u.x & 0xFFFFu));
+      s1 += bf16_bits_to_double((unsigned short)(u.x >> 16));
+      s2 += bf16_bits_to_double((unsigned short)(u.y & 0xFFFFu));
+      s3 += bf16_bits_to_double((unsigned short)(u.y >> 16));
+    };
+    int t = t0;
+    for (; t + 8 <= t1; t += 8) {                    // eight independent loads in flight
+      u32x2 u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[e] = *(const u32x2*)(kp + (int64_t)(t + e) * a.ks1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) add(u[e]);
+    }
+    for (; t < t1; ++t) add(*(const u32x2*)(kp + (int64_t)t * a.ks1));
+    const double n = (double)(t1 - t0);             // divided, as the mean is defined
+    const unsigned int lo = float_to_bf16_bits((float)(s0 / n)) |
+                            ((unsigned int)float_to_bf16_bits((float)(s1 / n)) << 16);
+    const unsigned int hi = float_to_bf16_bits((float)(s2 / n)) |
+                            ((unsigned int)float_to_bf16_bits((float)(s3 / n)) << 16);
+    *(u32x2*)out = (u32x2){lo, hi};
   }
-  const int t1 = min(lb, t0 + a.bk);
-  const uint16_t* kp = a.kc + b * a.ks0 + g * a.ks2 + d;
-  double s = 0.0;
-  for (int t = t0; t < t1; ++t) s += bf16_bits_to_double(kp[(int64_t)t * a.ks1]);
-  const double mean = s / (double)(t1 - t0);
-  *out = float_to_bf16_bits((float)mean);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -624,9 +652,9 @@ __global__ __launch_bounds__(D) void dec_combine(DecArgs a) {
 // ---------------------------------------------------------------------------------------
 hipError_t launch_block_summary(const DecArgs& a, hipStream_t s) {
   if (a.D == 64)
-    hipLaunchKernelGGL(dec_block_summary<64>, dim3(a.nKB, a.Hkv, a.B), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(dec_block_summary<64>, dim3(a.nKB, a.B), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(dec_block_summary<128>, dim3(a.nKB, a.Hkv, a.B), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(dec_block_summary<128>, dim3(a.nKB, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
