@@ -293,7 +293,11 @@ def bench_decode(args, dev):
             "us_per_step": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_from_profile(f"dec_splitk_{args.workload}_traffic", DEC_SRC)}}
+                         "traffic": traffic_from_profile(f"dec_splitk_{args.workload}_traffic", DEC_SRC),
+                         "kernel": "whole decode step (score, select, split-K, combine: one "
+                                   "library call, timed as one)",
+                         "units": f"{sel_bytes} B of selected K/V + {sum_bytes} B of block "
+                                  f"summaries per step"}}
 
 
 def main():
