@@ -575,54 +575,54 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
         if (tok > row || tok >= a.N) sacc[mt][r] = NEG_INF;
       }
   };
-  // P^T = exp2(S^T scale - m) in bf16; returns this lane's sum of the rounded values
-  auto expo = [&](const f32x16* sacc, bf16x8* pf) -> float {
+  // P^T of key half mt = exp2(S^T scale - m) in bf16 (pf[2 mt], pf[2 mt + 1]); returns this
+  // lane's sum of the rounded values
+  auto expo = [&](const f32x16* sacc, int mt, bf16x8* pf) -> float {
     const float mneg = -m_run;
     float ls = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int s2 = 0; s2 < 2; ++s2) {
+      f32x8 tt;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        f32x8 tt;
+      for (int e = 0; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * s2 + e], sl2, mneg));
+      const bf16x8 pb = __builtin_convertvector(tt, bf16x8);
+      pf[mt * 2 + s2] = pb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * s2 + e], sl2, mneg));
-        const bf16x8 pb = __builtin_convertvector(tt, bf16x8);
-        pf[mt * 2 + s2] = pb;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pb[e], pb[e + 1]};
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
-        }
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pb[e], pb[e + 1]};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
       }
+    }
     return ls;
   };
-  // The running max m stays fixed while every P value of a tile is at most 2^16 (checked on the
-  // lane's partial row sum, which bounds each value).  A tile that breaks the bound (scores more
-  // than 16 above m in the log2 domain, or the first tile, while m is still -1e30) moves m to
-  // the tile's row max, rescales O and l and recomputes P.  No per-tile row max is taken.
-  auto settle = [&](const f32x16* sacc, bf16x8* pf, float ts) {
+  // The running max m stays fixed while every P value of a key half is at most 2^16 (checked
+  // on the lane's partial row sum, which bounds each value).  A half that breaks the bound
+  // (scores more than 16 above m in the log2 domain, or the first tile, while m is still
+  // -1e30) moves m to the half's row max, rescales O and l -- which may already hold the other
+  // half's P V at the old m -- and recomputes its P.  No per-tile row max is taken.
+  auto settle = [&](const f32x16* sacc, int mt, bf16x8* pf, float ts) {
     if (__any(!(ts <= 65536.0f))) {
       float v = NEG_INF;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][r]);
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[mt][r]);
       const float mnew = fmaxf(m_run, half_pair_max(v) * sl2);
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
       m_run = mnew;
       l_run *= alpha;
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
-      ts = expo(sacc, pf);
+      ts = expo(sacc, mt, pf);
     }
     l_run += ts;
   };
-  // O^T += V^T P^T with transposing V reads from the stage at sb
-  auto pv = [&](const unsigned char* sb, const bf16x8* pf) {
+  // O^T += V^T P^T over the 16-key groups of key half mt, with transposing V reads from the
+  // stage at sb
+  auto pv = [&](const unsigned char* sb, int mt, const bf16x8* pf) {
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm) {
+        const int s4 = 2 * mt + s2;
         const unsigned char* vp = sb + v_rd + 16 * s4 * VPITCH + dm * 64;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp + 8 * VPITCH));
@@ -633,10 +633,11 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
       }
   };
 
-  // Software pipeline over the list.  On entry to step t, S(t) is in `cur` (masked).  Step t
-  // computes P(t) while the MFMAs of S(t+1) run, then P V(t), issues the DMA of tile t+3 into
-  // the stage of tile t-1 and waits for tile t+2, so at every barrier only the newest tile is
-  // in flight.
+  // Software pipeline over the list.  On entry to step t, S(t) is in `cur` (masked) and tiles
+  // t+1 and t+2 are in LDS.  Step t computes P(t)'s first key half while the MFMAs of S(t+1)
+  // run, P(t)'s second half while P V of the first half runs, and P V of the second half,
+  // then issues the DMA of tile t+3 into the stage of tile t-1 and waits for tile t+2, so at
+  // every barrier only the newest tile is in flight.
   if (n > 0) {
     issue(st0, list[0]);
     issue(st1, list[min(1, n - 1)]);
@@ -649,19 +650,25 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
                     f32x16* cur, f32x16* nxt, bool may_mask) {
       const int jd = list[min(t + 3, n - 1)];
       bf16x8 pf[4];
-      const float ts = expo(cur, pf);
+      const float t0s = expo(cur, 0, pf);
       qk(sn, nxt);
-      settle(cur, pf, ts);
-      pv(sc, pf);
+      settle(cur, 0, pf, t0s);
+      const float t1s = expo(cur, 1, pf);
+      pv(sc, 0, pf);
+      settle(cur, 1, pf, t1s);
+      pv(sc, 1, pf);
       if (may_mask && t + 1 >= n_main) mask(t + 1, nxt);
       issue(sd, jd);
       DMA_BARRIER(SLOTS);
     };
     auto last = [&](unsigned char* sc, f32x16* cur) {
       bf16x8 pf[4];
-      const float ts = expo(cur, pf);
-      settle(cur, pf, ts);
-      pv(sc, pf);
+      const float t0s = expo(cur, 0, pf);
+      settle(cur, 0, pf, t0s);
+      const float t1s = expo(cur, 1, pf);
+      pv(sc, 0, pf);
+      settle(cur, 1, pf, t1s);
+      pv(sc, 1, pf);
     };
     int t = 0;
     for (; t + 4 < n_main; t += 4) {          // the next tile of every step needs no mask
