@@ -21,10 +21,10 @@ import torch
 
 from . import _lib
 from ._lib import (SA_BLOCK, SA_STRIPE, SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE,  # noqa: F401
-                   SaError)
+                   SA_OP_CALIBRATE, SaError)
 
 __all__ = ["Lists", "estimate_mask", "sparse_prefill", "build_block_summary", "sparse_decode",
-           "workspace_size", "SaError", "load_library"]
+           "calibrate_theta", "workspace_size", "SaError", "load_library"]
 
 
 def load_library():
@@ -114,7 +114,7 @@ class Lists:
 def workspace_size(op, *, q=None, k=None, block_q=128, block_k=64, sink=32, local=256,
                    granularity="block", theta=None, shape=None, decode_params=None) -> int:
     lib = _lib.load()
-    if op == SA_OP_ESTIMATE:
+    if op in (SA_OP_ESTIMATE, SA_OP_CALIBRATE):
         s = _prefill_shape(q, k)
         p, keep = _sparse_params(block_q, block_k, sink, local, granularity,
                                  theta if theta is not None else 0.0, 0.0, q.shape[2])
@@ -185,6 +185,35 @@ def sparse_prefill(q, k, v, lists: Lists, *, block_q=128, block_k=64, sink=32, l
                "sa_sparse_prefill")
     del keep
     return o, lse_t
+
+
+def calibrate_theta(q, k, v, *, tau0=0.008, err_bound=0.4, max_halvings=16, block_q=128,
+                    block_k=64, sink=32, local=256, softmax_scale=0.0, workspace=None,
+                    stream=None):
+    """Per-head theta calibration (sa_calibrate_theta; block granularity).  Returns
+    (theta [Hq] float32, err [Hq] float32, halvings [Hq] int32) as numpy arrays: theta_h =
+    -ln(tau0) + halvings_h * ln 2, err_h = sum |O - O~| over the head's rows and dims / rows.
+    Synchronous (the library reads the errors back every round)."""
+    import numpy as np
+    lib = _lib.load()
+    _check_bf16("v", v, 4)
+    s = _prefill_shape(q, k, v, q)
+    p, keep = _sparse_params(block_q, block_k, sink, local, "block", 0.0, softmax_scale,
+                             q.shape[2])
+    need = int(lib.sa_workspace_size(SA_OP_CALIBRATE, ctypes.byref(s), ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    hq = q.shape[2]
+    theta = (ctypes.c_float * hq)()
+    err = (ctypes.c_float * hq)()
+    halv = (ctypes.c_int32 * hq)()
+    _lib.check(lib.sa_calibrate_theta(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                      float(tau0), float(err_bound), int(max_halvings), theta, err,
+                                      halv, _ptr(workspace), workspace.numel(), _stream(stream)),
+               "sa_calibrate_theta")
+    del keep
+    return (np.array(theta, dtype=np.float32), np.array(err, dtype=np.float32),
+            np.array(halv, dtype=np.int32))
 
 
 def _decode_shape(q, k_cache, v_cache, o=None) -> _lib.SaShape:

@@ -14,11 +14,12 @@ LIB_PATH = os.path.join(_HERE, "libsa.so")
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_PARAM, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY, \
     SA_ERR_WORKSPACE, SA_ERR_DEVICE = range(8)
 SA_BLOCK, SA_STRIPE = 0, 1
-SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE = 0, 1, 2
+SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE, SA_OP_CALIBRATE = 0, 1, 2, 3
 SA_MAX_Q_HEADS = 128
 
 EXPORTED = ("sa_workspace_size", "sa_estimate_mask", "sa_sparse_prefill",
-            "sa_build_block_summary", "sa_sparse_decode", "sa_status_string")
+            "sa_build_block_summary", "sa_sparse_decode", "sa_calibrate_theta",
+            "sa_status_string")
 
 
 class SaShape(ctypes.Structure):
@@ -76,6 +77,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sa_sparse_decode.restype = ctypes.c_int
     lib.sa_sparse_decode.argtypes = [P(SaShape), P(SaDecodeParams), vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, ctypes.c_size_t, vp]
+    lib.sa_calibrate_theta.restype = ctypes.c_int
+    lib.sa_calibrate_theta.argtypes = [P(SaShape), P(SaSparseParams), vp, vp, vp, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_int32, P(ctypes.c_float),
+                                       P(ctypes.c_float), P(ctypes.c_int32), vp, ctypes.c_size_t, vp]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_status_string.argtypes = [ctypes.c_int]
     _lib = lib

@@ -90,6 +90,28 @@ EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p) {
   return L;
 }
 
+// calibration workspace: the estimate's scratch, one block list, both outputs, the errors
+struct CalLayout {
+  size_t est, counts, idx, o_ref, o_sp, err, total;
+};
+
+CalLayout cal_layout(const sa_shape* s, const sa_sparse_params* p) {
+  CalLayout L{};
+  const int N = s->seq_q;
+  const int nQB = ceil_div(N, p->block_q), nKB = ceil_div(N, p->block_k);
+  const size_t rows = (size_t)s->batch * s->n_kv_heads * nQB;
+  const size_t oel = (size_t)s->batch * N * s->n_q_heads * s->head_dim;
+  size_t off = 0;
+  L.est = off;    off = align_up(off + est_layout(s, p).total);
+  L.counts = off; off = align_up(off + rows * sizeof(int32_t));
+  L.idx = off;    off = align_up(off + rows * nKB * sizeof(int32_t));
+  L.o_ref = off;  off = align_up(off + oel * 2);
+  L.o_sp = off;   off = align_up(off + oel * 2);
+  L.err = off;    off = align_up(off + (size_t)s->n_q_heads * sizeof(double));
+  L.total = off;
+  return L;
+}
+
 struct DecLayout {
   size_t scores, selected, partial, total;
 };
@@ -156,6 +178,13 @@ size_t sa_workspace_size(int op, const sa_shape* shape, const void* params) {
     const sa_sparse_params* p = (const sa_sparse_params*)params;
     if (check_prefill_shape(shape) != SA_OK || check_sparse_params(shape, p, true) != SA_OK) return 0;
     return est_layout(shape, p).total;
+  }
+  if (op == SA_OP_CALIBRATE) {
+    const sa_sparse_params* p = (const sa_sparse_params*)params;
+    if (check_prefill_shape(shape) != SA_OK || check_sparse_params(shape, p, false) != SA_OK ||
+        p->granularity != SA_BLOCK)
+      return 0;
+    return cal_layout(shape, p).total;
   }
   if (op == SA_OP_DECODE) {
     const sa_decode_params* p = (const sa_decode_params*)params;
@@ -303,6 +332,87 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params
   a.n_splits = decode_splits(shape, params);
   a.c = resolve_scale(params->softmax_scale, shape->head_dim);
   if (launch_decode(a, stream) != hipSuccess) return SA_ERR_DEVICE;
+  return SA_OK;
+}
+
+sa_status sa_calibrate_theta(const sa_shape* shape, const sa_sparse_params* params,
+                             const void* q, const void* k, const void* v,
+                             float tau0, float err_bound, int32_t max_halvings,
+                             float* theta_out, float* err_out, int32_t* halvings_out,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  sa_status st = check_prefill_shape(shape);
+  if (st != SA_OK) return st;
+  st = check_sparse_params(shape, params, false);
+  if (st != SA_OK) return st;
+  if (params->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !theta_out) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return SA_ERR_SHAPE;
+  if (!(tau0 > 0.f && tau0 <= 1.f) || !(err_bound > 0.f) || isinf(err_bound) ||
+      max_halvings < 0 || max_halvings > 64)
+    return SA_ERR_PARAM;
+  const CalLayout L = cal_layout(shape, params);
+  if (!ws) return SA_ERR_WORKSPACE;
+  if (ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0) return SA_ERR_WORKSPACE;
+
+  const int B = shape->batch, N = shape->seq_q, Hq = shape->n_q_heads, D = shape->head_dim;
+  const int nKB = ceil_div(N, params->block_k);
+  char* base = (char*)ws;
+  sa_lists lists;
+  lists.counts = (int32_t*)(base + L.counts);
+  lists.idx = (int32_t*)(base + L.idx);
+  lists.stride = nKB;
+  lists.margins = nullptr;
+  // both outputs contiguous [B, N, Hq, D]
+  sa_shape so = *shape;
+  so.o_stride[0] = (int64_t)N * Hq * D;
+  so.o_stride[1] = (int64_t)Hq * D;
+  so.o_stride[2] = D;
+  void* o_ref = base + L.o_ref;
+  void* o_sp = base + L.o_sp;
+  double* err_d = (double*)(base + L.err);
+  const size_t est_bytes = L.counts - L.est;
+
+  float theta[SA_MAX_Q_HEADS];
+  int kh[SA_MAX_Q_HEADS];
+  sa_sparse_params p = *params;
+  p.theta = theta;
+  // full attention: every causal block kept
+  for (int h = 0; h < Hq; ++h) theta[h] = INFINITY;
+  if ((st = sa_estimate_mask(&so, &p, q, k, &lists, base + L.est, est_bytes, stream)) != SA_OK) return st;
+  if ((st = sa_sparse_prefill(&so, &p, q, k, v, &lists, o_ref, nullptr, stream)) != SA_OK) return st;
+
+  const double theta0 = -log((double)tau0), ln2 = log(2.0);
+  for (int h = 0; h < Hq; ++h) {
+    kh[h] = 0;
+    theta[h] = (float)theta0;
+  }
+  double err_h[SA_MAX_Q_HEADS];
+  for (int round = 0;; ++round) {
+    if ((st = sa_estimate_mask(&so, &p, q, k, &lists, base + L.est, est_bytes, stream)) != SA_OK) return st;
+    if ((st = sa_sparse_prefill(&so, &p, q, k, v, &lists, o_sp, nullptr, stream)) != SA_OK) return st;
+    if (launch_head_l1((const uint16_t*)o_ref, (const uint16_t*)o_sp, B, N, Hq, D, err_d, stream) !=
+        hipSuccess)
+      return SA_ERR_DEVICE;
+    if (hipMemcpyAsync(err_h, err_d, Hq * sizeof(double), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return SA_ERR_DEVICE;
+    bool done = true;
+    for (int h = 0; h < Hq; ++h) {
+      err_h[h] /= (double)B * N;
+      if (!(err_h[h] < err_bound) && kh[h] < max_halvings) done = false;
+    }
+    if (done) break;
+    for (int h = 0; h < Hq; ++h)
+      if (!(err_h[h] < err_bound) && kh[h] < max_halvings) {
+        ++kh[h];
+        theta[h] = (float)(theta0 + kh[h] * ln2);
+      }
+  }
+  for (int h = 0; h < Hq; ++h) {
+    theta_out[h] = theta[h];
+    if (err_out) err_out[h] = (float)err_h[h];
+    if (halvings_out) halvings_out[h] = kh[h];
+  }
   return SA_OK;
 }
 

@@ -64,3 +64,5 @@ hipError_t launch_estimate(const EstArgs& a, int granularity, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs& a, int D, int granularity, hipStream_t s);
 hipError_t launch_block_summary(const DecArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
+hipError_t launch_head_l1(const uint16_t* o_ref, const uint16_t* o_sp, int B, int N, int Hq, int D,
+                          double* err, hipStream_t s);

@@ -56,7 +56,7 @@ typedef enum {
 } sa_status;
 
 enum { SA_BLOCK = 0, SA_STRIPE = 1 };
-enum { SA_OP_ESTIMATE = 0, SA_OP_PREFILL = 1, SA_OP_DECODE = 2 };
+enum { SA_OP_ESTIMATE = 0, SA_OP_PREFILL = 1, SA_OP_DECODE = 2, SA_OP_CALIBRATE = 3 };
 
 #define SA_MAX_Q_HEADS 128
 
@@ -104,9 +104,9 @@ typedef struct {
   float softmax_scale;
 } sa_decode_params;
 
-/* Workspace bytes an operation needs (op = SA_OP_ESTIMATE with sa_sparse_params, or
- * SA_OP_DECODE with sa_decode_params; SA_OP_PREFILL needs none).  Returns 0 for an
- * invalid request. */
+/* Workspace bytes an operation needs (op = SA_OP_ESTIMATE or SA_OP_CALIBRATE with
+ * sa_sparse_params, or SA_OP_DECODE with sa_decode_params; SA_OP_PREFILL needs none).
+ * Returns 0 for an invalid request. */
 size_t sa_workspace_size(int op, const sa_shape* shape, const void* params);
 
 /* Estimation pass (AnchorAttention Eq. (1)-(3); SALE low-precision estimate):
@@ -163,6 +163,30 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params
                            const void* k_summary, const int32_t* cache_len,
                            void* o, float* lse, int32_t* selected,
                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-head threshold calibration (SALE, "Assumptions & free parameters": the per-head
+ * threshold tau starts at 0.008 and is halved until the L1 output error
+ * Err(tau) = ||O - O~||_1 / N meets a user-chosen bound; the relative-score test keeps a
+ * block when its score is at least tau times the anchor's, i.e. theta = -ln tau in the
+ * logit units of Eq. (2)).  With this library's own passes: O is the attention with every
+ * causal block kept (theta = +inf), O~ the estimate + sparse prefill with the current
+ * thetas; Err_h = sum over batch, rows and head dims of |O - O~| for query head h, divided
+ * by batch * seq (the rows).  Starting from theta_h = -ln(tau0), every head whose Err_h is
+ * not below err_bound gets theta_h = -ln(tau0) + k_h ln 2 with k_h one larger, and the loop
+ * repeats, at most max_halvings times; all heads are evaluated together each round (the
+ * lists are unions over a KV head's query heads, so raising one head's theta can lower its
+ * group mates' errors).  Block granularity only (SA_ERR_UNSUPPORTED for stripes).
+ * params->theta is ignored.  theta_out: HOST float [n_q_heads], the calibrated thetas;
+ * err_out: nullable HOST float [n_q_heads], each head's Err at its final theta;
+ * halvings_out: nullable HOST int32 [n_q_heads], the k_h.  q, k, v as for
+ * sa_sparse_prefill; ws: at least sa_workspace_size(SA_OP_CALIBRATE, ...) bytes (it holds
+ * both outputs and the lists).  Unlike the other entry points this call is synchronous: it
+ * reads the errors back every round and returns after the last one. */
+sa_status sa_calibrate_theta(const sa_shape* shape, const sa_sparse_params* params,
+                             const void* q, const void* k, const void* v,
+                             float tau0, float err_bound, int32_t max_halvings,
+                             float* theta_out, float* err_out, int32_t* halvings_out,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* sa_status_string(sa_status status);

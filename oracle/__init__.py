@@ -18,6 +18,8 @@ What it computes, in the pages' order and notation:
 * ``attention`` -- masked softmax attention under given lists: the plain definition.
 * ``decode``    -- block-summary scoring, forced + top-K block selection and attention
   over the selected blocks for one query token per sequence.
+* ``calibrate`` -- SALE's per-head threshold calibration: tau halved from 0.008 until the
+  L1 output error against full attention meets a bound (theta = -ln tau).
 
 Parity pins: see ``tests/test_oracle_*.py``.  Every function is pinned by brute force,
 closed forms, invariants or an independent library routine; none is "parity unpinned".
@@ -37,3 +39,4 @@ from .estimate import (  # noqa: F401
 from .attention import attention_rows, attention_all, dense_causal_reference_mask  # noqa: F401
 from .decode import block_summary, decode_select, decode_attention  # noqa: F401
 from .diagnostics import pruned_mass_fraction, sparsity_from_kept, sale_log_margin  # noqa: F401
+from .calibrate import full_lists, head_l1_error, calibrate_theta  # noqa: F401
