@@ -300,6 +300,37 @@ def bench_decode(args, dev):
                                   f"summaries per step"}}
 
 
+def bench_calibrate(args, dev):
+    """Per-head theta calibration (sa_calibrate_theta) on a prefill workload: wall time of the
+    whole loop, rounds, calibrated thetas, halvings and final errors."""
+    import math
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    import synth
+    log(f"generating {args.workload}")
+    x = synth.make_prefill(args.workload, seed=args.seed)
+    B, N, Hq, D = x.q.shape
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    sa.calibrate_theta(q, k, v, tau0=0.008, err_bound=args.err_bound, max_halvings=0, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    th, err, hv = sa.calibrate_theta(q, k, v, tau0=0.008, err_bound=args.err_bound,
+                                     max_halvings=args.max_halvings, **kw)
+    wall = time.perf_counter() - t0
+    rounds = int(hv.max()) + 1
+    return {"metric": "per-head theta calibration wall time (tau from 0.008 halved until "
+                      "Err <= bound)", "value": round(wall * 1e3, 2), "unit": "ms",
+            "n_gpus": 1, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{args.workload}: batch {B}, {Hq}/{x.k.shape[2]} heads, "
+                                   f"d {D}, seq {N}", "err_bound": args.err_bound,
+                       "max_halvings": args.max_halvings},
+            "rounds": rounds, "ms_per_round": round(wall * 1e3 / (rounds + 1), 2),
+            "theta": [round(float(t), 4) for t in th], "halvings": hv.tolist(),
+            "err": [round(float(e), 5) for e in err],
+            "theta0": round(-math.log(0.008), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +346,10 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--kernel", default="attn_block")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time the per-head theta calibration on the prefill workload instead")
+    ap.add_argument("--err-bound", type=float, default=0.4)
+    ap.add_argument("--max-halvings", type=int, default=24)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -329,7 +364,9 @@ def main():
     dev = torch.device("cuda:0")
     import block_sparse_attention_estimate_amd as sa
     sa.load_library()
-    if args.workload in PREFILL:
+    if args.calibrate:
+        out = bench_calibrate(args, dev)
+    elif args.workload in PREFILL:
         out = bench_prefill(args, dev)
     else:
         out = bench_decode(args, dev)
