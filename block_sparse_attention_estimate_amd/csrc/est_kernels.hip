@@ -9,8 +9,10 @@
 //
 // Kernels, in launch order:
 //   est_quant_k       one workgroup per (b, g, key tile): int8 keys + one scale per tile
-//   est_anchor_pool   one workgroup per (b, g, query block): anchor max on bf16 MFMA over the
-//                     sink + local keys, block mean, pooled query (fp64 sum), int8 pooled query
+//   est_anchor_pool   one workgroup per (b, g, query block): the block's sink + local key rows
+//                     staged once in LDS (direct loads) for all G heads, anchor max on bf16
+//                     MFMA, block mean, pooled query (fp64 sum), int8 pooled query
+//                     (est_anchor_pool_gl: the same with global key reads, for large windows)
 //   est_score_block   int8 MFMA of key tiles against pooled queries, block max, margin,
 //                     max over the group's heads -> one keep bit per (query block, key block)
 //   est_score_stripe  same per key column (no block max)
@@ -81,8 +83,188 @@ __global__ __launch_bounds__(256) void est_quant_k(EstArgs a) {
 // S^T = K_region Q^T on 32x32x16 bf16 MFMA: a lane owns one query row (column n) and
 // sees 16 of the 32 keys of each tile, so the row max is in-lane plus one half swap.
 // ---------------------------------------------------------------------------------------
+#define EST_AP_WAVES 16
 template <int D>
-__global__ __launch_bounds__(256) void est_anchor_pool(EstArgs a) {
+__global__ __launch_bounds__(64 * EST_AP_WAVES) void est_anchor_pool(EstArgs a) {
+  constexpr int NW = EST_AP_WAVES;                 // waves: one 32-row tile each (G = 4, bq = 128)
+  constexpr int KS = D / 16;
+  constexpr int ROWB = D * 2;                       // bytes of one key row
+  constexpr int KPITCH = D == 128 ? 272 : 144;      // padded LDS row (conflict-free A reads)
+  // keys one query block can need: a 32-key sink tile block plus the causal window rounded
+  // out to 32-key tiles: sink tiles + (local + bq) rows + 32 of alignment
+  constexpr int MAXROWS = 512;
+  // work item (b, g, i): workgroups are dealt to the 8 XCDs round-robin, and XCD x takes a
+  // contiguous range of items, so the query blocks it runs together are neighbours whose key
+  // windows overlap in its L2
+  int item;
+  {
+    const int total = a.nQB * a.Hkv * a.B;
+    const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+    int start = 0;
+    for (int y = 0; y < x; ++y) start += (total - y + 7) / 8;   // workgroups XCD y receives
+    item = start + k;
+  }
+  const int i = item % a.nQB, g = (item / a.nQB) % a.Hkv, b = item / (a.nQB * a.Hkv);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int G = a.G;
+  const int r0 = i * a.bq;
+  const int r1 = min(a.N, r0 + a.bq);
+  const int nrows = r1 - r0;
+  const int ntph = (a.bq + 31) / 32;
+  __shared__ float xa_s[8][128];
+  __shared__ float qbar_s[8][128];
+  __shared__ __attribute__((aligned(1024))) unsigned char kw[MAXROWS * KPITCH];
+
+  // ---- the key rows this query block needs, staged once in LDS for all G heads ----
+  // tiles of 32 keys: the sink tiles [0, ceil(min(sink, r1) / 32)), then the window tiles
+  // from the tile holding max(0, r0 - local + 1) (not below the sink tiles) through r1 - 1
+  const int hi_blk = r1 - 1;
+  const int sink_end = min(a.sink, r1);
+  const int n_sink_t = (sink_end + 31) / 32;
+  const int lo_blk = max(0, r0 - a.local + 1);
+  const int win_start = max((lo_blk / 32) * 32, n_sink_t * 32);
+  const int n_win_t = win_start <= hi_blk ? (hi_blk - win_start) / 32 + 1 : 0;
+  const int n_rows = (n_sink_t + n_win_t) * 32;     // <= MAXROWS for local <= 352, bq <= 128
+  auto tile_start = [&](int t) { return t < n_sink_t ? t * 32 : win_start + (t - n_sink_t) * 32; };
+  {
+    const uint16_t* kb = a.k + b * a.ks0 + g * a.ks2;
+    const int nwin = (n_rows * KPITCH + 1023) / 1024;
+    for (int w = wave; w < nwin; w += NW) {
+      const int o = w * 1024 + lane * 16;
+      const int r = min(o / KPITCH, n_rows - 1), cb = o % KPITCH;
+      const int key = min(tile_start(r / 32) + (r % 32), a.N - 1);
+      __builtin_amdgcn_global_load_lds(kb + (int64_t)key * a.ks1 + (cb < ROWB ? cb / 2 : 0),
+                                       LDS_PTR(void, kw + w * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+    __syncthreads();
+  }
+  const int k_rd = l32 * KPITCH + half * 16;
+
+  // Q fragments of this wave's n-tiles (32 rows of one head each), the next one loaded while
+  // the current one's MFMAs run
+  auto load_q = [&](int nt, bf16x8* qf) {
+    const int hg = nt / ntph, tr = nt % ntph;
+    const int rowc = min(r0 + tr * 32 + l32, a.N - 1);
+    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + (g * G + hg) * a.qs2 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
+  };
+  bf16x8 qn[KS];
+  if (wave < G * ntph) load_q(wave, qn);
+  for (int nt = wave; nt < G * ntph; nt += NW) {
+    const int hg = nt / ntph, tr = nt % ntph;
+    const int ra = r0 + tr * 32;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
+    if (nt + NW < G * ntph) load_q(nt + NW, qn);
+    if (ra >= r1) continue;
+    const int row = ra + l32;
+    float mx = NEG_INF;
+    const int hi = min(ra + 31, a.N - 1);
+    const int lo = max(0, ra - a.local + 1);
+    // this n-tile's tiles: the sink tiles visible to it, then the window tiles from lo to hi
+    for (int t = 0; t < n_sink_t + n_win_t; ++t) {
+      const int ts = tile_start(t);
+      if (ts > hi) break;                              // tiles ascend; later ones are causal-masked
+      if (t >= n_sink_t && ts + 31 < lo) continue;     // window tile entirely before this window
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(kw + k_rd + t * 32 * KPITCH + ks * 32);
+        acc = mfma_bf16(kf, qf[ks], acc);
+      }
+      // a tile whose 32 keys are visible to all 32 rows of this n-tile needs no mask
+      const bool all_sink = ts + 31 < a.sink && ts + 31 <= ra;
+      const bool all_win = ts >= ra + 31 - a.local + 1 && ts + 31 <= ra;
+      if (all_sink || all_win) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
+          const bool ok = key <= row && (key < a.sink || key >= row - a.local + 1);
+          if (ok) mx = fmaxf(mx, acc[r]);
+        }
+      }
+    }
+    mx = fmaxf(mx, swap_halves(mx));
+    if (half == 0 && row < r1) xa_s[hg][row - r0] = __fmul_rn(mx, a.c);
+  }
+
+  // Pooled query: fp64 sum over the block's rows, one rounding to fp32, fp32 division.
+  // Thread t sums 8 dims (one 16-byte load per row) of every NW-th row; the NW row groups'
+  // fp64 partials meet in LDS (the key window is no longer needed).  Sums of bf16 values are
+  // exact in fp64 here, so neither split changes the result.
+  __syncthreads();
+  double* part = (double*)kw;                       // [NW][G * D]
+  {
+    const int ncg = G * D / 8;                      // 8-dim column groups of the G heads
+    for (int c = tid % 64; c < ncg; c += 64) {
+      const int rg = tid / 64;                      // row group = wave
+      const int hg = c / (D / 8), d8 = (c % (D / 8)) * 8;
+      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r0 * a.qs1 + (g * G + hg) * a.qs2 + d8;
+      double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+      int r = rg;
+      for (; r + 7 * NW < nrows; r += 8 * NW) {     // eight rows of this group in flight
+        u16x8 u[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = *(const u16x8*)(qp + (int64_t)(r + NW * j) * a.qs1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += bf16_bits_to_double(u[j][e]);
+      }
+      for (; r < nrows; r += NW) {
+        const u16x8 u = *(const u16x8*)(qp + (int64_t)r * a.qs1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += bf16_bits_to_double(u[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[rg * G * D + hg * D + d8 + e] = acc[e];
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < G * D; p += 64 * NW) {
+    double t = 0.0;
+    for (int w = 0; w < NW; ++w) t += part[w * G * D + p];
+    qbar_s[p / D][p % D] = __fdiv_rn((float)t, (float)nrows);
+  }
+  __syncthreads();
+
+  for (int hg = wave; hg < G; hg += NW) {
+    // block mean of the anchor (fp64 accumulation)
+    double s = 0.0;
+    for (int r = lane; r < nrows; r += 64) s += (double)xa_s[hg][r];
+    s = wave_sum_d(s);
+    float amax = 0.f;
+    for (int dd = lane; dd < D; dd += 64) amax = fmaxf(amax, fabsf(qbar_s[hg][dd]));
+    amax = wave_max(amax);
+    float inv = 0.f, scale = 1.f;
+    if (amax > 0.f) {
+      inv = __fdiv_rn(127.0f, amax);
+      scale = __fdiv_rn(amax, 127.0f);
+    }
+    const int64_t rowid = ((int64_t)(b * a.Hkv + g) * a.nQB + i) * G + hg;
+    int8_t* dst = a.qq + rowid * D;
+    for (int dd = lane; dd < D; dd += 64) {
+      float r = rintf(__fmul_rn(qbar_s[hg][dd], inv));
+      r = fminf(fmaxf(r, -127.f), 127.f);
+      dst[dd] = (int8_t)(int)r;
+    }
+    if (lane == 0) {
+      a.sq[rowid] = scale;
+      a.abar[rowid] = (float)(s / (double)nrows);
+    }
+  }
+}
+
+// The same pass for windows too large to stage in LDS (sink or local beyond the sizes the
+// staged kernel is built for): key tiles are read from global memory per row tile.
+template <int D>
+__global__ __launch_bounds__(256) void est_anchor_pool_gl(EstArgs a) {
   constexpr int KS = D / 16;
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -568,7 +750,13 @@ __global__ __launch_bounds__(256) void est_compact(EstArgs a, int unit) {
 template <int D>
 static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream_t s) {
   hipLaunchKernelGGL(est_quant_k<D>, dim3(a.nKB, a.Hkv, a.B), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(est_anchor_pool<D>, dim3(a.nQB, a.Hkv, a.B), dim3(256), 0, s, a);
+  // rows of the staged key window: sink tiles + window tiles of the largest query block
+  const int sink_rows = ((min(a.sink, a.N) + 31) / 32) * 32;
+  const int win_rows = ((a.local - 1 + a.bq - 1) / 32 + 2) * 32;
+  if (sink_rows + win_rows <= 512)
+    hipLaunchKernelGGL(est_anchor_pool<D>, dim3(a.nQB * a.Hkv * a.B), dim3(64 * EST_AP_WAVES), 0, s, a);
+  else
+    hipLaunchKernelGGL(est_anchor_pool_gl<D>, dim3(a.nQB, a.Hkv, a.B), dim3(256), 0, s, a);
   const int rows_total = a.nQB * a.G;
   const int n_rt = (rows_total + 255) / 256;
   const int n_jc = (a.nKB + 31) / 32;
