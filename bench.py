@@ -264,6 +264,8 @@ def bench_decode(args, dev):
     q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
     cl = torch.from_numpy(x.cache_len).to(dev)
     kbar = sa.build_block_summary(kc, cl, block_k=x.block_k)
+    if args.summary == "q4":
+        kbar = sa.quantize_block_summary(kbar, block_k=x.block_k)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     kw = dict(block_k=x.block_k, top_k=x.top_k, sink=x.sink, local=x.local)
@@ -280,7 +282,7 @@ def bench_decode(args, dev):
     us = e0.elapsed_time(e1) * 1e3 / args.steps
     nkb = -(-L // x.block_k)
     sel_bytes = B * Hkv * x.top_k * x.block_k * D * 2 * 2
-    sum_bytes = B * Hkv * nkb * D * 2
+    sum_bytes = B * Hkv * nkb * (D * 2 if args.summary == "bf16" else D // 2 + D // 32 * 2)
     gbs = (sel_bytes + sum_bytes) / (us * 1e-6) / 1e9
     return {"metric": "sparse decode step time and achieved HBM GB/s",
             "value": round(gbs, 1), "unit": "GB/s (algorithmic)", "n_gpus": 1,
@@ -288,7 +290,8 @@ def bench_decode(args, dev):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
             "config": {"workload": f"{args.workload}: batch {B}, {Hq}/{Hkv} heads, d {D}, "
-                                   f"cache {L}, top-{x.top_k} blocks of {x.block_k}",
+                                   f"cache {L}, top-{x.top_k} blocks of {x.block_k}, "
+                                   f"{args.summary} block summaries",
                        "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
             "us_per_step": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -346,6 +349,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--kernel", default="attn_block")
+    ap.add_argument("--summary", choices=["bf16", "q4"], default="bf16",
+                    help="decode: block summaries in bf16 or 4-bit codes + bf16 scales")
     ap.add_argument("--calibrate", action="store_true",
                     help="time the per-head theta calibration on the prefill workload instead")
     ap.add_argument("--err-bound", type=float, default=0.4)

@@ -23,8 +23,9 @@ from . import _lib
 from ._lib import (SA_BLOCK, SA_STRIPE, SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE,  # noqa: F401
                    SA_OP_CALIBRATE, SaError)
 
-__all__ = ["Lists", "estimate_mask", "sparse_prefill", "build_block_summary", "sparse_decode",
-           "calibrate_theta", "workspace_size", "SaError", "load_library"]
+__all__ = ["Lists", "estimate_mask", "sparse_prefill", "build_block_summary",
+           "quantize_block_summary", "sparse_decode", "calibrate_theta", "workspace_size",
+           "SaError", "load_library"]
 
 
 def load_library():
@@ -249,10 +250,28 @@ def build_block_summary(k_cache, cache_len, *, block_k=64, n_q_heads=None, out=N
     return kbar
 
 
+def quantize_block_summary(k_summary, *, block_k=64, seq_k=None, stream=None):
+    """4-bit summaries (sa_quantize_block_summary) of bf16 summaries [B, nKB, Hkv, d]:
+    returns (codes uint8 [B, nKB, Hkv, d/2], scales bf16 [B, nKB, Hkv, d/32])."""
+    lib = _lib.load()
+    _check_bf16("k_summary", k_summary, 4)
+    B, nkb, Hkv, D = k_summary.shape
+    s = _lib.SaShape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = B, Hkv, Hkv, D
+    s.seq_q, s.seq_k = 1, seq_k if seq_k is not None else nkb * block_k
+    codes = torch.empty((B, nkb, Hkv, D // 2), dtype=torch.uint8, device=k_summary.device)
+    scales = torch.empty((B, nkb, Hkv, D // 32), dtype=torch.bfloat16, device=k_summary.device)
+    _lib.check(lib.sa_quantize_block_summary(ctypes.byref(s), block_k, _ptr(k_summary), _ptr(codes),
+                                             _ptr(scales), _stream(stream)),
+               "sa_quantize_block_summary")
+    return codes, scales
+
+
 def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_k=64, sink=32,
                   local=256, n_splits=0, softmax_scale=0.0, workspace=None, out=None,
                   return_selected=True, stream=None):
-    """Top-K block-sparse decode (sa_sparse_decode).  q [B, Hq, d]; caches [B, L, Hkv, d].
+    """Top-K block-sparse decode (sa_sparse_decode, or sa_sparse_decode_q4 when k_summary is
+    the (codes, scales) pair of quantize_block_summary).  q [B, Hq, d]; caches [B, L, Hkv, d].
     Returns (o [B, Hq, d] bf16, lse [B, Hq] fp32, selected [B, Hkv, top_k] int32 or None)."""
     lib = _lib.load()
     _check_bf16("v_cache", v_cache, 4)
@@ -271,8 +290,15 @@ def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_
     sel = None
     if return_selected:
         sel = torch.empty((B, k_cache.shape[2], top_k), dtype=torch.int32, device=q.device)
-    _lib.check(lib.sa_sparse_decode(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k_cache),
-                                    _ptr(v_cache), _ptr(k_summary), _ptr(cache_len), _ptr(o),
-                                    _ptr(lse), _ptr(sel), _ptr(workspace), workspace.numel(),
-                                    _stream(stream)), "sa_sparse_decode")
+    if isinstance(k_summary, (tuple, list)):
+        codes, scales = k_summary
+        _lib.check(lib.sa_sparse_decode_q4(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k_cache),
+                                           _ptr(v_cache), _ptr(codes), _ptr(scales), _ptr(cache_len),
+                                           _ptr(o), _ptr(lse), _ptr(sel), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)), "sa_sparse_decode_q4")
+    else:
+        _lib.check(lib.sa_sparse_decode(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(k_summary), _ptr(cache_len), _ptr(o),
+                                        _ptr(lse), _ptr(sel), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)), "sa_sparse_decode")
     return o, lse, sel

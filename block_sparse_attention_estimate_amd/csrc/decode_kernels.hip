@@ -10,8 +10,10 @@
 // Kernels:
 //   dec_block_summary  kbar[b, J, g, :] = mean of the block's cached keys (exact fp64 sum ->
 //                      fp32 -> bf16), all KV heads of a block per workgroup, coalesced
+//   dec_summary_q4     4-bit summaries: codes and one bf16 scale per 32 dims
 //   dec_score_rows     score[b, g, J] = max over the group's heads of c * q_h . kbar_J, one
 //                      coalesced summary row per 16-lane group, DPP reductions
+//   dec_score_q4_mfma  the same from 4-bit summaries on bf16 MFMA (heads as MFMA columns)
 //   dec_select_radix   forced blocks + top (K - |F|) others by (score desc, block asc): radix
 //                      select of the K-th key (11 bits per pass, LDS histograms), ascending
 //                      output list
@@ -137,6 +139,148 @@ __global__ __launch_bounds__(256) void dec_score_rows(DecArgs a) {
     }
     if (sub == 0 && J < a.nKB)
       a.scores[((int64_t)b * a.Hkv + g) * a.nKB + J] = J < nb ? mx * a.c : NEG_INF;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 4-bit block summaries (SpotAttention "Key findings": an INT4 / FP4 selector key cache,
+// 3.5x smaller at no accuracy cost).  One thread per group of 32 dims of a bf16 summary row:
+// a = max |x|; scale = bf16(fp32(a / 7)); code = clamp(rint_even(fp32(x * fp32(7 / a))), -7, 7)
+// (all zero when a = 0).  Stored as offset-binary nibbles u = code + 8, 8 dims per 32-bit
+// word with dim 2j in nibble j and dim 2j+1 in nibble j+4: (word >> 4j) & 0x000F000F then
+// holds the pair (2j, 2j+1) in the two 16-bit halves, and OR-ing 0x4300 into each half
+// makes the bf16 values 128 + u = 136 + code exactly.
+__global__ __launch_bounds__(256) void dec_summary_q4(const uint16_t* ksum, uint8_t* codes,
+                                                      uint16_t* scales, int64_t n_groups) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= n_groups) return;
+  const uint16_t* x = ksum + gi * 32;
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u16x8 u = *(const u16x8*)(x + 8 * j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * j + e] = bf16_bits_to_float(u[e]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  const float inv = amax > 0.f ? __fdiv_rn(7.0f, amax) : 0.f;
+  unsigned int w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const float r = fminf(fmaxf(rintf(__fmul_rn(v[e], inv)), -7.f), 7.f);
+    const int d = e & 7;                               // dim 2j -> nibble j, 2j+1 -> nibble j+4
+    const int nib = (d >> 1) + ((d & 1) << 2);
+    w[e >> 3] |= (unsigned int)((int)r + 8) << (4 * nib);
+  }
+  *(u32x4*)(codes + gi * 16) = (u32x4){w[0], w[1], w[2], w[3]};
+  scales[gi] = amax > 0.f ? float_to_bf16_bits(__fdiv_rn(amax, 7.0f)) : (uint16_t)0;
+}
+
+// score[b, g, J] from 4-bit summaries on bf16 MFMA: S = Q Kbar'^T with the G query heads as
+// the 32-row dimension (zero beyond G) and 32 blocks as the columns, Kbar' holding the
+// summaries as bf16 values 136 + code.  Lane l then owns block J0 + l % 32 and heads
+// (l / 32) * 4 + 8 (r / 4) + r % 4 of its 16 accumulator entries, so for G <= 8 the group's
+// heads sit in entries r < 4 of the lane and of lane l ^ 32.  Per 32-dim group gi the
+// accumulator is sum q (136 + code); subtracting 136 sum q (per head and group) and
+// multiplying by the block's group scale gives sum q * scale * code (fp32, well inside the
+// selection's ambiguity band).  Each wave scores DEC_Q4_TILES consecutive 32-block tiles,
+// all of whose codes and scales are loaded up front.  Two tiles per wave keeps 4096 waves
+// in flight at 2048 blocks x 8 KV heads x batch 16 while one tile's loads still overlap
+// the other's MFMA work (measured: one tile 14.0 us, two 12.6 us, four 13.2 us).
+constexpr int DEC_Q4_TILES = 2;
+template <int D>
+__global__ __launch_bounds__(256) void dec_score_q4_mfma(DecArgs a) {
+  constexpr int KS = D / 16, NGR = D / 32, TILES = DEC_Q4_TILES;
+  const int g = blockIdx.x, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = tid >> 6;
+  const int Jw = (blockIdx.y * 4 + wave) * (32 * TILES);   // this wave's first block
+  if (Jw >= a.nKB) return;
+  const int nb = (min(max(a.cache_len[b], 0), a.L) + a.bk - 1) / a.bk;
+  const int64_t row0 = ((int64_t)b * a.nKB) * a.Hkv + g;   // row of block J: row0 + J * Hkv
+  // loads of one tile: the lane's code words (B operand: block J0 + l % 32, dims 16 ks +
+  // 8 half .. +8) and that block's group scales
+  auto load = [&](int J0, unsigned int* w, u32x2& sc) {
+    const int64_t rowi = row0 + (int64_t)min(J0 + l32, a.nKB - 1) * a.Hkv;
+    const uint8_t* crow = a.ksum_q4 + rowi * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) w[ks] = *(const unsigned int*)(crow + (2 * ks + half) * 4);
+    if (NGR == 4) sc = *(const u32x2*)(a.ksum_scale + rowi * NGR);
+    else sc = (u32x2){*(const unsigned int*)(a.ksum_scale + rowi * NGR), 0u};
+  };
+  // every tile's loads are issued up front (10 registers a tile)
+  unsigned int wt[TILES][KS];
+  u32x2 st[TILES];
+#pragma unroll
+  for (int tt = 0; tt < TILES; ++tt) load(Jw + 32 * tt, wt[tt], st[tt]);
+  // Q (A operand): lane l holds head l % 32 of the group (zero beyond G), dims 16 ks + 8 half
+  bf16x8 qf[KS];
+  float qs_l[NGR];                       // 136 * sum of head l % 32's dims in group gi
+  {
+    const int hc = min(l32, a.G - 1);
+    const uint16_t* qp = a.q + b * a.qs0 + (g * a.G + hc) * a.qs2 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = *(const bf16x8*)(qp + ks * 16);
+      if (l32 >= a.G) qf[ks] = (bf16x8){};
+    }
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi) {
+      float t = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += (float)qf[2 * gi + k2][e];
+      qs_l[gi] = 136.0f * half_pair_sum(t);
+    }
+  }
+  // the corrections of the heads in this lane's entries r = 0..3: heads 4 half + r
+  float qcor[4][NGR];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi) {
+      const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qs_l[gi]), r));
+      const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qs_l[gi]), 4 + r));
+      qcor[r][gi] = half ? v1 : v0;
+    }
+  const int nh = min(a.G - 4 * half, 4);            // valid heads among this lane's r = 0..3
+  float* out = a.scores + ((int64_t)b * a.Hkv + g) * a.nKB;
+#pragma unroll
+  for (int tt = 0; tt < TILES; ++tt) {
+    const int J0 = Jw + 32 * tt;
+    const unsigned int* w = wt[tt];
+    const u32x2 sc = st[tt];
+    f32x16 acc[NGR];
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi) acc[gi] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 pr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pr[j] = ((w[ks] >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+      bf16x8 kf;
+      __builtin_memcpy(&kf, &pr, 16);
+      acc[ks / 2] = mfma_bf16(qf[ks], kf, acc[ks / 2]);
+    }
+    const unsigned int sw[2] = {sc.x, sc.y};
+    float sg[NGR];
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi)
+      sg[gi] = bf16_bits_to_float((unsigned short)((sw[gi >> 1] >> (16 * (gi & 1))) & 0xFFFFu));
+    float mx = NEG_INF;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < NGR; ++gi) v += sg[gi] * (acc[gi][r] - qcor[r][gi]);
+      if (r < nh) mx = fmaxf(mx, v);
+    }
+    mx = half_pair_max(mx) * a.c;                      // heads 4..7 live in lane ^ 32
+    const int J = J0 + l32;
+    if (half == 0 && J < a.nKB) out[J] = J < nb ? mx : NEG_INF;
   }
 }
 
@@ -661,11 +805,16 @@ hipError_t launch_block_summary(const DecArgs& a, hipStream_t s) {
 template <int D>
 static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
   const dim3 sgrid(a.Hkv, (a.nKB + 127) / 128, a.B);
-  switch (a.G) {
-    case 1: hipLaunchKernelGGL((dec_score_rows<D, 1>), sgrid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dec_score_rows<D, 2>), sgrid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((dec_score_rows<D, 4>), sgrid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((dec_score_rows<D, 8>), sgrid, dim3(256), 0, s, a); break;
+  if (a.ksum_q4) {
+    hipLaunchKernelGGL(dec_score_q4_mfma<D>, dim3(a.Hkv, (a.nKB + 128 * DEC_Q4_TILES - 1) / (128 * DEC_Q4_TILES), a.B),
+                       dim3(256), 0, s, a);
+  } else {
+    switch (a.G) {
+      case 1: hipLaunchKernelGGL((dec_score_rows<D, 1>), sgrid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((dec_score_rows<D, 2>), sgrid, dim3(256), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((dec_score_rows<D, 4>), sgrid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((dec_score_rows<D, 8>), sgrid, dim3(256), 0, s, a); break;
+    }
   }
   hipLaunchKernelGGL(dec_select_radix, dim3(a.Hkv, a.B), dim3(256), a.nKB * sizeof(unsigned int), s, a);
   const dim3 grid(a.n_splits, a.Hkv, a.B);
@@ -680,6 +829,14 @@ static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
     }
   }
   hipLaunchKernelGGL(dec_combine<D>, dim3(a.Hq, a.B), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_summary_q4(const uint16_t* ksum, uint8_t* codes, uint16_t* scales, int64_t n_groups,
+                             hipStream_t s) {
+  if (n_groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(dec_summary_q4, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0, s, ksum,
+                     codes, scales, n_groups);
   return hipGetLastError();
 }
 

@@ -300,15 +300,18 @@ sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k, const v
   return SA_OK;
 }
 
-sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params, const void* q,
-                           const void* k_cache, const void* v_cache, const void* k_summary,
-                           const int32_t* cache_len, void* o, float* lse, int32_t* selected,
-                           void* ws, size_t ws_bytes, hipStream_t stream) {
+// shared by the bf16- and the 4-bit-summary decode entries (exactly one summary form given)
+static sa_status decode_impl(const sa_shape* shape, const sa_decode_params* params, const void* q,
+                             const void* k_cache, const void* v_cache, const void* k_summary,
+                             const void* codes, const void* scales, const int32_t* cache_len,
+                             void* o, float* lse, int32_t* selected, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   sa_status st = check_decode(shape, params);
   if (st != SA_OK) return st;
-  if (!q || !k_cache || !v_cache || !k_summary || !cache_len || !o) return SA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_summary) ||
-      !aligned16(o))
+  if (!q || !k_cache || !v_cache || !cache_len || !o) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return SA_ERR_SHAPE;
+  if (k_summary ? !aligned16(k_summary) : (!aligned16(codes) || !aligned16(scales)))
     return SA_ERR_SHAPE;
   const DecLayout L = dec_layout(shape, params);
   if (!ws) return SA_ERR_WORKSPACE;
@@ -320,6 +323,8 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params
   a.kc = (const uint16_t*)k_cache;
   a.vc = (const uint16_t*)v_cache;
   a.ksum = (const uint16_t*)k_summary;
+  a.ksum_q4 = (const uint8_t*)codes;
+  a.ksum_scale = (const uint16_t*)scales;
   a.cache_len = cache_len;
   a.o = (uint16_t*)o;
   a.lse = lse;
@@ -333,6 +338,40 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params
   a.c = resolve_scale(params->softmax_scale, shape->head_dim);
   if (launch_decode(a, stream) != hipSuccess) return SA_ERR_DEVICE;
   return SA_OK;
+}
+
+sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params, const void* q,
+                           const void* k_cache, const void* v_cache, const void* k_summary,
+                           const int32_t* cache_len, void* o, float* lse, int32_t* selected,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!k_summary) return SA_ERR_NULL;
+  return decode_impl(shape, params, q, k_cache, v_cache, k_summary, nullptr, nullptr, cache_len, o,
+                     lse, selected, ws, ws_bytes, stream);
+}
+
+sa_status sa_quantize_block_summary(const sa_shape* shape, int32_t block_k, const void* k_summary,
+                                    void* codes, void* scales, hipStream_t stream) {
+  sa_status st = check_shape_common(shape);
+  if (st != SA_OK) return st;
+  if (!k_summary || !codes || !scales) return SA_ERR_NULL;
+  if (block_k < 1) return SA_ERR_PARAM;
+  if (!aligned16(k_summary) || !aligned16(codes) || !aligned16(scales)) return SA_ERR_SHAPE;
+  const int64_t n_groups = (int64_t)shape->batch * ceil_div(shape->seq_k, block_k) *
+                           shape->n_kv_heads * (shape->head_dim / 32);
+  if (launch_summary_q4((const uint16_t*)k_summary, (uint8_t*)codes, (uint16_t*)scales, n_groups,
+                        stream) != hipSuccess)
+    return SA_ERR_DEVICE;
+  return SA_OK;
+}
+
+sa_status sa_sparse_decode_q4(const sa_shape* shape, const sa_decode_params* params, const void* q,
+                              const void* k_cache, const void* v_cache, const void* summary_codes,
+                              const void* summary_scales, const int32_t* cache_len, void* o,
+                              float* lse, int32_t* selected, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!summary_codes || !summary_scales) return SA_ERR_NULL;
+  return decode_impl(shape, params, q, k_cache, v_cache, nullptr, summary_codes, summary_scales,
+                     cache_len, o, lse, selected, ws, ws_bytes, stream);
 }
 
 sa_status sa_calibrate_theta(const sa_shape* shape, const sa_sparse_params* params,

@@ -49,6 +49,8 @@ struct DecArgs {
   const uint16_t* kc;
   const uint16_t* vc;
   const uint16_t* ksum;
+  const uint8_t* ksum_q4;    // nullable: 4-bit summary codes [B, nKB, Hkv, D/2] (scoring uses these)
+  const uint16_t* ksum_scale;  // bf16 scales [B, nKB, Hkv, D/32] of the 4-bit codes
   const int32_t* cache_len;
   uint16_t* o;
   float* lse;
@@ -63,6 +65,8 @@ struct DecArgs {
 hipError_t launch_estimate(const EstArgs& a, int granularity, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs& a, int D, int granularity, hipStream_t s);
 hipError_t launch_block_summary(const DecArgs& a, hipStream_t s);
+hipError_t launch_summary_q4(const uint16_t* ksum, uint8_t* codes, uint16_t* scales, int64_t n_groups,
+                             hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
 hipError_t launch_head_l1(const uint16_t* o_ref, const uint16_t* o_sp, int B, int N, int Hq, int D,
                           double* err, hipStream_t s);

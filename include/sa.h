@@ -164,6 +164,24 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params
                            void* o, float* lse, int32_t* selected,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* 4-bit block summaries (SpotAttention, "Key findings": quantising the selector's key cache
+ * to INT4 / FP4 shrinks it 3.5x at no accuracy cost).  From bf16 summaries (as written by
+ * sa_build_block_summary, contiguous [B, ceil(seq_k/block_k), Hkv, d]) each row is cut into
+ * groups of 32 dims; a group with a = max |x| gets scale = fp32(a / 7) rounded to bf16 and
+ * codes clamp(rint_even(fp32(x * fp32(7 / a))), -7, 7) (zeros and scale 0 when a = 0).
+ * codes: device uint8 [B, nKB, Hkv, d/2], two 4-bit two's-complement codes per byte with the
+ * even dim in the low nibble; scales: device bf16 [B, nKB, Hkv, d/32].  4.5 bits per dim. */
+sa_status sa_quantize_block_summary(const sa_shape* shape, int32_t block_k, const void* k_summary,
+                                    void* codes, void* scales, hipStream_t stream);
+
+/* sa_sparse_decode scoring the blocks from 4-bit summaries (scale * code per dim) instead
+ * of bf16 ones; everything else as sa_sparse_decode, with the same workspace size. */
+sa_status sa_sparse_decode_q4(const sa_shape* shape, const sa_decode_params* params,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              const void* summary_codes, const void* summary_scales,
+                              const int32_t* cache_len, void* o, float* lse, int32_t* selected,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Per-head threshold calibration (SALE, "Assumptions & free parameters": the per-head
  * threshold tau starts at 0.008 and is halved until the L1 output error
  * Err(tau) = ||O - O~||_1 / N meets a user-chosen bound; the relative-score test keeps a

@@ -37,6 +37,7 @@ from .estimate import (  # noqa: F401
     AMBIGUITY_BAND,
 )
 from .attention import attention_rows, attention_all, dense_causal_reference_mask  # noqa: F401
-from .decode import block_summary, decode_select, decode_attention  # noqa: F401
+from .decode import (block_summary, decode_select, decode_attention, quantize_summary_q4,  # noqa: F401
+                     dequantize_summary_q4, pack_q4)
 from .diagnostics import pruned_mass_fraction, sparsity_from_kept, sale_log_margin  # noqa: F401
 from .calibrate import full_lists, head_l1_error, calibrate_theta  # noqa: F401

@@ -13,6 +13,13 @@ Sources (review pages, cited by title and section):
 * KVpop (arXiv 2607.05061) -- referee minor comment 4: grouped query heads are
   aggregated with max.
 
+Quantised summaries (SpotAttention "Key findings": an INT4 / FP4 selector key cache is 3.5x
+smaller at no accuracy cost): each summary row is cut into groups of 32 dims; a group with
+a = max |x| gets the scale fp32(a / 7) rounded to bf16 and codes clamp(rint_even(fp32(x *
+fp32(7 / a))), -7, 7) (all zero for a = 0); the score then uses scale * code.  Storage
+(``pack_q4``) is a layout choice of this library, not the pages'.  4 code bits
+per dim plus one 16-bit scale per 32 dims is 4.5 bits per dim instead of 16 (3.56x).
+
 Readings: the summary is the mean of the block's cached keys (fp64 sum, fp64 division,
 rounded to fp32 and then to bf16, round to nearest even); the block score is the max over
 the group's query heads of c * q_h . kbar_J; the forced set is every block overlapping the
@@ -49,6 +56,46 @@ def block_summary(k_cache, cache_len, block_k: int) -> np.ndarray:
     return out
 
 
+Q4_GROUP = 32
+
+
+def quantize_summary_q4(kbar: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """kbar bf16 bits [..., D] -> (codes int8 [..., D] in [-7, 7], scales bf16 bits
+    [..., D / 32])."""
+    x = _f64(kbar).astype(np.float32)
+    shp = x.shape[:-1] + (x.shape[-1] // Q4_GROUP, Q4_GROUP)
+    xg = x.reshape(shp)
+    a = np.abs(xg).max(axis=-1)                                     # fp32 [..., D/32]
+    nz = a > 0
+    inv = np.where(nz, np.float32(7.0) / np.where(nz, a, np.float32(1.0)), np.float32(0.0))
+    inv = inv.astype(np.float32)
+    y = (xg * inv[..., None]).astype(np.float32)                  # one fp32 rounding
+    codes = np.clip(np.rint(y), -7, 7).astype(np.int8)
+    scale = np.where(nz, (a / np.float32(7.0)).astype(np.float32), np.float32(0.0))
+    return codes.reshape(x.shape), _f32_to_bf16_bits(scale.astype(np.float32))
+
+
+def dequantize_summary_q4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """scale * code as float64 [..., D] (exact: a bf16 scale times a small integer)."""
+    c = codes.astype(np.float64)
+    shp = c.shape[:-1] + (c.shape[-1] // Q4_GROUP, Q4_GROUP)
+    return (c.reshape(shp) * _f64(scales)[..., None]).reshape(c.shape)
+
+
+def pack_q4(codes: np.ndarray) -> np.ndarray:
+    """Storage of the codes: offset-binary nibbles u = code + 8 (1 .. 15); each 32-bit
+    little-endian word holds 8 consecutive dims, dim 2j in nibble j and dim 2j + 1 in nibble
+    j + 4 (j = 0..3).  Returns uint8 [..., D / 2]."""
+    u = (codes.astype(np.int64) + 8).astype(np.uint32)
+    shp = u.shape[:-1] + (u.shape[-1] // 8, 8)
+    u = u.reshape(shp)
+    w = np.zeros(shp[:-1], dtype=np.uint32)
+    for j in range(4):
+        w |= u[..., 2 * j] << np.uint32(4 * j)
+        w |= u[..., 2 * j + 1] << np.uint32(4 * (j + 4))
+    return w.view(np.uint8).reshape(codes.shape[:-1] + (codes.shape[-1] // 2,))
+
+
 def decode_forced(n_blocks: int, length: int, block_k: int, sink: int, local: int) -> np.ndarray:
     J = np.arange(n_blocks)
     sink_hit = J * block_k < sink
@@ -74,6 +121,7 @@ def decode_select(q, kbar, cache_len, *, block_k: int, top_k: int, sink: int, lo
         for g in range(Hkv):
             heads = np.nonzero(kv_of_q == g)[0]
             kb = _f64(kbar[b, :nkb, g, :])                          # [nkb, D]
+            # (kbar may be bf16 bits or float values, e.g. dequantised q4 summaries)
             qh = _f64(q[b, heads, :])                               # [heads, D]
             score = (c * (qh @ kb.T)).max(axis=0)                   # [nkb]
             forced = decode_forced(nkb, lb, block_k, sink, local)

@@ -16,7 +16,7 @@ from block_sparse_attention_estimate_amd import _lib  # noqa: E402
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -126,4 +126,10 @@ def test_validation_codes(lib):
     ds.seq_q = 1
     assert lib.sa_build_block_summary(ctypes.byref(ds), 0, FAKE, FAKE, FAKE, None) == _lib.SA_ERR_PARAM
     assert lib.sa_build_block_summary(ctypes.byref(ds), 64, None, FAKE, FAKE, None) == _lib.SA_ERR_NULL
+    assert lib.sa_quantize_block_summary(ctypes.byref(ds), 0, FAKE, FAKE, FAKE, None) == _lib.SA_ERR_PARAM
+    assert lib.sa_quantize_block_summary(ctypes.byref(ds), 64, FAKE, None, FAKE, None) == _lib.SA_ERR_NULL
+    args_q4 = [ctypes.byref(ds), ctypes.byref(dp), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None]
+    assert lib.sa_sparse_decode_q4(*args_q4, FAKE, dneed, None) == _lib.SA_ERR_NULL
+    args_q4[6] = FAKE
+    assert lib.sa_sparse_decode_q4(*args_q4, FAKE, dneed - 1, None) == _lib.SA_ERR_WORKSPACE
     assert lib.sa_workspace_size(_lib.SA_OP_PREFILL, ctypes.byref(s), ctypes.byref(p)) == 0

@@ -96,23 +96,31 @@ def test_stripe_64k_sampled(dev):
     _prefill_parity(dev, "stripe_64k", n_rows=24, n_attn=10)
 
 
-def test_decode_b16_128k(dev):
+@pytest.mark.parametrize("summary", ["bf16", "q4"])
+def test_decode_b16_128k(dev, summary):
     import torch
     import block_sparse_attention_estimate_amd as sa
-    log("generating decode_b16_128k")
+    log(f"generating decode_b16_128k ({summary} summaries)")
     x = synth.make_decode("decode_b16_128k")
     B, Hq, D = x.q.shape
     q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
     cl = torch.from_numpy(x.cache_len).to(dev)
     kbar = sa.build_block_summary(kc, cl, block_k=x.block_k)
-    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=x.block_k, top_k=x.top_k,
+    summ = kbar if summary == "bf16" else sa.quantize_block_summary(kbar, block_k=x.block_k)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, summ, cl, block_k=x.block_k, top_k=x.top_k,
                                    sink=x.sink, local=x.local)
     torch.cuda.synchronize()
     log("oracle block summaries")
     kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, x.block_k)
     kb = kbar.view(torch.int16).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(kb, kbar_ref)
-    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=x.block_k, top_k=x.top_k,
+    score_src = kbar_ref
+    if summary == "q4":
+        c_ref, s_ref = oracle.quantize_summary_q4(kbar_ref)
+        np.testing.assert_array_equal(summ[0].cpu().numpy(), oracle.pack_q4(c_ref))
+        np.testing.assert_array_equal(summ[1].view(torch.int16).cpu().numpy().view(np.uint16), s_ref)
+        score_src = oracle.dequantize_summary_q4(c_ref, s_ref)
+    ref = oracle.decode_select(x.q, score_src, x.cache_len, block_k=x.block_k, top_k=x.top_k,
                                sink=x.sink, local=x.local)
     s = sel.cpu().numpy()
     flips = 0

@@ -175,3 +175,43 @@ def test_decode_reduced(dev, batch, seq, hq, hkv, d, top_k, bk):
     assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
     assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
     log(f"  decode ok: flips={flips} max|dO|={err.max():.2e} mean={err.mean():.2e}")
+
+
+@pytest.mark.parametrize("batch,seq,hq,hkv,d,top_k", [(3, 5000, 8, 2, 128, 24), (2, 3000, 4, 1, 64, 8)])
+def test_decode_q4_reduced(dev, batch, seq, hq, hkv, d, top_k):
+    """4-bit summaries: codes and scales bit-exact, selection from scale * code within the
+    ambiguity band, attention over the selection as for bf16 summaries."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_decode(batch=batch, seq=seq, hq=hq, hkv=hkv, head_dim=d, top_k=top_k)
+    if batch >= 2:
+        x.cache_len[1] = seq - 937
+    log(f"decode q4 B={batch} L={seq} Hq={hq} Hkv={hkv} d={d} K={top_k}")
+    q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=64)
+    codes, scales = sa.quantize_block_summary(kbar, block_k=64)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, (codes, scales), cl, block_k=64, top_k=top_k,
+                                   sink=32, local=256)
+    torch.cuda.synchronize()
+    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, 64)
+    c_ref, s_ref = oracle.quantize_summary_q4(kbar_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), oracle.pack_q4(c_ref))
+    np.testing.assert_array_equal(scales.view(torch.int16).cpu().numpy().view(np.uint16), s_ref)
+    deq = oracle.dequantize_summary_q4(c_ref, s_ref)
+    ref = oracle.decode_select(x.q, deq, x.cache_len, block_k=64, top_k=top_k, sink=32, local=256)
+    s = sel.cpu().numpy()
+    used, flips = {}, 0
+    for (b, g), r in ref.items():
+        k_ = min(top_k, -(-int(x.cache_len[b]) // 64))
+        got = s[b, g, :k_]
+        assert (s[b, g, k_:] == -1).all() and np.all(np.diff(got) > 0)
+        diff = set(got.tolist()) ^ set(r["selected"].tolist())
+        assert diff <= set(r["ambiguous"].tolist()), ((b, g), sorted(diff))
+        flips += len(diff)
+        used[(b, g)] = got
+    O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used, block_k=64)
+    err = np.abs(o.float().cpu().numpy() - O)
+    assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
+    assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
+    log(f"  decode q4 ok: flips={flips} max|dO|={err.max():.2e}")
