@@ -169,8 +169,12 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params
  * sa_build_block_summary, contiguous [B, ceil(seq_k/block_k), Hkv, d]) each row is cut into
  * groups of 32 dims; a group with a = max |x| gets scale = fp32(a / 7) rounded to bf16 and
  * codes clamp(rint_even(fp32(x * fp32(7 / a))), -7, 7) (zeros and scale 0 when a = 0).
- * codes: device uint8 [B, nKB, Hkv, d/2], two 4-bit two's-complement codes per byte with the
- * even dim in the low nibble; scales: device bf16 [B, nKB, Hkv, d/32].  4.5 bits per dim. */
+ * codes: device uint8 [B, nKB, Hkv, d/2] holding offset-binary nibbles u = code + 8 (1..15):
+ * each little-endian 32-bit word covers 8 consecutive dims, dim 2j in nibble j and dim 2j+1
+ * in nibble j+4 (j = 0..3); scales: device bf16 [B, nKB, Hkv, d/32].  4.5 bits per dim.
+ * Errors: the shape checks common to every entry point, SA_ERR_NULL for a null pointer,
+ * SA_ERR_PARAM for block_k < 1, SA_ERR_SHAPE for a pointer not 16-byte aligned.
+ * Asynchronous on the stream. */
 sa_status sa_quantize_block_summary(const sa_shape* shape, int32_t block_k, const void* k_summary,
                                     void* codes, void* scales, hipStream_t stream);
 
