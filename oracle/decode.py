@@ -26,6 +26,15 @@ the group's query heads of c * q_h . kbar_J; the forced set is every block overl
 sink tokens [0, sink) or the recency window [L - local, L - 1]; the remaining K - |F|
 blocks are the highest scores, ties to the lower block index; the query sits at position
 L - 1 and sees every cached token.
+
+Per-query budget (SpotAttention abstract and Figure 2 caption: a dual top-p rule reads the
+budget from the selector's own distribution over blocks, and I holds the sink prefix, the
+recency window and the top-p content blocks; Figure 7 plots the cumulative mass of the blocks
+kept in descending score order).  The rule is named but not spelled out; the reading here:
+the distribution is pi_J = exp(score_J) / sum_J' exp(score_J') over the blocks of the cache,
+the forced blocks count first, and then content blocks are added in (score desc, block asc)
+order until the cumulative share reaches top_p; the selection never exceeds K blocks in all
+(the second bound of the rule).  top_p = 0 keeps the fixed K.
 """
 from __future__ import annotations
 
@@ -34,6 +43,8 @@ import numpy as np
 from .estimate import _f64, softmax_scale
 
 AMBIGUITY_BAND = 1e-3
+# a budget is ambiguous when a cumulative share next to the decision lies this close to top_p
+TOP_P_BAND = 1e-4
 
 
 def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -104,10 +115,34 @@ def decode_forced(n_blocks: int, length: int, block_k: int, sink: int, local: in
     return J[sink_hit | win_hit]
 
 
+def top_p_budget(score: np.ndarray, is_forced: np.ndarray, top_p: float):
+    """Number of content blocks the top-p rule adds to the forced set: the fewest, taken in
+    (score desc, block asc) order, that bring forced share + their share of
+    pi = softmax(score) to at least top_p.  Returns (k, order, ambiguous): order is the
+    content blocks in that order; ambiguous is True when the cumulative share after k - 1 or
+    after k blocks lies within TOP_P_BAND of top_p."""
+    score = np.asarray(score, dtype=np.float64)
+    w = np.exp(score - score.max())
+    z = w.sum()
+    order = sorted(np.nonzero(~is_forced)[0].tolist(), key=lambda J: (-score[J], J))
+    cum = [w[is_forced].sum() / z]                  # share after 0, 1, 2, ... content blocks
+    for J in order:
+        cum.append(cum[-1] + w[J] / z)
+    k = 0
+    while k < len(order) and cum[k] < top_p:
+        k += 1
+    near = [cum[k]] + ([cum[k - 1]] if k > 0 else [])
+    ambiguous = any(abs(v - top_p) < TOP_P_BAND for v in near)
+    return k, np.array(order, dtype=np.int64), ambiguous
+
+
 def decode_select(q, kbar, cache_len, *, block_k: int, top_k: int, sink: int, local: int,
-                  scale: float | None = None, kv_of_q=None) -> dict:
+                  scale: float | None = None, kv_of_q=None, top_p: float = 0.0) -> dict:
     """Per (b, g): ascending selected block ids, the scores and the ambiguous blocks
-    (non-forced blocks whose score lies within the band of the selection boundary)."""
+    (non-forced blocks whose score lies within the band of the selection boundary).  With
+    top_p > 0 the number of content blocks is the top-p budget capped at K - |F|; the entry
+    also holds the budget ("budget"), whether it is ambiguous ("budget_ambiguous") and the
+    content blocks in selection order ("order")."""
     B, Hq, D = q.shape
     Hkv = kbar.shape[2]
     c = float(softmax_scale(D, scale))
@@ -125,6 +160,23 @@ def decode_select(q, kbar, cache_len, *, block_k: int, top_k: int, sink: int, lo
             qh = _f64(q[b, heads, :])                               # [heads, D]
             score = (c * (qh @ kb.T)).max(axis=0)                   # [nkb]
             forced = decode_forced(nkb, lb, block_k, sink, local)
+            if top_p > 0:
+                is_f = np.zeros(nkb, dtype=bool)
+                is_f[forced] = True
+                k, order, bamb = top_p_budget(score, is_f, top_p)
+                n_pick = min(k, max(0, top_k - forced.size))
+                sel = np.union1d(forced, order[:n_pick])
+                rest = order
+                if 0 < n_pick < order.size:
+                    bound = score[order[n_pick - 1]]
+                    amb = rest[np.abs(score[rest] - bound) < AMBIGUITY_BAND]
+                else:
+                    amb = np.zeros(0, dtype=np.int64)
+                out[(b, g)] = dict(selected=sel.astype(np.int32), score=score,
+                                   forced=forced.astype(np.int32), ambiguous=amb.astype(np.int32),
+                                   budget=n_pick, budget_uncapped=k,
+                                   budget_ambiguous=bool(bamb) and n_pick == k, order=order)
+                continue
             if nkb <= top_k:
                 sel = np.arange(nkb)
                 amb = np.zeros(0, dtype=np.int64)
