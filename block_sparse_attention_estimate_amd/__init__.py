@@ -268,11 +268,14 @@ def quantize_block_summary(k_summary, *, block_k=64, seq_k=None, stream=None):
 
 
 def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_k=64, sink=32,
-                  local=256, n_splits=0, softmax_scale=0.0, workspace=None, out=None,
+                  local=256, n_splits=0, softmax_scale=0.0, top_p=0.0, workspace=None, out=None,
                   return_selected=True, stream=None):
     """Top-K block-sparse decode (sa_sparse_decode, or sa_sparse_decode_q4 when k_summary is
     the (codes, scales) pair of quantize_block_summary).  q [B, Hq, d]; caches [B, L, Hkv, d].
-    Returns (o [B, Hq, d] bf16, lse [B, Hq] fp32, selected [B, Hkv, top_k] int32 or None)."""
+    top_p in (0, 1] reads each (b, KV head)'s budget from the block-score distribution (at
+    most top_k blocks); 0 selects top_k.
+    Returns (o [B, Hq, d] bf16, lse [B, Hq] fp32, selected [B, Hkv, top_k] int32 or None;
+    unused entries of selected are -1)."""
     lib = _lib.load()
     _check_bf16("v_cache", v_cache, 4)
     o = out if out is not None else torch.empty_like(q)
@@ -280,6 +283,7 @@ def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_
     p = _lib.SaDecodeParams()
     p.block_k, p.top_k_blocks, p.sink_tokens, p.local_tokens = block_k, top_k, sink, local
     p.n_splits, p.softmax_scale = n_splits, float(softmax_scale or 0.0)
+    p.top_p = float(top_p or 0.0)
     need = int(lib.sa_workspace_size(SA_OP_DECODE, ctypes.byref(s), ctypes.byref(p)))
     if need == 0:
         raise SaError(_lib.SA_ERR_PARAM, "sa_workspace_size(decode)")

@@ -45,7 +45,8 @@ class SaLists(ctypes.Structure):
 class SaDecodeParams(ctypes.Structure):
     _fields_ = [("block_k", ctypes.c_int32), ("top_k_blocks", ctypes.c_int32),
                 ("sink_tokens", ctypes.c_int32), ("local_tokens", ctypes.c_int32),
-                ("n_splits", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("n_splits", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("top_p", ctypes.c_float)]
 
 
 _lib = None

@@ -16,7 +16,8 @@
 //   dec_score_q4_mfma  the same from 4-bit summaries on bf16 MFMA (heads as MFMA columns)
 //   dec_select_radix   forced blocks + top (K - |F|) others by (score desc, block asc): radix
 //                      select of the K-th key (11 bits per pass, LDS histograms), ascending
-//                      output list
+//                      output list; or a top-p budget of others by the same passes over
+//                      histograms of fixed-point softmax weight
 //   dec_splitk_mfma    64-key blocks: per (b, g, split), each wave takes whole blocks; the G
 //                      heads are the 32-wide row dimension of S^T = K Q^T and O^T = V^T P^T
 //                      on bf16 MFMA, K in registers, V -> LDS by direct loads; one partial per
@@ -303,30 +304,160 @@ SA_DEV int block_excl_sum(int v, bool reverse, int* wsum) {
   return ex;
 }
 
+// The same over 64-bit values.
+SA_DEV unsigned long long block_excl_sum_u64(unsigned long long v, bool reverse,
+                                             unsigned long long* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned long long incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long t = reverse ? __shfl_down(incl, o) : __shfl_up(incl, o);
+    if (reverse ? lane + o < 64 : lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (reverse ? lane == 0 : lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  unsigned long long ex = incl - v;
+  for (int w = 0; w < 4; ++w)
+    if (reverse ? w > wave : w < wave) ex += wsum[w];
+  return ex;
+}
+
 // Top-K by radix select.  One workgroup (256 threads) per (b, g).  Each candidate block
 // j < nb gets the order-preserving 32-bit key of its score (forced blocks: the maximum key);
 // the K-th largest key is found 11 bits at a time (3 passes at most; it stops early once the
 // bin it falls in is taken whole), then the
 // output takes every key above the threshold T and, among keys equal to T on the resolved
 // bits, the smallest block ids -- the order (key desc, block asc) -- in ascending block order.
+//
+// With top_p > 0 the number of content (non-forced) blocks is the top-p budget: each block
+// weighs w_j = exp(score_j - max score), held in fixed point (2^40 units, so every sum is an
+// exact integer and independent of the order of the additions); the same radix passes, with
+// histograms of weight besides counts, find the key at which the forced weight plus the
+// weight of the content keys above it first reaches top_p * sum w.  Keys equal on all 32 bits
+// have equal scores and weights, so the last r of them follow from one division.  When the
+// budget exceeds K - |forced| the fixed-K selection is made instead.
 __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   constexpr int BINS = 2048;
+  constexpr unsigned int FORCED = 0xFFFFFFFFu;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   extern __shared__ unsigned int skey[];             // [nKB]
   __shared__ unsigned int hist[BINS];
-  __shared__ unsigned int s_dig, s_need;
+  __shared__ unsigned long long hmass[BINS];
+  __shared__ unsigned int s_dig, s_need, s_cab;
   __shared__ int wsum[4];
+  __shared__ unsigned long long wsum64[4];
+  __shared__ unsigned long long s_z, s_f, s_wq;
+  __shared__ double s_needm;
+  __shared__ float s_max[4];
+  __shared__ int s_nf;
   const int lb = min(max(a.cache_len[b], 0), a.L);
   const int nb = (lb + a.bk - 1) / a.bk;
   const float* sc = a.scores + ((int64_t)b * a.Hkv + g) * a.nKB;
+  int nf_local = 0;
   for (int j = tid; j < nb; j += 256) {
     const bool forced = (j * a.bk < a.sink) || ((j + 1) * a.bk - 1 >= lb - a.local);
-    skey[j] = forced ? 0xFFFFFFFFu : float_order_key(sc[j]);
+    skey[j] = forced ? FORCED : float_order_key(sc[j]);
+    nf_local += forced;
   }
   const int kk = min(a.top_k, nb);
   unsigned int T = 0, mask = 0;                      // threshold on the resolved bits
   unsigned int need = (unsigned int)kk;
-  if (kk < nb) {
+  bool all = kk >= nb;                               // every block is selected
+  int total = kk;                                    // blocks selected
+  bool done = false;
+
+  if (a.top_p > 0.f) {
+    // max score, then the fixed-point weights and their sums (all, forced)
+    float mloc = NEG_INF;
+    for (int j = tid; j < nb; j += 256) mloc = fmaxf(mloc, sc[j]);
+    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+    if (tid == 0) { s_z = 0; s_f = 0; s_nf = 0; }
+    if ((tid & 63) == 0) s_max[tid >> 6] = mloc;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    auto wfix = [&](int j) -> unsigned long long {
+      return (unsigned long long)(expf(sc[j] - M) * 0x1p40f);
+    };
+    unsigned long long zl = 0, fl = 0;
+    for (int j = tid; j < nb; j += 256) {
+      const unsigned long long w = wfix(j);
+      zl += w;
+      if (skey[j] == FORCED) fl += w;
+    }
+    atomicAdd(&s_z, zl);
+    atomicAdd(&s_f, fl);
+    atomicAdd(&s_nf, nf_local);
+    __syncthreads();
+    const int nF = s_nf;
+    double needm = (double)a.top_p * (double)s_z - (double)s_f;
+    int n_content = 0;
+    unsigned int Tp = FORCED, maskp = FORCED, needp = (unsigned int)nF;
+    if (needm > 0.0) {
+      const int shifts[3] = {21, 10, 0};
+      unsigned int cab = 0;                          // content keys above the resolved prefix
+      Tp = 0;
+      maskp = 0;
+      for (int p = 0; p < 3; ++p) {
+        const int shift = shifts[p];
+        const unsigned int dmask = p == 2 ? 1023u : 2047u;
+        for (int e = tid; e < BINS; e += 256) {
+          hist[e] = 0;
+          hmass[e] = 0;
+        }
+        __syncthreads();
+        for (int j = tid; j < nb; j += 256) {
+          const unsigned int k = skey[j];
+          if (k != FORCED && (k & maskp) == Tp) {
+            const unsigned int dg = (k >> shift) & dmask;
+            atomicAdd(&hist[dg], 1u);
+            atomicAdd(&hmass[dg], wfix(j));
+          }
+        }
+        __syncthreads();
+        unsigned int c[8], totc = 0;
+        unsigned long long m[8], totm = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          c[e] = hist[8 * tid + e];
+          m[e] = hmass[8 * tid + e];
+          totc += c[e];
+          totm += m[e];
+        }
+        unsigned int runc = (unsigned int)block_excl_sum((int)totc, true, wsum);
+        unsigned long long runm = block_excl_sum_u64(totm, true, wsum64);
+#pragma unroll
+        for (int e = 7; e >= 0; --e) {
+          if ((double)runm < needm && (double)(runm + m[e]) >= needm) {   // crossing digit
+            s_dig = (unsigned int)(8 * tid + e);
+            s_needm = needm - (double)runm;
+            s_cab = runc;
+            s_wq = m[e] / c[e];                      // one weight per key on the last pass
+          }
+          runm += m[e];
+          runc += c[e];
+        }
+        __syncthreads();
+        needm = s_needm;
+        cab += s_cab;
+        Tp |= s_dig << shift;
+        maskp |= dmask << shift;
+      }
+      // every content key equal to Tp weighs s_wq: the first r of them complete the share
+      const unsigned int r = (unsigned int)max(1.0, ceil(needm / (double)s_wq));
+      n_content = (int)(cab + r);
+      needp = r;
+    }
+    if (n_content <= max(0, a.top_k - nF)) {
+      T = Tp;
+      mask = maskp;
+      need = needp;
+      all = false;
+      total = nF + n_content;
+      done = true;
+    }
+  }
+
+  if (!done && kk < nb) {
     const int shifts[3] = {21, 10, 0};
     for (int p = 0; p < 3; ++p) {
       const int shift = shifts[p];
@@ -368,7 +499,7 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   const int per = (nb + 255) / 256;
   const int j0 = tid * per;
   int eq = 0;
-  if (kk < nb)
+  if (!all)
     for (int e = 0; e < per && j0 + e < nb; ++e) eq += (skey[j0 + e] & mask) == T;
   int eq_before = block_excl_sum(eq, false, wsum);
   unsigned int sel_bits = 0;                           // bit e: block j0 + e selected
@@ -376,7 +507,7 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   for (int e = 0; e < per && e < MAXPER && j0 + e < nb; ++e) {
     const unsigned int k = skey[j0 + e] & mask;
     bool take;
-    if (kk >= nb || k > T) {
+    if (all || k > T) {
       take = true;
     } else if (k == T) {
       take = (unsigned int)eq_before < need;
@@ -393,7 +524,8 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   int32_t* out = a.selected + ((int64_t)b * a.Hkv + g) * a.top_k;
   for (int e = 0; e < per && e < MAXPER; ++e)
     if (sel_bits & (1u << e)) out[pos++] = j0 + e;
-  for (int p = kk + tid; p < a.top_k; p += 256) out[p] = -1;
+  for (int p = total + tid; p < a.top_k; p += 256) out[p] = -1;
+  if (tid == 0) a.sel_count[b * a.Hkv + g] = total;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -409,7 +541,7 @@ __global__ __launch_bounds__(256) void dec_splitk(DecArgs a) {
   const int sub = tid & 15, grp = tid >> 4;
   const int lb = min(max(a.cache_len[b], 0), a.L);
   const int nb = (lb + a.bk - 1) / a.bk;
-  const int nsel = min(a.top_k, nb);
+  const int nsel = a.sel_count[b * a.Hkv + g];
   const int bps = (nsel + a.n_splits - 1) / a.n_splits;
   const int blk0 = s * bps, blk1 = min(nsel, blk0 + bps);
   const int nkeys = max(0, blk1 - blk0) * a.bk;
@@ -578,7 +710,7 @@ __global__ __launch_bounds__(256, 1) void dec_splitk_mfma(DecArgs a) {
   unsigned char* reg1 = vb1 + wave * VREG;
   const int lb = min(max(a.cache_len[b], 0), a.L);
   const int nb = (lb + 63) / 64;
-  const int nsel = min(a.top_k, nb);
+  const int nsel = ((const __attribute__((address_space(4))) int32_t*)a.sel_count)[b * a.Hkv + g];
   const int bps = (nsel + a.n_splits - 1) / a.n_splits;
   const int blk0 = s * bps, blk1 = min(nsel, blk0 + bps);
   const int nw = max(0, (blk1 - blk0 - wave + 3) / 4);   // this wave's blocks

@@ -113,7 +113,7 @@ CalLayout cal_layout(const sa_shape* s, const sa_sparse_params* p) {
 }
 
 struct DecLayout {
-  size_t scores, selected, partial, total;
+  size_t scores, selected, counts, partial, total;
 };
 
 int decode_splits(const sa_shape* s, const sa_decode_params* p) {
@@ -133,6 +133,7 @@ DecLayout dec_layout(const sa_shape* s, const sa_decode_params* p) {
   size_t off = 0;
   L.scores = off;   off = align_up(off + (size_t)s->batch * s->n_kv_heads * nKB * sizeof(float));
   L.selected = off; off = align_up(off + (size_t)s->batch * s->n_kv_heads * p->top_k_blocks * sizeof(int32_t));
+  L.counts = off;   off = align_up(off + (size_t)s->batch * s->n_kv_heads * sizeof(int32_t));
   L.partial = off;  off = align_up(off + (size_t)s->batch * s->n_q_heads * ns * (s->head_dim + 2) * sizeof(float));
   L.total = off;
   return L;
@@ -147,6 +148,7 @@ sa_status check_decode(const sa_shape* s, const sa_decode_params* p) {
       p->n_splits < 0)
     return SA_ERR_PARAM;
   if (isnan(p->softmax_scale) || isinf(p->softmax_scale)) return SA_ERR_PARAM;
+  if (!(p->top_p >= 0.f && p->top_p <= 1.f)) return SA_ERR_PARAM;
   if (ceil_div(s->seq_k, p->block_k) > 8192) return SA_ERR_UNSUPPORTED;
   if (!strides_ok(s->q_stride) || !strides_ok(s->k_stride) || !strides_ok(s->v_stride) ||
       !strides_ok(s->o_stride))
@@ -331,6 +333,8 @@ static sa_status decode_impl(const sa_shape* shape, const sa_decode_params* para
   a.scores = (float*)(base + L.scores);
   a.selected = selected ? selected : (int32_t*)(base + L.selected);
   a.partial = (float*)(base + L.partial);
+  a.sel_count = (int32_t*)(base + L.counts);
+  a.top_p = params->top_p;
   a.top_k = params->top_k_blocks;
   a.sink = params->sink_tokens;
   a.local = params->local_tokens;

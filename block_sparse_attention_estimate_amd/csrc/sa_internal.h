@@ -55,11 +55,13 @@ struct DecArgs {
   uint16_t* o;
   float* lse;
   int32_t* selected;
+  int32_t* sel_count;      // [B, Hkv] blocks selected per (b, g)
   float* scores;           // [B, Hkv, nKBmax]
   float* partial;          // [B, Hq, n_splits, D + 2]
   int64_t qs0, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os2;
   int B, Hq, Hkv, G, D, L, bk, nKB, top_k, sink, local, n_splits;
   float c;
+  float top_p;             // 0: fixed K; (0, 1]: top-p budget capped at K
 };
 
 hipError_t launch_estimate(const EstArgs& a, int granularity, hipStream_t s);

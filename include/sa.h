@@ -98,10 +98,16 @@ typedef struct {
 
 /* Decode parameters: key-block size of the summaries and of the selection, number of
  * selected blocks K (forced blocks count toward K), sink and local (recency) sizes in
- * tokens, number of split-K partitions (0 = library choice), softmax scale as above. */
+ * tokens, number of split-K partitions (0 = library choice), softmax scale as above.
+ * top_p (SpotAttention abstract and Figure 2: a top-p rule reads each query's budget from the
+ * selector's distribution over blocks): 0 selects exactly min(K, blocks) blocks; in (0, 1]
+ * the forced blocks plus the fewest others, in (score desc, block asc) order, whose share of
+ * pi_J = softmax over the cache's blocks of score_J brings the cumulative share to at least
+ * top_p -- at most K blocks in all.  Other values: SA_ERR_PARAM. */
 typedef struct {
   int32_t block_k, top_k_blocks, sink_tokens, local_tokens, n_splits;
   float softmax_scale;
+  float top_p;
 } sa_decode_params;
 
 /* Workspace bytes an operation needs (op = SA_OP_ESTIMATE or SA_OP_CALIBRATE with
@@ -156,7 +162,8 @@ sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k,
  * cache_len-1, seeing every cached token) over the selected blocks and an LSE merge.
  * q: device bf16 [B, Hq, d] (q_stride[0] = batch stride, q_stride[2] = head stride);
  * o: device bf16 [B, Hq, d] likewise (o_stride); lse: nullable device fp32 [B, Hq];
- * selected: nullable device int32 [B, Hkv, top_k_blocks], ascending, padded with -1.
+ * selected: nullable device int32 [B, Hkv, top_k_blocks], ascending, padded with -1 (with
+ * top_p the number of entries before the padding is each (b, g)'s budget).
  * ws: at least sa_workspace_size(SA_OP_DECODE, ...) bytes. */
 sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params,
                            const void* q, const void* k_cache, const void* v_cache,

@@ -94,3 +94,33 @@ def oracle_estimate_for(x, theta, rows=None, **over):
     if rows is None:
         return oracle.estimate_all(x.q, x.k, theta, **kw)
     return oracle.estimate_rows(x.q, x.k, theta, rows=rows, **kw)
+
+
+def check_topp_selection(sel_np, ref, band=1e-3):
+    """GPU selection under a top-p budget against the oracle's: each (b, g) selects its forced
+    blocks plus k content blocks, k equal to the oracle's budget (or one off where the oracle
+    flags that budget ambiguous), and those are the first k of the oracle's (score desc, block
+    asc) order except blocks whose score lies within `band` of the k-th.  Returns
+    ({(b, g): selected}, number of budgets one off, number of exchanged blocks)."""
+    used, off, flips = {}, 0, 0
+    for (b, g), r in ref.items():
+        row = sel_np[b, g]
+        n = int((row >= 0).sum())
+        got = row[:n]
+        assert (row[n:] == -1).all() and np.all(np.diff(got) > 0), (b, g)
+        k_gpu = n - r["forced"].size
+        if k_gpu != r["budget"]:
+            assert r["budget_ambiguous"] and abs(k_gpu - r["budget"]) <= 1, \
+                ((b, g), k_gpu, r["budget"])
+            off += 1
+        order, score = r["order"], r["score"]
+        expect = set(r["forced"].tolist()) | set(order[:k_gpu].tolist())
+        diff = set(got.tolist()) ^ expect
+        if diff:
+            assert k_gpu > 0, ((b, g), sorted(diff))
+            bound = score[order[k_gpu - 1]]
+            amb = {int(J) for J in order if abs(score[J] - bound) < band}
+            assert diff <= amb, ((b, g), sorted(diff))
+            flips += len(diff)
+        used[(b, g)] = got
+    return used, off, flips

@@ -121,6 +121,10 @@ def test_validation_codes(lib):
     dp.top_k_blocks = 0
     assert lib.sa_sparse_decode(*args, FAKE, dneed, None) == _lib.SA_ERR_PARAM
     dp.top_k_blocks = 8
+    for bad in (float("nan"), -0.1, 1.5):
+        dp.top_p = bad
+        assert lib.sa_sparse_decode(*args, FAKE, dneed, None) == _lib.SA_ERR_PARAM
+    dp.top_p = 0.0
     ds.seq_q = 2
     assert lib.sa_sparse_decode(*args, FAKE, dneed, None) == _lib.SA_ERR_SHAPE
     ds.seq_q = 1

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import MAX_ABS, MEAN_ABS, compare_lists, log, to_dev
+from helpers import MAX_ABS, MEAN_ABS, check_topp_selection, compare_lists, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -96,8 +96,10 @@ def test_stripe_64k_sampled(dev):
     _prefill_parity(dev, "stripe_64k", n_rows=24, n_attn=10)
 
 
-@pytest.mark.parametrize("summary", ["bf16", "q4"])
+@pytest.mark.parametrize("summary", ["bf16", "q4", "bf16-topp"])
 def test_decode_b16_128k(dev, summary):
+    """bf16-topp: top_p = 0.5 with a cap of 256 blocks, which the budgets of this workload
+    (about 80 to 200 blocks) stay under."""
     import torch
     import block_sparse_attention_estimate_amd as sa
     log(f"generating decode_b16_128k ({summary} summaries)")
@@ -106,9 +108,10 @@ def test_decode_b16_128k(dev, summary):
     q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
     cl = torch.from_numpy(x.cache_len).to(dev)
     kbar = sa.build_block_summary(kc, cl, block_k=x.block_k)
-    summ = kbar if summary == "bf16" else sa.quantize_block_summary(kbar, block_k=x.block_k)
-    o, lse, sel = sa.sparse_decode(q, kc, vc, summ, cl, block_k=x.block_k, top_k=x.top_k,
-                                   sink=x.sink, local=x.local)
+    summ = sa.quantize_block_summary(kbar, block_k=x.block_k) if summary == "q4" else kbar
+    top_p, top_k = (0.5, 256) if summary == "bf16-topp" else (0.0, x.top_k)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, summ, cl, block_k=x.block_k, top_k=top_k,
+                                   sink=x.sink, local=x.local, top_p=top_p)
     torch.cuda.synchronize()
     log("oracle block summaries")
     kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, x.block_k)
@@ -120,9 +123,21 @@ def test_decode_b16_128k(dev, summary):
         np.testing.assert_array_equal(summ[0].cpu().numpy(), oracle.pack_q4(c_ref))
         np.testing.assert_array_equal(summ[1].view(torch.int16).cpu().numpy().view(np.uint16), s_ref)
         score_src = oracle.dequantize_summary_q4(c_ref, s_ref)
-    ref = oracle.decode_select(x.q, score_src, x.cache_len, block_k=x.block_k, top_k=x.top_k,
-                               sink=x.sink, local=x.local)
+    ref = oracle.decode_select(x.q, score_src, x.cache_len, block_k=x.block_k, top_k=top_k,
+                               sink=x.sink, local=x.local, top_p=top_p)
     s = sel.cpu().numpy()
+    if top_p > 0:
+        used, off, flips = check_topp_selection(s, ref)
+        budgets = [r["budget"] for r in ref.values()]
+        log(f"  top-p selection ok: budgets {min(budgets)}..{max(budgets)} one-off={off} flips={flips}")
+        assert max(budgets) < top_k - 5
+        O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used,
+                                         block_k=x.block_k)
+        err = np.abs(o.float().cpu().numpy() - O)
+        log(f"  decode attention: max|dO|={err.max():.2e} mean={err.mean():.2e}")
+        assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
+        assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
+        return
     flips = 0
     same = {}
     for (b, g), r in ref.items():

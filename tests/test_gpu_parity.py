@@ -10,8 +10,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import (compare_lists, compare_outputs, log, lists_from_ref, oracle_estimate_for,
-                     to_dev, upload_lists)
+from helpers import (check_topp_selection, compare_lists, compare_outputs, log, lists_from_ref,
+                     oracle_estimate_for, to_dev, upload_lists)
 
 pytestmark = pytest.mark.gpu
 
@@ -215,3 +215,42 @@ def test_decode_q4_reduced(dev, batch, seq, hq, hkv, d, top_k):
     assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
     assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
     log(f"  decode q4 ok: flips={flips} max|dO|={err.max():.2e}")
+
+
+@pytest.mark.parametrize("batch,seq,hq,hkv,d,top_k,bk,top_p,summary",
+                         [(3, 5000, 8, 2, 128, 79, 64, 0.5, "bf16"),
+                          (2, 3000, 4, 1, 64, 47, 64, 0.9, "bf16"),
+                          (2, 3000, 8, 2, 128, 12, 64, 0.9, "bf16"),    # the cap of K binds
+                          (2, 3000, 8, 2, 128, 94, 32, 0.7, "bf16"),
+                          (2, 5000, 8, 2, 128, 79, 64, 0.02, "bf16"),   # forced share suffices
+                          (3, 5000, 8, 2, 128, 79, 64, 0.8, "q4")])
+def test_decode_topp_reduced(dev, batch, seq, hq, hkv, d, top_k, bk, top_p, summary):
+    """Top-p budget: per (b, g) the forced blocks plus the oracle's budget of content blocks
+    (one off only where the oracle's cumulative share lies within its band of top_p), in the
+    oracle's score order outside the score band; attention over the GPU's selection."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_decode(batch=batch, seq=seq, hq=hq, hkv=hkv, head_dim=d, top_k=top_k)
+    if batch >= 2:
+        x.cache_len[1] = seq - 937
+    log(f"decode top-p={top_p} {summary} B={batch} L={seq} Hq={hq} Hkv={hkv} d={d} K={top_k} bk={bk}")
+    q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=bk)
+    summ = kbar if summary == "bf16" else sa.quantize_block_summary(kbar, block_k=bk)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, summ, cl, block_k=bk, top_k=top_k, sink=32,
+                                   local=256, top_p=top_p)
+    torch.cuda.synchronize()
+    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, bk)
+    if summary == "q4":
+        kbar_ref = oracle.dequantize_summary_q4(*oracle.quantize_summary_q4(kbar_ref))
+    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=bk, top_k=top_k, sink=32,
+                               local=256, top_p=top_p)
+    used, off, flips = check_topp_selection(sel.cpu().numpy(), ref)
+    budgets = [r["budget"] for r in ref.values()]
+    O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used, block_k=bk)
+    err = np.abs(o.float().cpu().numpy() - O)
+    assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
+    assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
+    log(f"  top-p ok: budgets {min(budgets)}..{max(budgets)} one-off={off} flips={flips} "
+        f"max|dO|={err.max():.2e}")
