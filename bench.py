@@ -268,8 +268,10 @@ def bench_decode(args, dev):
         kbar = sa.quantize_block_summary(kbar, block_k=x.block_k)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-    kw = dict(block_k=x.block_k, top_k=x.top_k, sink=x.sink, local=x.local)
+    top_k = args.top_k or x.top_k
+    kw = dict(block_k=x.block_k, top_k=top_k, sink=x.sink, local=x.local, top_p=args.top_p)
     o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
+    n_sel = int((sel >= 0).sum().item())                 # blocks selected over all (b, g)
     for _ in range(args.warmup):
         sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
     torch.cuda.synchronize()
@@ -281,7 +283,7 @@ def bench_decode(args, dev):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / args.steps
     nkb = -(-L // x.block_k)
-    sel_bytes = B * Hkv * x.top_k * x.block_k * D * 2 * 2
+    sel_bytes = n_sel * x.block_k * D * 2 * 2
     sum_bytes = B * Hkv * nkb * (D * 2 if args.summary == "bf16" else D // 2 + D // 32 * 2)
     gbs = (sel_bytes + sum_bytes) / (us * 1e-6) / 1e9
     return {"metric": "sparse decode step time and achieved HBM GB/s",
@@ -290,10 +292,13 @@ def bench_decode(args, dev):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
             "config": {"workload": f"{args.workload}: batch {B}, {Hq}/{Hkv} heads, d {D}, "
-                                   f"cache {L}, top-{x.top_k} blocks of {x.block_k}, "
+                                   f"cache {L}, " + (f"top-{top_k} blocks of {x.block_k}, "
+                                   if args.top_p == 0 else f"top-p {args.top_p} budget (at most "
+                                   f"{top_k} blocks of {x.block_k}), ") +
                                    f"{args.summary} block summaries",
                        "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
             "us_per_step": round(us, 2),
+            "mean_blocks_selected": round(n_sel / (B * Hkv), 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_from_profile(f"dec_splitk_{args.workload}_traffic", DEC_SRC),
@@ -351,6 +356,10 @@ def main():
     ap.add_argument("--kernel", default="attn_block")
     ap.add_argument("--summary", choices=["bf16", "q4"], default="bf16",
                     help="decode: block summaries in bf16 or 4-bit codes + bf16 scales")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="decode: per-(b, KV head) budget from the block-score distribution")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="decode: block cap (default: the workload's K)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time the per-head theta calibration on the prefill workload instead")
     ap.add_argument("--err-bound", type=float, default=0.4)
