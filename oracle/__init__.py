@@ -20,6 +20,8 @@ What it computes, in the pages' order and notation:
   over the selected blocks for one query token per sequence.
 * ``calibrate`` -- SALE's per-head threshold calibration: tau halved from 0.008 until the
   L1 output error against full attention meets a bound (theta = -ln tau).
+* ``estimate_sale`` -- SALE's element-wise low-bit estimate with the relative attention
+  score (the row's log-sum-exp over its sink-local area as the reference).
 
 Parity pins: see ``tests/test_oracle_*.py``.  Every function is pinned by brute force,
 closed forms, invariants or an independent library routine; none is "parity unpinned".
@@ -41,3 +43,4 @@ from .decode import (block_summary, decode_select, decode_attention, quantize_su
                      dequantize_summary_q4, pack_q4)
 from .diagnostics import pruned_mass_fraction, sparsity_from_kept, sale_log_margin  # noqa: F401
 from .calibrate import full_lists, head_l1_error, calibrate_theta  # noqa: F401
+from .estimate_sale import estimate_rows_sale, estimate_all_sale, relative_scores  # noqa: F401
