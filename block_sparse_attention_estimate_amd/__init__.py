@@ -72,10 +72,17 @@ def _prefill_shape(q, k, v=None, o=None) -> _lib.SaShape:
     return s
 
 
-def _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale, n_q_heads):
+_ESTIMATORS = {"pooled": _lib.SA_EST_POOLED, "relative": _lib.SA_EST_RELATIVE}
+
+
+def _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale, n_q_heads,
+                   estimator="pooled"):
     p = _lib.SaSparseParams()
     p.block_q, p.block_k, p.sink_tokens, p.local_tokens = block_q, block_k, sink, local
     p.granularity = _gran(granularity)
+    if estimator not in _ESTIMATORS:
+        raise ValueError(f"estimator must be one of {sorted(_ESTIMATORS)}")
+    p.estimator = _ESTIMATORS[estimator]
     p.softmax_scale = float(softmax_scale or 0.0)
     arr = None
     if theta is not None:
@@ -145,13 +152,15 @@ def alloc_lists(q, k, *, block_q, block_k=64, granularity="block", stride=None,
 
 def estimate_mask(q, k, theta, *, block_q=128, block_k=64, sink=32, local=256,
                   granularity="block", softmax_scale=0.0, stride=None, margins=False,
-                  workspace=None, out: Lists | None = None, stream=None) -> Lists:
-    """Anchor-based estimation pass (sa_estimate_mask).  q [B, N, Hq, d], k [B, N, Hkv, d]
-    bf16 CUDA tensors; theta scalar or [Hq] in logit units."""
+                  estimator="pooled", workspace=None, out: Lists | None = None,
+                  stream=None) -> Lists:
+    """Estimation pass (sa_estimate_mask).  q [B, N, Hq, d], k [B, N, Hkv, d] bf16 CUDA
+    tensors; theta scalar or [Hq] in logit units; estimator "pooled" (anchor vs pooled
+    query) or "relative" (element-wise estimate against the row's sink-local log-sum-exp)."""
     lib = _lib.load()
     s = _prefill_shape(q, k)
     p, keep = _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale,
-                             q.shape[2])
+                             q.shape[2], estimator)
     lists = out if out is not None else alloc_lists(q, k, block_q=block_q, block_k=block_k,
                                                     granularity=granularity, stride=stride,
                                                     margins=margins)
@@ -189,8 +198,8 @@ def sparse_prefill(q, k, v, lists: Lists, *, block_q=128, block_k=64, sink=32, l
 
 
 def calibrate_theta(q, k, v, *, tau0=0.008, err_bound=0.4, max_halvings=16, block_q=128,
-                    block_k=64, sink=32, local=256, softmax_scale=0.0, workspace=None,
-                    stream=None):
+                    block_k=64, sink=32, local=256, softmax_scale=0.0, estimator="pooled",
+                    workspace=None, stream=None):
     """Per-head theta calibration (sa_calibrate_theta; block granularity).  Returns
     (theta [Hq] float32, err [Hq] float32, halvings [Hq] int32) as numpy arrays: theta_h =
     -ln(tau0) + halvings_h * ln 2, err_h = sum |O - O~| over the head's rows and dims / rows.
@@ -200,7 +209,7 @@ def calibrate_theta(q, k, v, *, tau0=0.008, err_bound=0.4, max_halvings=16, bloc
     _check_bf16("v", v, 4)
     s = _prefill_shape(q, k, v, q)
     p, keep = _sparse_params(block_q, block_k, sink, local, "block", 0.0, softmax_scale,
-                             q.shape[2])
+                             q.shape[2], estimator)
     need = int(lib.sa_workspace_size(SA_OP_CALIBRATE, ctypes.byref(s), ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libsa.so")
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_PARAM, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY, \
     SA_ERR_WORKSPACE, SA_ERR_DEVICE = range(8)
 SA_BLOCK, SA_STRIPE = 0, 1
+SA_EST_POOLED, SA_EST_RELATIVE = 0, 1
 SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE, SA_OP_CALIBRATE = 0, 1, 2, 3
 SA_MAX_Q_HEADS = 128
 
@@ -34,7 +35,7 @@ class SaSparseParams(ctypes.Structure):
     _fields_ = [("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("sink_tokens", ctypes.c_int32), ("local_tokens", ctypes.c_int32),
                 ("granularity", ctypes.c_int32), ("theta", ctypes.POINTER(ctypes.c_float)),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("estimator", ctypes.c_int32)]
 
 
 class SaLists(ctypes.Structure):

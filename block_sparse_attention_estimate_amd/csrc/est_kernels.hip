@@ -17,6 +17,9 @@
 //                     max over the group's heads -> one keep bit per (query block, key block)
 //   est_score_stripe  same per key column (no block max)
 //   est_compact       bits | forced, causal -> ascending index lists + counts
+// With the relative-score estimator (SALE) est_anchor_pool and est_score_block are replaced
+// by est_quant_q_rows (int8 query rows) and est_score_rel (element-wise estimate, LSE of the
+// sink-local keys, block max of S~ - LSE + theta, max over the group).
 //
 // Floating-point steps that decide an integer (int8 codes, keep bits) use explicit
 // round-to-nearest operations (__fmul_rn, __fdiv_rn, rintf) in the order the oracle uses.
@@ -685,6 +688,275 @@ __global__ __launch_bounds__(256) void est_score_stripe(EstArgs a, int n_rt, int
 }
 
 // ---------------------------------------------------------------------------------------
+// Relative-score estimate (SALE, "What carries the argument"; the log form of the test as
+// corrected in referee major comment 1).
+//
+// est_quant_q_rows: int8 query rows, the rule of the key tiles applied per (b, h, row):
+// a = max |q_r|, scale = a / 127, code = rint(q * (127 / a)).  16 lanes per row.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void est_quant_q_rows(EstArgs a) {
+  constexpr int EPL = D / 16;                        // elements per lane (8 or 4)
+  const int tid = threadIdx.x, sub = tid & 15;
+  const int64_t nrows = (int64_t)a.B * a.N * a.Hq;
+  const int64_t R = (int64_t)blockIdx.x * 16 + (tid >> 4);   // rows in (b, token, head) order
+  const bool valid = R < nrows;
+  const int64_t Rc = valid ? R : nrows - 1;
+  const int h = (int)(Rc % a.Hq);
+  const int r = (int)((Rc / a.Hq) % a.N);
+  const int b = (int)(Rc / ((int64_t)a.Hq * a.N));
+  const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r * a.qs1 + h * a.qs2 + sub * EPL;
+  float v[EPL];
+  if (EPL == 8) {
+    const u16x8 u = *(const u16x8*)qp;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = bf16_bits_to_float(u[e]);
+  } else {
+    const u32x2 u = *(const u32x2*)qp;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      v[e] = bf16_bits_to_float((unsigned short)(((e < 2 ? u.x : u.y) >> (16 * (e & 1))) & 0xFFFFu));
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));   // the 16 lanes
+  float inv = 0.f, scale = 1.f;
+  if (amax > 0.f) {
+    inv = __fdiv_rn(127.0f, amax);
+    scale = __fdiv_rn(amax, 127.0f);
+  }
+  unsigned int w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    float x = rintf(__fmul_rn(v[e], inv));
+    x = fminf(fmaxf(x, -127.f), 127.f);
+    w[e >> 2] |= ((unsigned int)((int)x & 0xFF)) << (8 * (e & 3));
+  }
+  if (!valid) return;
+  const int64_t orow = ((int64_t)b * a.Hq + h) * a.N + r;
+  int8_t* dst = a.qr + orow * D + sub * EPL;
+  if (EPL == 8)
+    *(u32x2*)dst = (u32x2){w[0], w[1]};
+  else
+    *(unsigned int*)dst = w[0];
+  if (sub == 0) a.sr[orow] = scale;
+}
+
+// est_score_rel: one workgroup per (b, g, query block), longest blocks first.  The block's
+// rows of every head of the group are cut into units of 64 rows of one head; each wave takes
+// two units at a time, keeps their int8 rows as the B operand of D^T = K_q Q_q^T (32x32x32
+// int8 MFMA, exact int32), and
+//  1. over the row's sink and local keys (their tiles only) forms LSE_r of the estimated
+//     logits S~ = fp32(D) * fp32(fp32(s_q s_K) c) -- a lane owns one row and 16 of the keys
+//     of each 32-key subtile, the other 16 sit in lane ^ 32;
+//  2. over every causal key tile J takes the row's max of D (S~ is increasing in D for a
+//     row and tile, so the max of S~ is S~ of the max), S~ - LSE_r + theta_h, the max over
+//     the wave's rows and units, and folds it into the block's margin for J with an LDS
+//     atomic max on order-preserving keys.
+// The margins of all units (heads and row ranges) then give one keep bit per key block.
+template <int D>
+__global__ __launch_bounds__(256) void est_score_rel(EstArgs a) {
+  constexpr int KS = D / 32;
+  extern __shared__ unsigned int mkey[];             // [nKB] best margin key per key block
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
+  const int BG = a.B * a.Hkv;
+  const int bg = blockIdx.x % BG;
+  const int I = a.nQB - 1 - blockIdx.x / BG;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int r0 = I * a.bq;
+  const int e = min(a.N, r0 + a.bq) - 1;
+  const int ncand = e / 64 + 1;
+  for (int j = tid; j < ncand; j += 256) mkey[j] = 0u;
+  __syncthreads();
+  const int SUBS = a.bq / 64;
+  const int U = a.G * SUBS;
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
+  const float* skb = a.sk + (int64_t)bg * a.nKB;
+  const int sink_last = a.sink > 0 ? (min(a.sink, a.N) - 1) / 64 : -1;
+
+  auto load_k = [&](int J, i32x4 (*kf)[KS]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[mt][ks] = *(const i32x4*)(kbase + (int64_t)(J * 64 + mt * 32 + l32) * D + ks * 32);
+  };
+
+  for (int u0 = 0; u0 < U; u0 += 8) {
+    const int ua = u0 + 2 * wave;
+    const int nu = max(0, min(2, U - ua));
+    if (nu == 0) continue;
+    i32x4 qf[2][2][KS];
+    float sqv[2][2], lse[2][2], thv[2];
+    int rowv[2][2], rmin[2], rmax[2];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int u = min(ua + uu, U - 1);
+      const int hg = u / SUBS, sb = u % SUBS;
+      const int h = g * a.G + hg;
+      thv[uu] = a.theta[h];
+      rmin[uu] = r0 + sb * 64;
+      rmax[uu] = min(rmin[uu] + 63, a.N - 1);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = rmin[uu] + nt * 32 + l32;
+        rowv[uu][nt] = row;
+        const int64_t orow = ((int64_t)b * a.Hq + h) * a.N + min(row, a.N - 1);
+        const int8_t* qp = a.qr + orow * D + half * 16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[uu][nt][ks] = *(const i32x4*)(qp + ks * 32);
+        sqv[uu][nt] = a.sr[orow];
+      }
+    }
+    const bool two = nu == 2;
+    // D^T of one unit against the key tile in kf
+    auto dots = [&](int uu, i32x4 (*kf)[KS], i32x16 (*acc)[2]) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (i32x16){};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_i8(kf[mt][ks], qf[uu][nt][ks], acc[mt][nt]);
+    };
+
+    // 1. LSE over each row's sink and local keys, from the tiles that hold them
+    float mr[2][2], sr_[2][2];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        mr[uu][nt] = NEG_INF;
+        sr_[uu][nt] = 0.f;
+      }
+    const int wlo = max(0, min(rmin[0], two ? rmin[1] : rmin[0]) - a.local + 1) / 64;
+    const int whi = max(rmax[0], two ? rmax[1] : rmax[0]) / 64;
+    for (int J = 0; J <= whi; ++J) {
+      if (J > sink_last && J < wlo) J = wlo;           // skip the tiles between the areas
+      i32x4 kf[2][KS];
+      load_k(J, kf);
+      const float skv = skb[J];
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        if (uu == 1 && !two) break;
+        if (J * 64 > rmax[uu]) continue;
+        i32x16 acc[2][2];
+        dots(uu, kf, acc);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int row = rowv[uu][nt];
+          const float mult = __fmul_rn(__fmul_rn(sqv[uu][nt], skv), a.c);
+          float x[32];
+          float tm = NEG_INF;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+              const bool in = key <= row && key < a.N && (key < a.sink || key >= row - a.local + 1);
+              const float v = in ? __fmul_rn((float)acc[mt][nt][r], mult) : NEG_INF;
+              x[mt * 16 + r] = v;
+              tm = fmaxf(tm, v);
+            }
+          if (tm > NEG_INF) {
+            const float mn = fmaxf(mr[uu][nt], tm);
+            float sacc = sr_[uu][nt] * __expf(mr[uu][nt] - mn);
+#pragma unroll
+            for (int t = 0; t < 32; ++t) sacc += __expf(x[t] - mn);
+            mr[uu][nt] = mn;
+            sr_[uu][nt] = sacc;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float mo = swap_halves(mr[uu][nt]), so = swap_halves(sr_[uu][nt]);
+        const float mt_ = fmaxf(mr[uu][nt], mo);
+        float st = 0.f;
+        if (mr[uu][nt] > NEG_INF) st += sr_[uu][nt] * __expf(mr[uu][nt] - mt_);
+        if (mo > NEG_INF) st += so * __expf(mo - mt_);
+        // rows past the end of the sequence take no part
+        lse[uu][nt] = (rowv[uu][nt] < a.N && mt_ > NEG_INF) ? mt_ + logf(st) : __builtin_huge_valf();
+      }
+
+    // 2. every causal key tile: best (S~ - LSE + theta) over the wave's rows and units
+    const int Jend = max(rmax[0], two ? rmax[1] : rmax[0]) / 64 + 1;
+    i32x4 kf[2][KS], kn[2][KS];
+    load_k(0, kf);
+    for (int J = 0; J < Jend; ++J) {
+      if (J + 1 < Jend) load_k(J + 1, kn);
+      const float skv = skb[J];
+      float best = NEG_INF;
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        if (uu == 1 && !two) break;
+        if (J * 64 > rmax[uu]) continue;
+        i32x16 acc[2][2];
+        dots(uu, kf, acc);
+        const bool need_mask = J * 64 + 63 > rmin[uu] || J * 64 + 63 >= a.N;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int row = rowv[uu][nt];
+          int m = INT32_MIN;
+          if (!need_mask) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) m = max(m, acc[mt][nt][r]);
+          } else {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+                if (key <= row && key < a.N) m = max(m, acc[mt][nt][r]);
+              }
+          }
+          m = max(m, swap_halves_i(m));
+          if (m != INT32_MIN && row < a.N) {
+            const float mult = __fmul_rn(__fmul_rn(sqv[uu][nt], skv), a.c);
+            const float rel = __fmul_rn((float)m, mult) - lse[uu][nt];
+            best = fmaxf(best, rel + thv[uu]);
+          }
+        }
+      }
+      best = wave_max(best);
+      if (lane == 0 && best > NEG_INF) atomicMax(&mkey[J], float_order_key(best));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = kn[mt][ks];
+    }
+  }
+  __syncthreads();
+  // keep bits (forced blocks are added by the compaction) and the optional margins
+  const int64_t brow = (int64_t)bg * a.nQB + I;
+  for (int J0 = wave * 64; J0 < a.W * 32; J0 += 256) {
+    const int J = J0 + lane;
+    float margin = NEG_INF;
+    if (J < ncand && mkey[J] != 0u) {
+      const unsigned int k = mkey[J];
+      margin = __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+    }
+    const unsigned long long bal = __ballot(J < ncand && margin >= 0.f);
+    if (lane == 0) {
+      const int w = J0 / 32;
+      a.bits[brow * a.W + w] = (unsigned int)bal;
+      if (w + 1 < a.W) a.bits[brow * a.W + w + 1] = (unsigned int)(bal >> 32);
+    }
+    if (a.margins && J < ncand) a.margins[brow * a.nKB + J] = margin;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Compaction: per (b, g, i) row, keep = (bits | forced) & causal candidates, written as
 // ascending indices; `unit` = block_k (block lists) or 1 (stripe lists).
 // ---------------------------------------------------------------------------------------
@@ -750,6 +1022,14 @@ __global__ __launch_bounds__(256) void est_compact(EstArgs a, int unit) {
 template <int D>
 static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream_t s) {
   hipLaunchKernelGGL(est_quant_k<D>, dim3(a.nKB, a.Hkv, a.B), dim3(256), 0, s, a);
+  if (a.estimator == SA_EST_RELATIVE) {
+    const int64_t rows = (int64_t)a.B * a.N * a.Hq;
+    hipLaunchKernelGGL(est_quant_q_rows<D>, dim3((unsigned int)((rows + 15) / 16)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(est_score_rel<D>, dim3(a.B * a.Hkv * a.nQB), dim3(256),
+                       (size_t)a.nKB * sizeof(unsigned int), s, a);
+    hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, a.bk);
+    return hipGetLastError();
+  }
   // rows of the staged key window: sink tiles + window tiles of the largest query block
   const int sink_rows = ((min(a.sink, a.N) + 31) / 32) * 32;
   const int win_rows = ((a.local - 1 + a.bq - 1) / 32 + 2) * 32;

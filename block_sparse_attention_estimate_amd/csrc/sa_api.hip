@@ -57,6 +57,8 @@ sa_status check_sparse_params(const sa_shape* s, const sa_sparse_params* p, bool
   if (!p) return SA_ERR_NULL;
   if (need_theta && !p->theta) return SA_ERR_NULL;
   if (p->granularity != SA_BLOCK && p->granularity != SA_STRIPE) return SA_ERR_PARAM;
+  if (p->estimator != SA_EST_POOLED && p->estimator != SA_EST_RELATIVE) return SA_ERR_PARAM;
+  if (p->estimator == SA_EST_RELATIVE && p->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
   if (p->sink_tokens < 0 || p->local_tokens < 1) return SA_ERR_PARAM;
   if (p->block_q != 64 && p->block_q != 128) return SA_ERR_UNSUPPORTED;
   if (p->block_k != 64) return SA_ERR_UNSUPPORTED;
@@ -68,7 +70,7 @@ sa_status check_sparse_params(const sa_shape* s, const sa_sparse_params* p, bool
 }
 
 struct EstLayout {
-  size_t kq, sk, qq, sq, abar, bits, total;
+  size_t kq, sk, qq, sq, abar, bits, qr, sr, total;
   int W;
 };
 
@@ -86,6 +88,9 @@ EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p) {
   L.sq = off;   off = align_up(off + (size_t)B * Hq * nQB * sizeof(float));
   L.abar = off; off = align_up(off + (size_t)B * Hq * nQB * sizeof(float));
   L.bits = off; off = align_up(off + (size_t)B * Hkv * nQB * L.W * sizeof(uint32_t));
+  const size_t rows = p->estimator == SA_EST_RELATIVE ? (size_t)B * Hq * N : 0;
+  L.qr = off;   off = align_up(off + rows * D);
+  L.sr = off;   off = align_up(off + rows * sizeof(float));
   L.total = off;
   return L;
 }
@@ -232,6 +237,9 @@ sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params
   a.sq = (float*)(base + L.sq);
   a.abar = (float*)(base + L.abar);
   a.bits = (uint32_t*)(base + L.bits);
+  a.qr = (int8_t*)(base + L.qr);
+  a.sr = (float*)(base + L.sr);
+  a.estimator = params->estimator;
   a.W = L.W;
   a.counts = out->counts;
   a.idx = out->idx;

@@ -20,6 +20,9 @@ struct EstArgs {
   float* sq;               // [B, Hkv, nQB, G] pooled-query scales
   float* abar;             // [B, Hkv, nQB, G] block-averaged anchors
   uint32_t* bits;          // [B, Hkv, nQB, W] keep bits
+  int8_t* qr;              // relative estimator: int8 query rows [B, Hq, N, D]
+  float* sr;               // and their scales [B, Hq, N]
+  int estimator;           // SA_EST_POOLED or SA_EST_RELATIVE
   int W;                   // words per bit row
   // outputs
   int32_t* counts;

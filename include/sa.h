@@ -78,7 +78,21 @@ typedef struct {
   int32_t granularity;            /* SA_BLOCK or SA_STRIPE */
   const float* theta;             /* host [n_q_heads] */
   float softmax_scale;
+  int32_t estimator;              /* SA_EST_POOLED (0) or SA_EST_RELATIVE (1) */
 } sa_sparse_params;
+
+/* Estimators of sa_estimate_mask.
+ * SA_EST_POOLED (AnchorAttention Eq. 1-2): per query block, the anchor (row max over each
+ *   row's sink and local keys, averaged over the block) against int8 scores of the pooled
+ *   query: margin = score - (anchor - theta).  Block and stripe granularity.
+ * SA_EST_RELATIVE (SALE, "What carries the argument" and referee major comment 1): every
+ *   (row, key) pair of the block is estimated from int8 Q (one scale per row) and int8 K
+ *   tiles; a key block is kept when, for some row r and causal key j in it,
+ *   S~[r, j] - LSE_r >= -theta, with LSE_r the log-sum-exp of S~ over row r's sink and local
+ *   keys (theta = -ln tau of SALE's relative score).  Block granularity only
+ *   (SA_ERR_UNSUPPORTED for stripes); its workspace also holds the int8 queries
+ *   (B * seq * n_q_heads * (head_dim + 4) bytes). */
+enum { SA_EST_POOLED = 0, SA_EST_RELATIVE = 1 };
 
 /* Per-row kept lists (the index set I of Eq. (3)), one row per (batch, KV head, query
  * block), rows ordered (b, g, i).  Row r holds counts[r] ascending key-block ids (block

@@ -88,6 +88,15 @@ def test_validation_codes(lib):
     assert _est(lib, s, pu, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
     pq, keep4 = _params(4.0, bq=96)
     assert _est(lib, s, pq, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
+    pe, keep6 = _params(4.0)
+    pe.estimator = 2
+    assert _est(lib, s, pe, ws_bytes=need) == _lib.SA_ERR_PARAM
+    pe.estimator, pe.granularity = _lib.SA_EST_RELATIVE, _lib.SA_STRIPE
+    assert _est(lib, s, pe, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
+    pe.granularity = _lib.SA_BLOCK
+    need_rel = lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(pe))
+    assert need_rel >= need + 256 * 4 * (128 + 4)       # + int8 query rows and their scales
+    assert _est(lib, s, pe, ws_bytes=need_rel - 1) == _lib.SA_ERR_WORKSPACE
     bad = _shape(Hq=6, Hkv=4)
     assert _est(lib, bad, p, ws_bytes=need) == _lib.SA_ERR_SHAPE
     d96 = _shape(D=96)

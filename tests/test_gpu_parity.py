@@ -254,3 +254,44 @@ def test_decode_topp_reduced(dev, batch, seq, hq, hkv, d, top_k, bk, top_p, summ
     assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
     log(f"  top-p ok: budgets {min(budgets)}..{max(budgets)} one-off={off} flips={flips} "
         f"max|dO|={err.max():.2e}")
+
+
+@pytest.mark.parametrize("seq,hq,hkv,d,bq", [(4000, 8, 2, 128, 128), (1500, 16, 2, 128, 128),
+                                             (1000, 4, 2, 64, 64), (777, 2, 2, 128, 128),
+                                             (2100, 4, 1, 64, 128), (200, 4, 1, 128, 64)])
+def test_relative_estimator_reduced(dev, seq, hq, hkv, d, bq):
+    """SALE's element-wise estimate: lists bit-exact outside the band, margins within 1e-3 of
+    the oracle's, at thetas from forced-only to dense; attention under the oracle's lists."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill("llama8b_32k", seq=seq, hq=hq, hkv=hkv, head_dim=d)
+    x.block_q = bq
+    grp = hq // hkv
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=bq, block_k=64, sink=32, local=256)
+    base = np.repeat(np.array([4.0, 6.0, 8.0, 5.0] * 8, np.float32)[:hkv], grp)
+    for theta in [base, np.full(hq, -np.inf, np.float32), np.full(hq, np.inf, np.float32),
+                  base + np.linspace(0, 1, hq, dtype=np.float32)]:
+        log(f"relative N={seq} Hq={hq} Hkv={hkv} d={d} bq={bq} theta={np.unique(theta)[:4]}")
+        lists = sa.estimate_mask(q, k, theta, estimator="relative", margins=True, **kw)
+        torch.cuda.synchronize()
+        ref = oracle.estimate_all_sale(x.q, x.k, theta, **kw)
+        rows, entries, flips = compare_lists(lists, ref)
+        mg = lists.margins.cpu().numpy()
+        worst = 0.0
+        for (b, g, i), r in ref.items():
+            m_ref = r["margin"]
+            m_gpu = mg[b, g, i, :m_ref.size]
+            fin = np.isfinite(m_ref)
+            assert np.array_equal(np.isfinite(m_gpu), fin), (b, g, i)
+            if fin.any():
+                worst = max(worst, float(np.abs(m_gpu[fin] - m_ref[fin]).max()))
+        assert worst < 1e-3, worst
+        log(f"  lists ok: entries={entries} flips={flips} max|dmargin|={worst:.1e}")
+    nqb = -(-seq // bq)
+    dl = upload_lists(ref, (1, hkv, nqb), dev, "block", lists.stride)
+    o, lse = sa.sparse_prefill(q, k, v, dl, **kw)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_all(x.q, x.k, x.v, lists_from_ref(ref), block_q=bq, block_k=64,
+                                  granularity="block")
+    compare_outputs(o, lse, O, LSE)
