@@ -21,6 +21,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA
 
 PREFILL = ("llama8b_128k", "llama8b_32k", "stripe_64k")
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_estimate_amd", "csrc", "attn_kernels.hip")
@@ -163,20 +164,24 @@ def bench_prefill(args, dev):
     G = Hq // Hkv
     q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
     kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    if args.theta is not None:
+        x.theta = np.full(Hq, args.theta, np.float32)
+    est = args.estimator
     stride = None
     if x.granularity == "stripe":
         stride = args.stripe_capacity
     lists = sa.alloc_lists(q, k, block_q=x.block_q, block_k=x.block_k,
                            granularity=x.granularity, stride=stride)
     ws = torch.empty(sa.workspace_size(sa.SA_OP_ESTIMATE, q=q, k=k, granularity=x.granularity,
-                                       **kw), dtype=torch.uint8, device=dev)
+                                       estimator=est, **kw), dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        sa.estimate_mask(q, k, x.theta, granularity=x.granularity, workspace=ws, out=lists, **kw)
+        sa.estimate_mask(q, k, x.theta, granularity=x.granularity, estimator=est, workspace=ws,
+                         out=lists, **kw)
         if ev is not None:
             ev[1].record(stream)
         sa.sparse_prefill(q, k, v, lists, out=o, lse=False, **kw)
@@ -231,8 +236,8 @@ def bench_prefill(args, dev):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload}: batch {B}, {Hq}/{Hkv} heads, d {D}, "
                                f"seq {N}, block {x.block_q}x{x.block_k}, sink {x.sink}, "
-                               f"local {x.local}, {x.granularity}, theta per query head "
-                               f"{sorted(set(np.round(x.theta, 3).tolist()))}",
+                               f"local {x.local}, {x.granularity}, {est} estimator, theta per "
+                               f"query head {sorted(set(np.round(x.theta, 3).tolist()))}",
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_step, 3),
         "estimate_ms": round(est_avg, 3), "attention_ms": round(att_avg, 3),
@@ -247,6 +252,12 @@ def bench_prefill(args, dev):
                      "units": f"{kept_units} kept (head, {x.block_q}x{x.block_k} tile) x "
                               f"{flops_per_unit / 1e6:.3f} MFLOP"},
     }
+    if est == "relative":
+        # the element-wise estimate: 2 d int8 ops per causal (row, key) pair and query head
+        pairs = float(N) * (N + 1) / 2
+        est_ops = 2.0 * D * pairs * Hq * B
+        out["estimate_int8_tops"] = round(est_ops / (est_avg * 1e-3) / 1e12, 1)
+        out["estimate_frac_of_int8_peak"] = round(est_ops / (est_avg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)
     if args.cpu_baseline:
         log("cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline_prefill(x, dense_flops)
@@ -356,6 +367,10 @@ def main():
     ap.add_argument("--kernel", default="attn_block")
     ap.add_argument("--summary", choices=["bf16", "q4"], default="bf16",
                     help="decode: block summaries in bf16 or 4-bit codes + bf16 scales")
+    ap.add_argument("--estimator", choices=["pooled", "relative"], default="pooled",
+                    help="prefill: anchor vs pooled query, or the element-wise relative score")
+    ap.add_argument("--theta", type=float, default=None,
+                    help="prefill: one theta for every head instead of the workload's")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="decode: per-(b, KV head) budget from the block-score distribution")
     ap.add_argument("--top-k", type=int, default=0,

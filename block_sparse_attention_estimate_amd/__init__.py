@@ -120,12 +120,13 @@ class Lists:
 
 
 def workspace_size(op, *, q=None, k=None, block_q=128, block_k=64, sink=32, local=256,
-                   granularity="block", theta=None, shape=None, decode_params=None) -> int:
+                   granularity="block", theta=None, estimator="pooled", shape=None,
+                   decode_params=None) -> int:
     lib = _lib.load()
     if op in (SA_OP_ESTIMATE, SA_OP_CALIBRATE):
         s = _prefill_shape(q, k)
         p, keep = _sparse_params(block_q, block_k, sink, local, granularity,
-                                 theta if theta is not None else 0.0, 0.0, q.shape[2])
+                                 theta if theta is not None else 0.0, 0.0, q.shape[2], estimator)
         return int(lib.sa_workspace_size(op, ctypes.byref(s), ctypes.byref(p)))
     if op == SA_OP_DECODE:
         return int(lib.sa_workspace_size(op, ctypes.byref(shape), ctypes.byref(decode_params)))
