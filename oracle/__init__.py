@@ -36,6 +36,7 @@ from .estimate import (  # noqa: F401
     forced_columns,
     estimate_rows,
     estimate_all,
+    group_step,
     AMBIGUITY_BAND,
 )
 from .attention import attention_rows, attention_all, dense_causal_reference_mask  # noqa: F401

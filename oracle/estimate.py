@@ -258,3 +258,41 @@ def estimate_all(q, k, theta, *, block_q, block_k, sink, local, granularity="blo
                          local=local, granularity=granularity, rows=rows, scale=scale,
                          kv_of_q=kv_of_q, quantized=quantized, keep_margins=keep_margins,
                          per_head=per_head)
+
+
+# --------------------------------------------------------------------------------------
+# AnchorAttention's step: grouped identification of query blocks.
+# --------------------------------------------------------------------------------------
+def group_step(ref: dict, step: int) -> dict:
+    """Query blocks identified in groups of ``step`` (AnchorAttention, "Assumptions & free
+    parameters": step groups query blocks for identification, and a key selected by any block
+    of a group is marked active for every block of the group; 16 in its experiments).
+
+    Reading: "selected" is the threshold test (margin >= 0), not the forced set; each block
+    keeps its own forced entries and its causal candidates, so
+    kept(i) = forced(i) | {J in candidates(i) : margin(i', J) >= 0 for some i' in group(i)}.
+    ``ref`` must hold every block of each group it touches, with margins.  An entry is
+    ambiguous for a block when it is ambiguous in any block of the group.  Margins are left
+    per block."""
+    if step <= 1:
+        return ref
+    groups: dict = {}
+    for (b, g, i), r in ref.items():
+        groups.setdefault((b, g, i // step), []).append((i, r))
+    out = {}
+    for (b, g, _), members in groups.items():
+        selected, amb = set(), set()
+        for i, r in members:
+            m = r["margin"]
+            selected |= set(np.nonzero(m >= 0)[0].tolist())
+            amb |= set(np.nonzero(np.abs(m) < AMBIGUITY_BAND)[0].tolist())
+        for i, r in members:
+            nc = r["n_candidates"]
+            forced = set(r["forced"].tolist())
+            kept = forced | {J for J in selected if J < nc}
+            rec = dict(r)
+            rec["kept"] = np.array(sorted(kept), dtype=np.int32)
+            rec["ambiguous"] = np.array(sorted(J for J in amb if J < nc and J not in forced),
+                                        dtype=np.int32)
+            out[(b, g, i)] = rec
+    return out
