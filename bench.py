@@ -180,8 +180,8 @@ def bench_prefill(args, dev):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        sa.estimate_mask(q, k, x.theta, granularity=x.granularity, estimator=est, workspace=ws,
-                         out=lists, **kw)
+        sa.estimate_mask(q, k, x.theta, granularity=x.granularity, estimator=est,
+                         step=args.step, workspace=ws, out=lists, **kw)
         if ev is not None:
             ev[1].record(stream)
         sa.sparse_prefill(q, k, v, lists, out=o, lse=False, **kw)
@@ -237,7 +237,8 @@ def bench_prefill(args, dev):
         "config": {"workload": f"{args.workload}: batch {B}, {Hq}/{Hkv} heads, d {D}, "
                                f"seq {N}, block {x.block_q}x{x.block_k}, sink {x.sink}, "
                                f"local {x.local}, {x.granularity}, {est} estimator, theta per "
-                               f"query head {sorted(set(np.round(x.theta, 3).tolist()))}",
+                               f"query head {sorted(set(np.round(x.theta, 3).tolist()))}" +
+                               (f", step {args.step}" if args.step > 1 else ""),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_step, 3),
         "estimate_ms": round(est_avg, 3), "attention_ms": round(att_avg, 3),
@@ -369,6 +370,8 @@ def main():
                     help="decode: block summaries in bf16 or 4-bit codes + bf16 scales")
     ap.add_argument("--estimator", choices=["pooled", "relative"], default="pooled",
                     help="prefill: anchor vs pooled query, or the element-wise relative score")
+    ap.add_argument("--step", type=int, default=1,
+                    help="prefill: identify query blocks in groups of STEP (AnchorAttention)")
     ap.add_argument("--theta", type=float, default=None,
                     help="prefill: one theta for every head instead of the workload's")
     ap.add_argument("--top-p", type=float, default=0.0,

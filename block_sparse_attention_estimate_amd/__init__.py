@@ -76,13 +76,14 @@ _ESTIMATORS = {"pooled": _lib.SA_EST_POOLED, "relative": _lib.SA_EST_RELATIVE}
 
 
 def _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale, n_q_heads,
-                   estimator="pooled"):
+                   estimator="pooled", step=1):
     p = _lib.SaSparseParams()
     p.block_q, p.block_k, p.sink_tokens, p.local_tokens = block_q, block_k, sink, local
     p.granularity = _gran(granularity)
     if estimator not in _ESTIMATORS:
         raise ValueError(f"estimator must be one of {sorted(_ESTIMATORS)}")
     p.estimator = _ESTIMATORS[estimator]
+    p.step = int(step)
     p.softmax_scale = float(softmax_scale or 0.0)
     arr = None
     if theta is not None:
@@ -153,15 +154,16 @@ def alloc_lists(q, k, *, block_q, block_k=64, granularity="block", stride=None,
 
 def estimate_mask(q, k, theta, *, block_q=128, block_k=64, sink=32, local=256,
                   granularity="block", softmax_scale=0.0, stride=None, margins=False,
-                  estimator="pooled", workspace=None, out: Lists | None = None,
+                  estimator="pooled", step=1, workspace=None, out: Lists | None = None,
                   stream=None) -> Lists:
     """Estimation pass (sa_estimate_mask).  q [B, N, Hq, d], k [B, N, Hkv, d] bf16 CUDA
     tensors; theta scalar or [Hq] in logit units; estimator "pooled" (anchor vs pooled
-    query) or "relative" (element-wise estimate against the row's sink-local log-sum-exp)."""
+    query) or "relative" (element-wise estimate against the row's sink-local log-sum-exp);
+    step > 1 identifies query blocks in groups of `step` (AnchorAttention's step)."""
     lib = _lib.load()
     s = _prefill_shape(q, k)
     p, keep = _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale,
-                             q.shape[2], estimator)
+                             q.shape[2], estimator, step)
     lists = out if out is not None else alloc_lists(q, k, block_q=block_q, block_k=block_k,
                                                     granularity=granularity, stride=stride,
                                                     margins=margins)

@@ -35,7 +35,8 @@ class SaSparseParams(ctypes.Structure):
     _fields_ = [("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("sink_tokens", ctypes.c_int32), ("local_tokens", ctypes.c_int32),
                 ("granularity", ctypes.c_int32), ("theta", ctypes.POINTER(ctypes.c_float)),
-                ("softmax_scale", ctypes.c_float), ("estimator", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("estimator", ctypes.c_int32),
+                ("step", ctypes.c_int32)]
 
 
 class SaLists(ctypes.Structure):

@@ -16,6 +16,7 @@
 //   est_score_block   int8 MFMA of key tiles against pooled queries, block max, margin,
 //                     max over the group's heads -> one keep bit per (query block, key block)
 //   est_score_stripe  same per key column (no block max)
+//   est_step_or       (step > 1) keep bits OR-ed over groups of `step` query blocks
 //   est_compact       bits | forced, causal -> ascending index lists + counts
 // With the relative-score estimator (SALE) est_anchor_pool and est_score_block are replaced
 // by est_quant_q_rows (int8 query rows) and est_score_rel (element-wise estimate, LSE of the
@@ -957,6 +958,24 @@ __global__ __launch_bounds__(256) void est_score_rel(EstArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Grouped identification (AnchorAttention's step): the keep bits of every query block of a
+// group of `step` become the OR over the group; the compaction then adds each block's forced
+// entries and keeps its causal candidates only.  One workgroup per (b, g, group).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void est_step_or(EstArgs a) {
+  const int n_groups = (a.nQB + a.step - 1) / a.step;
+  const int gi = blockIdx.x % n_groups;
+  const int bg = blockIdx.x / n_groups;
+  const int i0 = gi * a.step, i1 = min(a.nQB, i0 + a.step);
+  uint32_t* rows = a.bits + ((int64_t)bg * a.nQB) * a.W;
+  for (int w = threadIdx.x; w < a.W; w += 256) {
+    unsigned int acc = 0u;
+    for (int i = i0; i < i1; ++i) acc |= rows[(int64_t)i * a.W + w];
+    for (int i = i0; i < i1; ++i) rows[(int64_t)i * a.W + w] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Compaction: per (b, g, i) row, keep = (bits | forced) & causal candidates, written as
 // ascending indices; `unit` = block_k (block lists) or 1 (stripe lists).
 // ---------------------------------------------------------------------------------------
@@ -1019,6 +1038,12 @@ __global__ __launch_bounds__(256) void est_compact(EstArgs a, int unit) {
 }
 
 // ---------------------------------------------------------------------------------------
+static void launch_step_or(const EstArgs& a, hipStream_t s) {
+  if (a.step <= 1 || a.nQB <= 1) return;
+  const int n_groups = (a.nQB + a.step - 1) / a.step;
+  hipLaunchKernelGGL(est_step_or, dim3(a.B * a.Hkv * n_groups), dim3(256), 0, s, a);
+}
+
 template <int D>
 static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream_t s) {
   hipLaunchKernelGGL(est_quant_k<D>, dim3(a.nKB, a.Hkv, a.B), dim3(256), 0, s, a);
@@ -1027,6 +1052,7 @@ static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream
     hipLaunchKernelGGL(est_quant_q_rows<D>, dim3((unsigned int)((rows + 15) / 16)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(est_score_rel<D>, dim3(a.B * a.Hkv * a.nQB), dim3(256),
                        (size_t)a.nKB * sizeof(unsigned int), s, a);
+    launch_step_or(a, s);
     hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, a.bk);
     return hipGetLastError();
   }
@@ -1050,9 +1076,11 @@ static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream
     else
       hipLaunchKernelGGL((est_score_stripe<D, false>), dim3(a.B * a.Hkv * n_rt_s * n_jc), dim3(256), 0,
                          s, a, n_rt_s, n_jc);
+    launch_step_or(a, s);
     hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, 1);
   } else {
     hipLaunchKernelGGL(est_score_block<D>, dim3(grid), dim3(256), 0, s, a, n_rt, n_jc);
+    launch_step_or(a, s);
     hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, a.bk);
   }
   return hipGetLastError();

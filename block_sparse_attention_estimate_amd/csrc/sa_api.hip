@@ -59,6 +59,7 @@ sa_status check_sparse_params(const sa_shape* s, const sa_sparse_params* p, bool
   if (p->granularity != SA_BLOCK && p->granularity != SA_STRIPE) return SA_ERR_PARAM;
   if (p->estimator != SA_EST_POOLED && p->estimator != SA_EST_RELATIVE) return SA_ERR_PARAM;
   if (p->estimator == SA_EST_RELATIVE && p->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
+  if (p->step < 0) return SA_ERR_PARAM;
   if (p->sink_tokens < 0 || p->local_tokens < 1) return SA_ERR_PARAM;
   if (p->block_q != 64 && p->block_q != 128) return SA_ERR_UNSUPPORTED;
   if (p->block_k != 64) return SA_ERR_UNSUPPORTED;
@@ -240,6 +241,7 @@ sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params
   a.qr = (int8_t*)(base + L.qr);
   a.sr = (float*)(base + L.sr);
   a.estimator = params->estimator;
+  a.step = params->step;
   a.W = L.W;
   a.counts = out->counts;
   a.idx = out->idx;

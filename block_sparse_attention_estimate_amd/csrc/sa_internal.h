@@ -23,6 +23,7 @@ struct EstArgs {
   int8_t* qr;              // relative estimator: int8 query rows [B, Hq, N, D]
   float* sr;               // and their scales [B, Hq, N]
   int estimator;           // SA_EST_POOLED or SA_EST_RELATIVE
+  int step;                // query blocks per identification group (<= 1: none)
   int W;                   // words per bit row
   // outputs
   int32_t* counts;

@@ -79,7 +79,15 @@ typedef struct {
   const float* theta;             /* host [n_q_heads] */
   float softmax_scale;
   int32_t estimator;              /* SA_EST_POOLED (0) or SA_EST_RELATIVE (1) */
+  int32_t step;                   /* query-block group size of the identification, 0 or 1: none */
 } sa_sparse_params;
+
+/* step (AnchorAttention, "Assumptions & free parameters": query blocks are identified in
+ * groups of `step`, 16 in its experiments, and a key selected by any block of a group is
+ * active for every block of it): with step > 1 the list of query block i holds its forced
+ * entries and every causal candidate of i that passes the threshold for some block of i's
+ * group {floor(i / step) * step, ...}.  Margins, when requested, stay per block.
+ * step < 0: SA_ERR_PARAM. */
 
 /* Estimators of sa_estimate_mask.
  * SA_EST_POOLED (AnchorAttention Eq. 1-2): per query block, the anchor (row max over each

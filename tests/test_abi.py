@@ -94,6 +94,9 @@ def test_validation_codes(lib):
     pe.estimator, pe.granularity = _lib.SA_EST_RELATIVE, _lib.SA_STRIPE
     assert _est(lib, s, pe, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
     pe.granularity = _lib.SA_BLOCK
+    ps, keep7 = _params(4.0)
+    ps.step = -1
+    assert _est(lib, s, ps, ws_bytes=need) == _lib.SA_ERR_PARAM
     need_rel = lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(pe))
     assert need_rel >= need + 256 * 4 * (128 + 4)       # + int8 query rows and their scales
     assert _est(lib, s, pe, ws_bytes=need_rel - 1) == _lib.SA_ERR_WORKSPACE

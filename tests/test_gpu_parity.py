@@ -295,3 +295,34 @@ def test_relative_estimator_reduced(dev, seq, hq, hkv, d, bq):
     O, LSE = oracle.attention_all(x.q, x.k, x.v, lists_from_ref(ref), block_q=bq, block_k=64,
                                   granularity="block")
     compare_outputs(o, lse, O, LSE)
+
+
+@pytest.mark.parametrize("name,seq,estimator,step", [("llama8b_32k", 4000, "pooled", 4),
+                                                    ("llama8b_32k", 4000, "pooled", 16),
+                                                    ("stripe_64k", 3000, "pooled", 4),
+                                                    ("llama8b_32k", 3000, "relative", 16),
+                                                    ("llama8b_32k", 2100, "relative", 3)])
+def test_step_grouping(dev, name, seq, estimator, step):
+    """Grouped identification: lists equal the oracle's grouped lists (bit-exact outside the
+    band of any block of the group)."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill(name, seq=seq, hq=8, hkv=2)
+    # thetas at which both estimators select blocks beyond the forced ones on this data
+    theta = np.repeat(np.array([11.0, 12.0] if estimator == "pooled" else [4.0, 6.0],
+                               np.float32), 4)
+    q, k = to_dev(x.q, dev), to_dev(x.k, dev)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    log(f"step={step} {estimator} {name} N={seq}")
+    lists = sa.estimate_mask(q, k, theta, granularity=x.granularity, estimator=estimator,
+                             step=step, stride=seq if x.granularity == "stripe" else None, **kw)
+    torch.cuda.synchronize()
+    if estimator == "pooled":
+        ref = oracle.estimate_all(x.q, x.k, theta, granularity=x.granularity, **kw)
+    else:
+        ref = oracle.estimate_all_sale(x.q, x.k, theta, **kw)
+    grouped = oracle.group_step(ref, step)
+    rows, entries, flips = compare_lists(lists, grouped)
+    plain = sum(r["kept"].size for r in ref.values())
+    log(f"  grouped lists ok: entries={entries} (ungrouped {plain}) flips={flips}")
+    assert entries > plain
