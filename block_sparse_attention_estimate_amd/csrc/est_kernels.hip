@@ -757,7 +757,7 @@ __global__ __launch_bounds__(256) void est_quant_q_rows(EstArgs a) {
 //     atomic max on order-preserving keys.
 // The margins of all units (heads and row ranges) then give one keep bit per key block.
 template <int D>
-__global__ __launch_bounds__(256) void est_score_rel(EstArgs a) {
+__global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
   constexpr int KS = D / 32;
   extern __shared__ unsigned int mkey[];             // [nKB] best margin key per key block
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -852,26 +852,23 @@ __global__ __launch_bounds__(256) void est_score_rel(EstArgs a) {
         for (int nt = 0; nt < 2; ++nt) {
           const int row = rowv[uu][nt];
           const float mult = __fmul_rn(__fmul_rn(sqv[uu][nt], skv), a.c);
-          float x[32];
-          float tm = NEG_INF;
+          // online log-sum-exp over the lane's keys of the row's area
+          float m_ = mr[uu][nt], s_ = sr_[uu][nt];
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
               const bool in = key <= row && key < a.N && (key < a.sink || key >= row - a.local + 1);
-              const float v = in ? __fmul_rn((float)acc[mt][nt][r], mult) : NEG_INF;
-              x[mt * 16 + r] = v;
-              tm = fmaxf(tm, v);
+              if (in) {
+                const float v = __fmul_rn((float)acc[mt][nt][r], mult);
+                const float mn = fmaxf(m_, v);
+                s_ = s_ * __expf(m_ - mn) + __expf(v - mn);
+                m_ = mn;
+              }
             }
-          if (tm > NEG_INF) {
-            const float mn = fmaxf(mr[uu][nt], tm);
-            float sacc = sr_[uu][nt] * __expf(mr[uu][nt] - mn);
-#pragma unroll
-            for (int t = 0; t < 32; ++t) sacc += __expf(x[t] - mn);
-            mr[uu][nt] = mn;
-            sr_[uu][nt] = sacc;
-          }
+          mr[uu][nt] = m_;
+          sr_[uu][nt] = s_;
         }
       }
     }
