@@ -21,6 +21,7 @@ import numpy as np
 
 from .attention import attention_all
 from .estimate import estimate_all
+from .estimate_sale import estimate_all_sale
 
 
 def full_lists(n: int, b: int, hkv: int, block_q: int, block_k: int) -> dict:
@@ -44,9 +45,10 @@ def head_l1_error(o_ref: np.ndarray, o: np.ndarray) -> np.ndarray:
 
 def calibrate_theta(q, k, v, *, tau0: float = 0.008, err_bound: float = 0.4,
                     max_halvings: int = 16, block_q: int, block_k: int, sink: int, local: int,
-                    scale=None) -> dict:
+                    scale=None, estimator: str = "pooled") -> dict:
     """Returns dict(theta [Hq] float32, err [Hq] float64, halvings [Hq] int, history: list of
-    (theta, err) per round)."""
+    (theta, err) per round).  estimator "relative" calibrates SALE's own element-wise
+    estimate (``estimate_sale``) instead of the pooled one."""
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     kw = dict(block_q=block_q, block_k=block_k)
@@ -56,8 +58,12 @@ def calibrate_theta(q, k, v, *, tau0: float = 0.008, err_bound: float = 0.4,
     history = []
     while True:
         theta = np.array([theta0 + int(kh) * math.log(2.0) for kh in halv], dtype=np.float32)
-        est = estimate_all(q, k, theta, sink=sink, local=local, granularity="block", scale=scale,
-                           keep_margins=False, **kw)
+        if estimator == "relative":
+            est = estimate_all_sale(q, k, theta, sink=sink, local=local, scale=scale,
+                                    keep_margins=False, **kw)
+        else:
+            est = estimate_all(q, k, theta, sink=sink, local=local, granularity="block",
+                               scale=scale, keep_margins=False, **kw)
         o, _ = attention_all(q, k, v, {key: r["kept"] for key, r in est.items()}, scale=scale, **kw)
         err = head_l1_error(o_ref, o)
         history.append((theta.copy(), err.copy()))

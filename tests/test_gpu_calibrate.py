@@ -50,14 +50,18 @@ def test_calibrate_wiring(dev):
     np.testing.assert_allclose(err, want, rtol=1e-5, atol=1e-9)
 
 
-@pytest.mark.parametrize("bound", [0.05, 0.06])
-def test_calibrate_against_oracle(dev, bound):
+@pytest.mark.parametrize("estimator,bound", [("pooled", 0.05), ("pooled", 0.06),
+                                             ("relative", 0.02), ("relative", 0.03)])
+def test_calibrate_against_oracle(dev, estimator, bound):
+    """relative: SALE's own pipeline -- its element-wise estimate with tau halved from 0.008."""
     import block_sparse_attention_estimate_amd as sa
     x, q, k, v = _data(dev)
     kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
-    th, err, hv = sa.calibrate_theta(q, k, v, tau0=0.008, err_bound=bound, max_halvings=24, **kw)
-    log(f"bound {bound}: gpu halvings {hv.tolist()} err {np.round(err, 4).tolist()}")
-    ref = oracle.calibrate_theta(x.q, x.k, x.v, tau0=0.008, err_bound=bound, max_halvings=24, **kw)
+    th, err, hv = sa.calibrate_theta(q, k, v, tau0=0.008, err_bound=bound, max_halvings=24,
+                                     estimator=estimator, **kw)
+    log(f"{estimator} bound {bound}: gpu halvings {hv.tolist()} err {np.round(err, 4).tolist()}")
+    ref = oracle.calibrate_theta(x.q, x.k, x.v, tau0=0.008, err_bound=bound, max_halvings=24,
+                                 estimator=estimator, **kw)
     hist = np.array([e for _, e in ref["history"]])          # [rounds, Hq]
     log(f"          oracle halvings {ref['halvings'].tolist()} err {np.round(ref['err'], 4).tolist()}")
     for h in range(q.shape[2]):

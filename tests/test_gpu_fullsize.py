@@ -22,7 +22,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0):
+def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled"):
     import torch
     import block_sparse_attention_estimate_amd as sa
     log(f"generating {name}")
@@ -34,7 +34,8 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0):
     q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
     kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
     stride = 8192 if x.granularity == "stripe" else None
-    lists = sa.estimate_mask(q, k, x.theta, granularity=x.granularity, stride=stride, **kw)
+    lists = sa.estimate_mask(q, k, x.theta, granularity=x.granularity, stride=stride,
+                             estimator=estimator, **kw)
     o, lse = sa.sparse_prefill(q, k, v, lists, **kw)
     torch.cuda.synchronize()
     assert not lists.overflowed()
@@ -49,10 +50,15 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0):
         while len(gi) < n_rows:
             gi.add((int(rng.integers(0, Hkv)), int(rng.integers(0, nqb))))
         rows = sorted((0, g, i) for g, i in gi)
-    log(f"oracle estimate of {len(rows)} rows")
-    ref = oracle.estimate_rows(x.q, x.k, x.theta, rows=rows, keep_margins=False,
-                               block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local,
-                               granularity=x.granularity)
+    log(f"oracle estimate of {len(rows)} rows ({estimator})")
+    if estimator == "pooled":
+        ref = oracle.estimate_rows(x.q, x.k, x.theta, rows=rows, keep_margins=False,
+                                   block_q=x.block_q, block_k=x.block_k, sink=x.sink,
+                                   local=x.local, granularity=x.granularity)
+    else:
+        ref = oracle.estimate_rows_sale(x.q, x.k, x.theta, rows=rows, keep_margins=False,
+                                        block_q=x.block_q, block_k=x.block_k, sink=x.sink,
+                                        local=x.local)
     nrows, entries, flips = compare_lists(lists, ref)
     log(f"  lists ok: rows={nrows} entries={entries} ambiguous flips={flips}")
     counts = lists.counts.cpu().numpy()
@@ -86,6 +92,12 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0):
 
 def test_llama8b_32k_every_row(dev):
     _prefill_parity(dev, "llama8b_32k", n_rows=None, n_attn=16)
+
+
+def test_llama8b_32k_relative_sampled(dev):
+    """SALE's element-wise estimator at the 32K workload (theta 4.0 on every head keeps about
+    half of the blocks there)."""
+    _prefill_parity(dev, "llama8b_32k", n_rows=32, n_attn=10, estimator="relative")
 
 
 def test_llama8b_128k_sampled(dev):
