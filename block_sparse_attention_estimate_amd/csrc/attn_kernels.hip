@@ -408,20 +408,6 @@ __global__ __launch_bounds__(128 * HPW) void attn_sparse(AttnArgs a) {
 //    k0..k0+3 of dim d0 + i -- exactly the 4 keys the P^T register layout pairs with that lane.
 // ---------------------------------------------------------------------------------------
 
-// Workgroup barrier for the DMA pipeline.  __syncthreads() carries a workgroup release fence,
-// and since the direct-to-LDS loads write LDS the fence makes the compiler wait for every one
-// of them (vmcnt(0)) -- including the prefetch just issued.  Here the wait is explicit: this
-// wave's DMAs older than the newest n are complete and its LDS reads have returned; after the
-// barrier the same holds for every wave.  The empty asm statements keep the compiler from
-// moving memory operations across the barrier.
-#define DMA_BARRIER(n)                                   \
-  do {                                                   \
-    __builtin_amdgcn_s_waitcnt(VMCNT_LGKM0_IMM(n));      \
-    asm volatile("" ::: "memory");                       \
-    __builtin_amdgcn_s_barrier();                        \
-    asm volatile("" ::: "memory");                       \
-  } while (0)
-
 template <int D, int HPW>
 __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   // The host pass only needs this kernel's signature (for its launch stub).

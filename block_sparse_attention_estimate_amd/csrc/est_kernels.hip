@@ -406,7 +406,9 @@ __global__ __launch_bounds__(256) void est_anchor_pool_gl(EstArgs a) {
 // in-lane plus one half swap.  Workgroup = 4 waves x 64 rows (256 rows), 32 key blocks.
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void est_score_block(EstArgs a, int n_rt, int n_jc) {
+__global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, int n_jc) {
+  // The host pass only needs this kernel's signature (for its launch stub).
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KS = D / 32;
   constexpr int NT = 2;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -443,38 +445,50 @@ __global__ __launch_bounds__(256) void est_score_block(EstArgs a, int n_rt, int 
     for (int ks = 0; ks < KS; ++ks) qf[nt][ks] = *(const i32x4*)(qp + ks * 32);
   }
   const int e_min = min(a.N, ((rt * 256 + wave * 64) / G + 1) * a.bq) - 1;
-  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
+  // K tiles go HBM -> LDS with direct loads into four stages shared by the four waves (rows
+  // padded to D + 16 bytes: the 16 rows one quarter-wave reads land on distinct banks)
+  constexpr int KP = D + 16;
+  constexpr int WIN = (64 * KP + 1023) / 1024;       // 1 KB windows per tile
+  constexpr int SL = (WIN + 3) / 4;                   // windows per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks2[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks3[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D;
+  int s_off[SL];                                      // byte offset in a tile of this lane's 16 bytes
+#pragma unroll
+  for (int k = 0; k < SL; ++k) {
+    const int o = min(wave + 4 * k, WIN - 1) * 1024 + lane * 16;
+    const int r = min(o / KP, 63), c = o % KP;
+    s_off[k] = r * D + (c < D ? c : 0);               // pads and the tail get a harmless copy
+  }
+  auto issue = [&](unsigned char* st, int J) {
+    const int8_t* tb = kbase + (int64_t)J * 64 * D;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      const int wdw = wave + 4 * k;
+      __builtin_amdgcn_global_load_lds(tb + s_off[k], LDS_PTR(void, wdw < WIN ? st + wdw * 1024 : kspare), 16, 0, 0);
+    }
+  };
+  const int k_rd = l32 * KP + half * 16;
   unsigned int bits[NT] = {0u, 0u};
 
-  i32x4 kf[2][KS], kn[2][KS];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[mt][ks] = *(const i32x4*)(kbase + (int64_t)(J0 * 64 + mt * 32 + l32) * D + ks * 32);
-  for (int J = J0; J < J_end; ++J) {
-    if (J + 1 < J_end) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kn[mt][ks] = *(const i32x4*)(kbase + (int64_t)((J + 1) * 64 + mt * 32 + l32) * D + ks * 32);
-    }
+  // one key tile: D^T on int8 MFMA, block max, margin, max over the group, keep bit
+  auto tile = [&](const unsigned char* st, int J) {
     i32x16 acc[2][NT];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (i32x16){};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int mt = 0; mt < 2; ++mt) {
+        const i32x4 kf = *(const i32x4*)(st + k_rd + mt * 32 * KP + ks * 32);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_i8(kf[mt][ks], qf[nt][ks], acc[mt][nt]);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = kn[mt][ks];
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_i8(kf, qf[nt][ks], acc[mt][nt]);
+      }
     const float skv = a.sk[(int64_t)bg * a.nKB + J];
     const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
 #pragma unroll
@@ -509,7 +523,33 @@ __global__ __launch_bounds__(256) void est_score_block(EstArgs a, int n_rt, int 
         a.margins[((int64_t)bg * a.nQB + iq) * a.nKB + J] = margin;
       }
     }
+  };
+
+  // Tile J0 + j is in stage j % 4; tiles j+1 and j+2 are loaded or in flight.  Step j
+  // computes tile j, issues tile j+3 (clamped to the last tile, so every wave issues SL loads
+  // per step) into the stage of tile j-1 and waits until tile j+1 has landed.
+  const int nt_ = J_end - J0;
+  issue(ks0, J0);
+  issue(ks1, J0 + min(1, nt_ - 1));
+  issue(ks2, J0 + min(2, nt_ - 1));
+  DMA_BARRIER(2 * SL);
+  auto step = [&](const unsigned char* sc, unsigned char* sd, int j) {
+    tile(sc, J0 + j);
+    issue(sd, J0 + min(j + 3, nt_ - 1));
+    DMA_BARRIER(2 * SL);
+  };
+  int j = 0;
+  for (; j + 4 <= nt_; j += 4) {
+    step(ks0, ks3, j);
+    step(ks1, ks0, j + 1);
+    step(ks2, ks1, j + 2);
+    step(ks3, ks2, j + 3);
   }
+  if (j < nt_) step(ks0, ks3, j);
+  if (j + 1 < nt_) step(ks1, ks0, j + 1);
+  if (j + 2 < nt_) step(ks2, ks1, j + 2);
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (half == 0 && rowR[nt] < rows_total && (rowR[nt] % G) == 0) {
@@ -517,6 +557,7 @@ __global__ __launch_bounds__(256) void est_score_block(EstArgs a, int n_rt, int 
       a.bits[((int64_t)bg * a.nQB + iq) * a.W + jc] = bits[nt];
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 // ---------------------------------------------------------------------------------------

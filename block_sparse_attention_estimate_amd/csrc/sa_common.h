@@ -99,6 +99,20 @@ SA_DEV int wave_uniform(int v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Workgroup barrier for the DMA pipeline.  __syncthreads() carries a workgroup release fence,
+// and since the direct-to-LDS loads write LDS the fence makes the compiler wait for every one
+// of them (vmcnt(0)) -- including the prefetch just issued.  Here the wait is explicit: this
+// wave's DMAs older than the newest n are complete and its LDS reads have returned; after the
+// barrier the same holds for every wave.  The empty asm statements keep the compiler from
+// moving memory operations across the barrier.
+#define DMA_BARRIER(n)                                   \
+  do {                                                   \
+    __builtin_amdgcn_s_waitcnt(VMCNT_LGKM0_IMM(n));      \
+    asm volatile("" ::: "memory");                       \
+    __builtin_amdgcn_s_barrier();                        \
+    asm volatile("" ::: "memory");                       \
+  } while (0)
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger unsigned).
 SA_DEV unsigned int float_order_key(float f) {
   unsigned int u = __float_as_uint(f);
