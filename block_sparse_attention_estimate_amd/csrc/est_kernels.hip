@@ -799,6 +799,8 @@ __global__ __launch_bounds__(256) void est_quant_q_rows(EstArgs a) {
 // The margins of all units (heads and row ranges) then give one keep bit per key block.
 template <int D>
 __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
+  // The host pass only needs this kernel's signature (for its launch stub).
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KS = D / 32;
   extern __shared__ unsigned int mkey[];             // [nKB] best margin key per key block
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -826,10 +828,39 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
         kf[mt][ks] = *(const i32x4*)(kbase + (int64_t)(J * 64 + mt * 32 + l32) * D + ks * 32);
   };
 
+  // main-loop key tiles go HBM -> LDS with direct loads into four stages shared by the four
+  // waves (rows padded to D + 16 bytes: the 16 rows one quarter-wave reads land on distinct
+  // banks)
+  constexpr int KP = D + 16;
+  constexpr int WIN = (64 * KP + 1023) / 1024;
+  constexpr int SL = (WIN + 3) / 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks2[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks3[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
+  const int8_t* ktile0 = a.kq + ((int64_t)bg * a.nKB * 64) * D;
+  int s_off[SL];
+#pragma unroll
+  for (int k = 0; k < SL; ++k) {
+    const int o = min(wave + 4 * k, WIN - 1) * 1024 + lane * 16;
+    const int r = min(o / KP, 63), c = o % KP;
+    s_off[k] = r * D + (c < D ? c : 0);               // pads and the tail get a harmless copy
+  }
+  auto issue = [&](unsigned char* st, int J) {
+    const int8_t* tb = ktile0 + (int64_t)J * 64 * D;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      const int wdw = wave + 4 * k;
+      __builtin_amdgcn_global_load_lds(tb + s_off[k], LDS_PTR(void, wdw < WIN ? st + wdw * 1024 : kspare), 16, 0, 0);
+    }
+  };
+  const int k_rd = l32 * KP + half * 16;
+  const int Jn = ncand;                                // causal key tiles of the block
+
   for (int u0 = 0; u0 < U; u0 += 8) {
     const int ua = u0 + 2 * wave;
-    const int nu = max(0, min(2, U - ua));
-    if (nu == 0) continue;
+    const int nu = max(0, min(2, U - ua));            // 0: this wave only loads and waits
     i32x4 qf[2][2][KS];
     float sqv[2][2], lse[2][2], thv[2];
     int rowv[2][2], rmin[2], rmax[2];
@@ -877,7 +908,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
         sr_[uu][nt] = 0.f;
       }
     const int wlo = max(0, min(rmin[0], two ? rmin[1] : rmin[0]) - a.local + 1) / 64;
-    const int whi = max(rmax[0], two ? rmax[1] : rmax[0]) / 64;
+    const int whi = nu > 0 ? max(rmax[0], two ? rmax[1] : rmax[0]) / 64 : -1;
     for (int J = 0; J <= whi; ++J) {
       if (J > sink_last && J < wlo) J = wlo;           // skip the tiles between the areas
       i32x4 kf[2][KS];
@@ -927,11 +958,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
       }
 
     // 2. every causal key tile: best (S~ - LSE + theta) over the wave's rows and units
-    const int Jend = max(rmax[0], two ? rmax[1] : rmax[0]) / 64 + 1;
-    i32x4 kf[2][KS], kn[2][KS];
-    load_k(0, kf);
-    for (int J = 0; J < Jend; ++J) {
-      if (J + 1 < Jend) load_k(J + 1, kn);
+    auto tile = [&](const unsigned char* st, int J) {
       const float skv = skb[J];
       float best = NEG_INF;
 #pragma unroll
@@ -939,7 +966,18 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
         if (uu == 1 && !two) break;
         if (J * 64 > rmax[uu]) continue;
         i32x16 acc[2][2];
-        dots(uu, kf, acc);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (i32x16){};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const i32x4 kf = *(const i32x4*)(st + k_rd + mt * 32 * KP + ks * 32);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_i8(kf, qf[uu][nt][ks], acc[mt][nt]);
+          }
         const bool need_mask = J * 64 + 63 > rmin[uu] || J * 64 + 63 >= a.N;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -969,11 +1007,32 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
       }
       best = wave_max(best);
       if (lane == 0 && best > NEG_INF) atomicMax(&mkey[J], float_order_key(best));
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = kn[mt][ks];
+    };
+    // Tile j is in stage j % 4; tiles j+1 and j+2 are loaded or in flight.  Step j computes
+    // tile j (waves with units), issues tile j+3 (clamped to the last tile, so every wave
+    // issues SL loads per step) into the stage of tile j-1 and waits until tile j+1 landed.
+    issue(ks0, 0);
+    issue(ks1, min(1, Jn - 1));
+    issue(ks2, min(2, Jn - 1));
+    DMA_BARRIER(2 * SL);
+    auto step = [&](const unsigned char* sc, unsigned char* sd, int J) {
+      if (nu > 0) tile(sc, J);
+      issue(sd, min(J + 3, Jn - 1));
+      DMA_BARRIER(2 * SL);
+    };
+    int J = 0;
+    for (; J + 4 <= Jn; J += 4) {
+      step(ks0, ks3, J);
+      step(ks1, ks0, J + 1);
+      step(ks2, ks1, J + 2);
+      step(ks3, ks2, J + 3);
     }
+    if (J < Jn) step(ks0, ks3, J);
+    if (J + 1 < Jn) step(ks1, ks0, J + 1);
+    if (J + 2 < Jn) step(ks2, ks1, J + 2);
+    // the stages are reused by the next pass: every load has landed and every wave is done
+    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+    __syncthreads();
   }
   __syncthreads();
   // keep bits (forced blocks are added by the compaction) and the optional margins
@@ -993,6 +1052,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
     }
     if (a.margins && J < ncand) a.margins[brow * a.nKB + J] = margin;
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 // ---------------------------------------------------------------------------------------
