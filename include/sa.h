@@ -32,6 +32,9 @@
  *    failure is reported as SA_ERR_DEVICE.
  *  - Supported (v1): head_dim in {64, 128}; block_q in {64, 128}; block_k == 64;
  *    n_q_heads <= 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8}.
+ *  - Sizes: batch, head counts, seq_q and seq_k are at least 1; an empty problem is
+ *    SA_ERR_SHAPE (there is nothing to launch: callers skip the call).  seq_q < 2^30; at most
+ *    8192 key blocks for decode.
  */
 #ifndef SA_H_
 #define SA_H_

@@ -149,3 +149,23 @@ def test_validation_codes(lib):
     args_q4[6] = FAKE
     assert lib.sa_sparse_decode_q4(*args_q4, FAKE, dneed - 1, None) == _lib.SA_ERR_WORKSPACE
     assert lib.sa_workspace_size(_lib.SA_OP_PREFILL, ctypes.byref(s), ctypes.byref(p)) == 0
+
+
+def test_empty_problems_rejected(lib):
+    p, keep = _params(4.0)
+    for field in ("batch", "seq_q", "seq_k", "n_q_heads", "n_kv_heads"):
+        s = _shape()
+        setattr(s, field, 0)
+        assert _est(lib, s, p, ws_bytes=1 << 30) == _lib.SA_ERR_SHAPE, field
+        assert lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(p)) == 0
+    ds = _shape(B=0, N=1000)
+    ds.seq_q = 1
+    dp = _lib.SaDecodeParams()
+    dp.block_k, dp.top_k_blocks, dp.sink_tokens, dp.local_tokens = 64, 8, 32, 256
+    assert lib.sa_sparse_decode(ctypes.byref(ds), ctypes.byref(dp), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, None, None, FAKE, 1 << 30, None) == _lib.SA_ERR_SHAPE
+    # the decode cache is limited to 8192 key blocks
+    big = _shape(B=1, N=8192 * 64 + 1)
+    big.seq_q = 1
+    assert lib.sa_sparse_decode(ctypes.byref(big), ctypes.byref(dp), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, None, None, FAKE, 1 << 30, None) == _lib.SA_ERR_UNSUPPORTED

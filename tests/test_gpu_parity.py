@@ -326,3 +326,41 @@ def test_step_grouping(dev, name, seq, estimator, step):
     plain = sum(r["kept"].size for r in ref.values())
     log(f"  grouped lists ok: entries={entries} (ungrouped {plain}) flips={flips}")
     assert entries > plain
+
+
+@pytest.mark.parametrize("top_p,top_k", [(0.0, 64), (0.5, 8192)])
+def test_decode_max_cache(dev, top_p, top_k):
+    """The largest cache the library takes: 8192 blocks of 64 keys (524288 tokens), fixed K
+    and a top-p budget over every block."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    L = 8192 * 64
+    x = synth.make_decode(batch=1, seq=L, hq=4, hkv=1, head_dim=64, top_k=top_k)
+    log(f"decode max cache L={L} top_p={top_p} K={top_k}")
+    q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=64)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=64, top_k=top_k, sink=32,
+                                   local=256, top_p=top_p)
+    torch.cuda.synchronize()
+    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, 64)
+    np.testing.assert_array_equal(kbar.view(torch.int16).cpu().numpy().view(np.uint16), kbar_ref)
+    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=64, top_k=top_k, sink=32,
+                               local=256, top_p=top_p)
+    s = sel.cpu().numpy()
+    if top_p > 0:
+        used, off, flips = check_topp_selection(s, ref)
+        log(f"  budget {ref[(0, 0)]['budget']} one-off={off} flips={flips}")
+    else:
+        used, flips = {}, 0
+        for (b, g), r in ref.items():
+            got = s[b, g]
+            assert np.all(np.diff(got) > 0)
+            diff = set(got.tolist()) ^ set(r["selected"].tolist())
+            assert diff <= set(r["ambiguous"].tolist()), sorted(diff)
+            flips += len(diff)
+            used[(b, g)] = got
+    O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used, block_k=64)
+    err = np.abs(o.float().cpu().numpy() - O)
+    assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
+    assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
