@@ -25,6 +25,13 @@ Readings (the design notes of the repository list them with their reasons):
   integer dot product; em, el and LSE are evaluated in fp64 from those fp32 values;
 * grouped query heads: the union (max of margins) over the group, as for the pooled form;
   forced blocks, candidates and the ambiguity band are those of ``estimate_rows``.
+
+4-bit variant (``lowbit="mxfp4"``; the pages' estimate is 4-bit): Q rows and K rows are
+quantised to MXFP4 as the OCP Microscaling Formats (MX) v1.0 specification defines it -- per
+block of 32 consecutive head dims a shared power-of-two scale 2^e with e = floor(log2(max|x|))
+- 2 (the largest E2M1 exponent) clamped to [-127, 127], and elements E2M1 = round-to-nearest-
+even of x / 2^e onto {0, 0.5, 1, 1.5, 2, 3, 4, 6} with saturation at 6.  The dot product of
+the dequantised values is exact in fp64; S~ = fp32(fp32(dot) * c).
 """
 from __future__ import annotations
 
@@ -32,6 +39,39 @@ import numpy as np
 
 from .estimate import (AMBIGUITY_BAND, _f64, forced_blocks, quantize_key_tiles, quantize_q8,
                        query_block_rows, softmax_scale)
+
+
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+MX_BLOCK = 32
+
+
+def quantize_mxfp4(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP4 per block of 32 along the last axis.  Returns (values, exps): values are the
+    signed E2M1 numbers [..., d] (before scaling), exps the shared exponents [..., d / 32]
+    (int); the dequantised tensor is values * 2.0 ** exps (repeated over each block)."""
+    x = np.asarray(x, dtype=np.float32)
+    shp = x.shape
+    xb = x.reshape(shp[:-1] + (shp[-1] // MX_BLOCK, MX_BLOCK)).astype(np.float64)
+    amax = np.abs(xb).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))).astype(np.int64) - 2
+    e = np.where(amax > 0, e, -127)
+    e = np.clip(e, -127, 127)
+    y = np.abs(xb) / np.ldexp(1.0, e)[..., None]           # exact: a power-of-two scale
+    # round to nearest on the E2M1 grid, ties to the even code (mantissa bit 0)
+    idx = np.searchsorted(E2M1_GRID, y, side="left")
+    idx = np.clip(idx, 1, len(E2M1_GRID) - 1)
+    lo, hi = E2M1_GRID[idx - 1], E2M1_GRID[idx]
+    d_lo, d_hi = y - lo, hi - y
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((idx % 2) == 0))
+    code = np.where(pick_hi, idx, idx - 1)
+    code = np.where(y >= E2M1_GRID[-1], len(E2M1_GRID) - 1, code)       # saturate at 6
+    vals = np.sign(xb) * E2M1_GRID[code]
+    return vals.reshape(shp), e
+
+
+def dequantize_mxfp4(vals: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    return vals * np.repeat(np.ldexp(1.0, exps), MX_BLOCK, axis=-1)
 
 
 def area_mask(r0: int, r1: int, n_keys: int, sink: int, local: int) -> np.ndarray:
@@ -55,9 +95,11 @@ def relative_scores(s_hat: np.ndarray, r0: int, sink: int, local: int) -> np.nda
 
 def estimate_rows_sale(q, k, theta, *, block_q: int, block_k: int, sink: int, local: int,
                        rows, scale: float | None = None, kv_of_q=None, quantized: bool = True,
-                       keep_margins: bool = True, per_head: bool = False) -> dict:
+                       keep_margins: bool = True, per_head: bool = False,
+                       lowbit: str = "int8") -> dict:
     """Kept block lists of the rows ``rows`` = iterable of (b, g, i) under the element-wise
-    estimate; the result has the layout of ``estimate_rows`` (block granularity)."""
+    estimate; the result has the layout of ``estimate_rows`` (block granularity).  lowbit:
+    "int8" (rows of Q and tiles of K) or "mxfp4" (32-dim blocks of Q and K rows)."""
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     c = softmax_scale(D, scale)
@@ -70,8 +112,11 @@ def estimate_rows_sale(q, k, theta, *, block_q: int, block_k: int, sink: int, lo
     for (b, g, i) in rows:
         if cache_key != (b, g):
             kf = _f64(k[b, :, g, :])
-            kq, sk = quantize_key_tiles(kf, block_k)
-            kq64 = kq.astype(np.float64)
+            if lowbit == "mxfp4":
+                kq64 = dequantize_mxfp4(*quantize_mxfp4(kf.astype(np.float32)))
+            else:
+                kq, sk = quantize_key_tiles(kf, block_k)
+                kq64 = kq.astype(np.float64)
             cache_key = (b, g)
         r0, r1 = query_block_rows(i, N, block_q)
         e = r1 - 1
@@ -81,7 +126,11 @@ def estimate_rows_sale(q, k, theta, *, block_q: int, block_k: int, sink: int, lo
         margins = []
         for h in heads:
             qb = _f64(q[b, r0:r1, h, :])
-            if quantized:
+            if quantized and lowbit == "mxfp4":
+                qd = dequantize_mxfp4(*quantize_mxfp4(qb.astype(np.float32)))
+                dots = kq64[: e + 1] @ qd.T                              # exact in fp64
+                s_hat = (dots.astype(np.float32) * c).astype(np.float32).astype(np.float64)
+            elif quantized:
                 qq, sq = quantize_q8(qb.astype(np.float32), axis=1)      # per query row
                 dots = kq64[: e + 1] @ qq.astype(np.float64).T           # exact integers
                 mult = ((sq[None, :] * sk[tile][:, None]).astype(np.float32) * c).astype(np.float32)
@@ -112,11 +161,12 @@ def estimate_rows_sale(q, k, theta, *, block_q: int, block_k: int, sink: int, lo
 
 
 def estimate_all_sale(q, k, theta, *, block_q, block_k, sink, local, scale=None, kv_of_q=None,
-                      quantized=True, keep_margins=True, per_head=False) -> dict:
+                      quantized=True, keep_margins=True, per_head=False, lowbit="int8") -> dict:
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     nqb = -(-N // block_q)
     rows = [(b, g, i) for b in range(B) for g in range(Hkv) for i in range(nqb)]
     return estimate_rows_sale(q, k, theta, block_q=block_q, block_k=block_k, sink=sink,
                               local=local, rows=rows, scale=scale, kv_of_q=kv_of_q,
-                              quantized=quantized, keep_margins=keep_margins, per_head=per_head)
+                              quantized=quantized, keep_margins=keep_margins, per_head=per_head,
+                              lowbit=lowbit)

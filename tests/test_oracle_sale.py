@@ -17,9 +17,10 @@ import pytest
 
 import oracle
 from oracle.estimate import quantize_key_tiles, quantize_q8
+from oracle.estimate_sale import dequantize_mxfp4, quantize_mxfp4
 
 
-def _brute(q, k, theta, *, block_q, block_k, sink, local, quantized):
+def _brute(q, k, theta, *, block_q, block_k, sink, local, quantized, lowbit="int8"):
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
@@ -29,7 +30,9 @@ def _brute(q, k, theta, *, block_q, block_k, sink, local, quantized):
     for b in range(B):
         for g in range(Hkv):
             kf = k[b, :, g, :].astype(np.float64)
-            if quantized:
+            if quantized and lowbit == "mxfp4":
+                kd = dequantize_mxfp4(*quantize_mxfp4(kf.astype(np.float32)))
+            elif quantized:
                 kq, sk = quantize_key_tiles(kf, block_k)
             for i in range(nqb):
                 r0, r1 = i * block_q, min(N, (i + 1) * block_q)
@@ -38,12 +41,17 @@ def _brute(q, k, theta, *, block_q, block_k, sink, local, quantized):
                     tau = math.exp(-theta[h])
                     for r in range(r0, r1):
                         qr = q[b, r, h, :].astype(np.float64)
-                        if quantized:
+                        if quantized and lowbit == "mxfp4":
+                            qd = dequantize_mxfp4(*quantize_mxfp4(qr.astype(np.float32)[None, :]))[0]
+                        elif quantized:
                             qq, sq = quantize_q8(qr.astype(np.float32)[None, :], axis=1)
                             qi = [int(v) for v in qq[0]]
                         s = []
                         for j in range(r + 1):
-                            if quantized:
+                            if quantized and lowbit == "mxfp4":
+                                dot = sum(qd[t] * kd[j, t] for t in range(D))   # exact
+                                s.append(float(np.float32(np.float32(dot) * np.float32(c))))
+                            elif quantized:
                                 dot = sum(qi[t] * int(kq[j, t]) for t in range(D))
                                 mult = np.float32(np.float32(sq[0] * sk[j // block_k]) * np.float32(c))
                                 s.append(float(np.float32(np.float32(dot) * mult)))
@@ -60,19 +68,19 @@ def _brute(q, k, theta, *, block_q, block_k, sink, local, quantized):
     return out
 
 
-@pytest.mark.parametrize("quantized", [False, True])
+@pytest.mark.parametrize("quantized,lowbit", [(False, "int8"), (True, "int8"), (True, "mxfp4")])
 @pytest.mark.parametrize("seed", [0, 1])
-def test_brute_force_literal_relative_score(quantized, seed):
+def test_brute_force_literal_relative_score(quantized, lowbit, seed):
     rng = np.random.default_rng(seed)
-    B, N, Hq, Hkv, D = 1, 150, 4, 2, 16
+    B, N, Hq, Hkv, D = 1, 150, 4, 2, 32
     q = rng.normal(size=(B, N, Hq, D)).astype(np.float32)
     k = rng.normal(size=(B, N, Hkv, D)).astype(np.float32)
     k[:, 100:103] += 2.5 * q[:, 140:143, ::2]            # a few strong keys
     kw = dict(block_q=32, block_k=16, sink=8, local=40)
     for th in [1.5, 3.0, 4.5]:
         theta = np.array([th, th + 0.7, th - 0.4, th + 0.2])
-        ref = oracle.estimate_all_sale(q, k, theta, quantized=quantized, **kw)
-        bf = _brute(q, k, theta, quantized=quantized, **kw)
+        ref = oracle.estimate_all_sale(q, k, theta, quantized=quantized, lowbit=lowbit, **kw)
+        bf = _brute(q, k, theta, quantized=quantized, lowbit=lowbit, **kw)
         for key, r in ref.items():
             diff = set(r["kept"].tolist()) ^ set(bf[key])
             assert diff <= set(r["ambiguous"].tolist()), (key, th, sorted(diff))
