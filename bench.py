@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense fp4 MFMA
 
 PREFILL = ("llama8b_128k", "llama8b_32k", "stripe_64k")
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_estimate_amd", "csrc", "attn_kernels.hip")
@@ -253,12 +254,14 @@ def bench_prefill(args, dev):
                      "units": f"{kept_units} kept (head, {x.block_q}x{x.block_k} tile) x "
                               f"{flops_per_unit / 1e6:.3f} MFLOP"},
     }
-    if est == "relative":
-        # the element-wise estimate: 2 d int8 ops per causal (row, key) pair and query head
+    if est != "pooled":
+        # the element-wise estimate: 2 d ops per causal (row, key) pair and query head, on
+        # int8 or block-scaled fp4 MFMA
         pairs = float(N) * (N + 1) / 2
         est_ops = 2.0 * D * pairs * Hq * B
-        out["estimate_int8_tops"] = round(est_ops / (est_avg * 1e-3) / 1e12, 1)
-        out["estimate_frac_of_int8_peak"] = round(est_ops / (est_avg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)
+        peak, kind = (PEAK_INT8_TOPS, "int8") if est == "relative" else (PEAK_FP4_TFLOPS, "fp4")
+        out[f"estimate_{kind}_tops"] = round(est_ops / (est_avg * 1e-3) / 1e12, 1)
+        out[f"estimate_frac_of_{kind}_peak"] = round(est_ops / (est_avg * 1e-3) / 1e12 / peak, 4)
     if args.cpu_baseline:
         log("cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline_prefill(x, dense_flops)
@@ -368,8 +371,10 @@ def main():
     ap.add_argument("--kernel", default="attn_block")
     ap.add_argument("--summary", choices=["bf16", "q4"], default="bf16",
                     help="decode: block summaries in bf16 or 4-bit codes + bf16 scales")
-    ap.add_argument("--estimator", choices=["pooled", "relative"], default="pooled",
-                    help="prefill: anchor vs pooled query, or the element-wise relative score")
+    ap.add_argument("--estimator", choices=["pooled", "relative", "relative_mxfp4"],
+                    default="pooled",
+                    help="prefill: anchor vs pooled query, or the element-wise relative score "
+                         "(int8 or MXFP4 operands)")
     ap.add_argument("--step", type=int, default=1,
                     help="prefill: identify query blocks in groups of STEP (AnchorAttention)")
     ap.add_argument("--theta", type=float, default=None,

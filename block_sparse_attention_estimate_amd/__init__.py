@@ -72,7 +72,8 @@ def _prefill_shape(q, k, v=None, o=None) -> _lib.SaShape:
     return s
 
 
-_ESTIMATORS = {"pooled": _lib.SA_EST_POOLED, "relative": _lib.SA_EST_RELATIVE}
+_ESTIMATORS = {"pooled": _lib.SA_EST_POOLED, "relative": _lib.SA_EST_RELATIVE,
+               "relative_mxfp4": _lib.SA_EST_RELATIVE_MXFP4}
 
 
 def _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale, n_q_heads,
@@ -158,7 +159,8 @@ def estimate_mask(q, k, theta, *, block_q=128, block_k=64, sink=32, local=256,
                   stream=None) -> Lists:
     """Estimation pass (sa_estimate_mask).  q [B, N, Hq, d], k [B, N, Hkv, d] bf16 CUDA
     tensors; theta scalar or [Hq] in logit units; estimator "pooled" (anchor vs pooled
-    query) or "relative" (element-wise estimate against the row's sink-local log-sum-exp);
+    query), "relative" (element-wise int8 estimate against the row's sink-local log-sum-exp)
+    or "relative_mxfp4" (the same with MXFP4 operands on the block-scaled fp4 MFMA);
     step > 1 identifies query blocks in groups of `step` (AnchorAttention's step)."""
     lib = _lib.load()
     s = _prefill_shape(q, k)

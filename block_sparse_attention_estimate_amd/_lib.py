@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libsa.so")
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_PARAM, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY, \
     SA_ERR_WORKSPACE, SA_ERR_DEVICE = range(8)
 SA_BLOCK, SA_STRIPE = 0, 1
-SA_EST_POOLED, SA_EST_RELATIVE = 0, 1
+SA_EST_POOLED, SA_EST_RELATIVE, SA_EST_RELATIVE_MXFP4 = 0, 1, 2
 SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE, SA_OP_CALIBRATE = 0, 1, 2, 3
 SA_MAX_Q_HEADS = 128
 

@@ -20,7 +20,8 @@
 //   est_compact       bits | forced, causal -> ascending index lists + counts
 // With the relative-score estimator (SALE) est_anchor_pool and est_score_block are replaced
 // by est_quant_q_rows (int8 query rows) and est_score_rel (element-wise estimate, LSE of the
-// sink-local keys, block max of S~ - LSE + theta, max over the group).
+// sink-local keys, block max of S~ - LSE + theta, max over the group); with MXFP4 operands by
+// est_quant_rows_fp4 (Q and K rows) and est_score_rel_fp4 (block-scaled fp4 MFMA).
 //
 // Floating-point steps that decide an integer (int8 codes, keep bits) use explicit
 // round-to-nearest operations (__fmul_rn, __fdiv_rn, rintf) in the order the oracle uses.
@@ -1056,6 +1057,331 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// MXFP4 relative estimate (the pages' estimate is 4-bit; here the OCP Microscaling v1.0
+// MXFP4 format that the gfx950 block-scaled fp4 MFMA consumes).
+//
+// est_quant_rows_fp4: one thread per 32 head dims of a Q row (which = 0) or a K row (which =
+// 1, rows up to the padded key count; rows past the sequence become zeros).  Shared exponent
+// e = floor(log2 max|x|) - 2 clamped to [-127, 127] (stored as the E8M0 byte e + 127), codes
+// E2M1 of |x| * 2^-e (exact scaling) rounded to nearest with ties to the even code, saturating
+// at 6, sign in bit 3; 32 codes in 16 bytes, dim j of the block in nibble j (low nibble first).
+// ---------------------------------------------------------------------------------------
+SA_DEV unsigned int e2m1_code(float y) {
+  // grid 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 go
+  // to the even code
+  if (y <= 0.25f) return 0u;
+  if (y < 0.75f) return 1u;
+  if (y <= 1.25f) return 2u;
+  if (y < 1.75f) return 3u;
+  if (y <= 2.5f) return 4u;
+  if (y < 3.5f) return 5u;
+  if (y <= 5.0f) return 6u;
+  return 7u;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void est_quant_rows_fp4(EstArgs a, int which) {
+  constexpr int NC = D / 32;                         // blocks per row
+  const int64_t rows = which == 0 ? (int64_t)a.B * a.N * a.Hq : (int64_t)a.B * a.Hkv * a.nKB * 64;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * NC) return;
+  const int c = (int)(t % NC);
+  const int64_t row = t / NC;
+  const uint16_t* src = nullptr;
+  uint8_t* codes;
+  uint8_t* scales;
+  if (which == 0) {                                  // row = (b, token, head): out [B, Hq, N]
+    const int h = (int)(row % a.Hq);
+    const int r = (int)((row / a.Hq) % a.N);
+    const int b = (int)(row / ((int64_t)a.Hq * a.N));
+    src = a.q + b * a.qs0 + (int64_t)r * a.qs1 + h * a.qs2 + c * 32;
+    const int64_t orow = ((int64_t)b * a.Hq + h) * a.N + r;
+    codes = (uint8_t*)a.qr + orow * (D / 2) + c * 16;
+    scales = (uint8_t*)a.sr + orow * NC + c;
+  } else {                                           // row = (b, g, token of the padded tiles)
+    const int r = (int)(row % ((int64_t)a.nKB * 64));
+    const int bg = (int)(row / ((int64_t)a.nKB * 64));
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    if (r < a.N) src = a.k + b * a.ks0 + (int64_t)r * a.ks1 + g * a.ks2 + c * 32;
+    codes = a.k4 + row * (D / 2) + c * 16;
+    scales = a.k4s + row * NC + c;
+  }
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u16x8 u = (u16x8)(0);
+    if (src) u = *(const u16x8*)(src + 8 * j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * j + e] = bf16_bits_to_float(u[e]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  int ex = -127;
+  if (amax > 0.f) ex = max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 129, -127);
+  unsigned int w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    unsigned int code = e2m1_code(ldexpf(fabsf(v[e]), -ex));
+    if (v[e] < 0.f) code |= 8u;
+    w[e >> 3] |= code << (4 * (e & 7));
+  }
+  *(u32x4*)codes = (u32x4){w[0], w[1], w[2], w[3]};
+  *scales = (uint8_t)(ex + 127);
+}
+
+// est_score_rel_fp4: est_score_rel with the dot products on v_mfma_scale_f32_32x32x64
+// (fp4 x fp4, one E8M0 scale per lane = per 32 dims of its row): a lane holds 32 dims (16
+// bytes) of its key row (A) or query row (B) per 64-dim k-step, lane halves taking the two
+// 32-dim blocks, and the MFMA returns the real dot product; S~ = fp32(dot) * c.
+typedef int v8i_ __attribute__((ext_vector_type(8)));
+SA_DEV f32x16 mfma_fp4(i32x4 a, i32x4 b, f32x16 c, int sa, int sb) {
+  const v8i_ av = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  const v8i_ bv = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void est_score_rel_fp4(EstArgs a) {
+  // The host pass only needs this kernel's signature (for its launch stub).
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int S = D / 64;                          // 64-dim k-steps
+  constexpr int CB = D / 2, SB = D / 32;             // code / scale bytes per row
+  extern __shared__ unsigned int mkey[];             // [nKB] best margin key per key block
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
+  const int BG = a.B * a.Hkv;
+  const int bg = blockIdx.x % BG;
+  const int I = a.nQB - 1 - blockIdx.x / BG;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int r0 = I * a.bq;
+  const int e = min(a.N, r0 + a.bq) - 1;
+  const int ncand = e / 64 + 1;
+  for (int j = tid; j < ncand; j += 256) mkey[j] = 0u;
+  __syncthreads();
+  const int SUBS = a.bq / 64;
+  const int U = a.G * SUBS;
+  const uint8_t* kc0 = a.k4 + ((int64_t)bg * a.nKB * 64) * CB;
+  const uint8_t* ksc0 = a.k4s + ((int64_t)bg * a.nKB * 64) * SB;
+  const int sink_last = a.sink > 0 ? (min(a.sink, a.N) - 1) / 64 : -1;
+
+  // key tiles in LDS: 64 code rows (pitch CB + 16: the 16 rows one quarter-wave reads land on
+  // distinct banks), then the 64 rows' scale bytes
+  constexpr int KP = CB + 16;
+  constexpr int CODEB = 64 * KP, TILEB = CODEB + 64 * SB;
+  constexpr int WIN = (TILEB + 1023) / 1024;
+  constexpr int SL = (WIN + 3) / 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks2[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks3[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
+  int s_off[SL];
+  bool s_sc[SL];                                     // wave-uniform: slot copies scale bytes
+#pragma unroll
+  for (int k = 0; k < SL; ++k) {
+    const int o = min(wave + 4 * k, WIN - 1) * 1024 + lane * 16;
+    if (o < CODEB) {
+      const int r = o / KP, c = o % KP;
+      s_off[k] = r * CB + (c < CB ? c : 0);         // pads get a harmless copy
+      s_sc[k] = false;
+    } else {
+      const int so = o - CODEB;
+      s_off[k] = so < 64 * SB ? so : 0;
+      s_sc[k] = true;
+    }
+  }
+  auto issue = [&](unsigned char* st, int J) {
+    const uint8_t* ct = kc0 + (int64_t)J * 64 * CB;
+    const uint8_t* stl = ksc0 + (int64_t)J * 64 * SB;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      const int wdw = wave + 4 * k;
+      __builtin_amdgcn_global_load_lds((s_sc[k] ? stl : ct) + s_off[k],
+                                       LDS_PTR(void, wdw < WIN ? st + wdw * 1024 : kspare), 16, 0, 0);
+    }
+  };
+  const int Jn = ncand;
+
+  for (int u0 = 0; u0 < U; u0 += 8) {
+    const int ua = u0 + 2 * wave;
+    const int nu = max(0, min(2, U - ua));            // 0: this wave only loads and waits
+    i32x4 qf[2][2][S];
+    int qs[2][2][S];
+    float lse[2][2], thv[2];
+    int rowv[2][2], rmin[2], rmax[2];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int u = min(ua + uu, U - 1);
+      const int hg = u / SUBS, sb = u % SUBS;
+      const int h = g * a.G + hg;
+      thv[uu] = a.theta[h];
+      rmin[uu] = r0 + sb * 64;
+      rmax[uu] = min(rmin[uu] + 63, a.N - 1);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = rmin[uu] + nt * 32 + l32;
+        rowv[uu][nt] = row;
+        const int64_t orow = ((int64_t)b * a.Hq + h) * a.N + min(row, a.N - 1);
+        const uint8_t* qp = (const uint8_t*)a.qr + orow * CB + half * 16;
+        const uint8_t* sp = (const uint8_t*)a.sr + orow * SB + half;
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) {
+          qf[uu][nt][s2] = *(const i32x4*)(qp + s2 * 32);
+          qs[uu][nt][s2] = sp[s2 * 2];
+        }
+      }
+    }
+    const bool two = nu == 2;
+    // real dot products of one unit's rows with key rows from `kc` (codes) / `ksc` (scales)
+    auto dots = [&](int uu, const uint8_t* kc, int kpitch, const uint8_t* ksc, f32x16 (*acc)[2]) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (f32x16){};
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const i32x4 kf = *(const i32x4*)(kc + (mt * 32 + l32) * kpitch + (2 * s2 + half) * 16);
+          const int ksv = ksc[(mt * 32 + l32) * SB + 2 * s2 + half];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = mfma_fp4(kf, qf[uu][nt][s2], acc[mt][nt], ksv, qs[uu][nt][s2]);
+        }
+    };
+
+    // 1. LSE over each row's sink and local keys (their tiles, read from global memory)
+    float mr[2][2], sr_[2][2];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        mr[uu][nt] = NEG_INF;
+        sr_[uu][nt] = 0.f;
+      }
+    const int wlo = max(0, min(rmin[0], two ? rmin[1] : rmin[0]) - a.local + 1) / 64;
+    const int whi = nu > 0 ? max(rmax[0], two ? rmax[1] : rmax[0]) / 64 : -1;
+    for (int J = 0; J <= whi; ++J) {
+      if (J > sink_last && J < wlo) J = wlo;           // skip the tiles between the areas
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        if (uu == 1 && !two) break;
+        if (J * 64 > rmax[uu]) continue;
+        f32x16 acc[2][2];
+        dots(uu, kc0 + (int64_t)J * 64 * CB, CB, ksc0 + (int64_t)J * 64 * SB, acc);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int row = rowv[uu][nt];
+          float m_ = mr[uu][nt], s_ = sr_[uu][nt];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+              const bool in = key <= row && key < a.N && (key < a.sink || key >= row - a.local + 1);
+              if (in) {
+                const float v = __fmul_rn(acc[mt][nt][r], a.c);
+                const float mn = fmaxf(m_, v);
+                s_ = s_ * __expf(m_ - mn) + __expf(v - mn);
+                m_ = mn;
+              }
+            }
+          mr[uu][nt] = m_;
+          sr_[uu][nt] = s_;
+        }
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float mo = swap_halves(mr[uu][nt]), so = swap_halves(sr_[uu][nt]);
+        const float mt_ = fmaxf(mr[uu][nt], mo);
+        float st = 0.f;
+        if (mr[uu][nt] > NEG_INF) st += sr_[uu][nt] * __expf(mr[uu][nt] - mt_);
+        if (mo > NEG_INF) st += so * __expf(mo - mt_);
+        lse[uu][nt] = (rowv[uu][nt] < a.N && mt_ > NEG_INF) ? mt_ + logf(st) : __builtin_huge_valf();
+      }
+
+    // 2. every causal key tile: best (S~ - LSE + theta) over the wave's rows and units
+    auto tile = [&](const unsigned char* st, int J) {
+      float best = NEG_INF;
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        if (uu == 1 && !two) break;
+        if (J * 64 > rmax[uu]) continue;
+        f32x16 acc[2][2];
+        dots(uu, st, KP, st + CODEB, acc);
+        const bool need_mask = J * 64 + 63 > rmin[uu] || J * 64 + 63 >= a.N;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int row = rowv[uu][nt];
+          float m = NEG_INF;
+          if (!need_mask) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[mt][nt][r]);
+          } else {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+                if (key <= row && key < a.N) m = fmaxf(m, acc[mt][nt][r]);
+              }
+          }
+          m = fmaxf(m, swap_halves(m));
+          if (m > NEG_INF && row < a.N) best = fmaxf(best, __fmul_rn(m, a.c) - lse[uu][nt] + thv[uu]);
+        }
+      }
+      best = wave_max(best);
+      if (lane == 0 && best > NEG_INF) atomicMax(&mkey[J], float_order_key(best));
+    };
+    issue(ks0, 0);
+    issue(ks1, min(1, Jn - 1));
+    issue(ks2, min(2, Jn - 1));
+    DMA_BARRIER(2 * SL);
+    auto step = [&](const unsigned char* sc, unsigned char* sd, int J) {
+      if (nu > 0) tile(sc, J);
+      issue(sd, min(J + 3, Jn - 1));
+      DMA_BARRIER(2 * SL);
+    };
+    int J = 0;
+    for (; J + 4 <= Jn; J += 4) {
+      step(ks0, ks3, J);
+      step(ks1, ks0, J + 1);
+      step(ks2, ks1, J + 2);
+      step(ks3, ks2, J + 3);
+    }
+    if (J < Jn) step(ks0, ks3, J);
+    if (J + 1 < Jn) step(ks1, ks0, J + 1);
+    if (J + 2 < Jn) step(ks2, ks1, J + 2);
+    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+    __syncthreads();
+  }
+  // keep bits (forced blocks are added by the compaction) and the optional margins
+  const int64_t brow = (int64_t)bg * a.nQB + I;
+  for (int J0 = wave * 64; J0 < a.W * 32; J0 += 256) {
+    const int J = J0 + lane;
+    float margin = NEG_INF;
+    if (J < ncand && mkey[J] != 0u) {
+      const unsigned int k = mkey[J];
+      margin = __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+    }
+    const unsigned long long bal = __ballot(J < ncand && margin >= 0.f);
+    if (lane == 0) {
+      const int w = J0 / 32;
+      a.bits[brow * a.W + w] = (unsigned int)bal;
+      if (w + 1 < a.W) a.bits[brow * a.W + w + 1] = (unsigned int)(bal >> 32);
+    }
+    if (a.margins && J < ncand) a.margins[brow * a.nKB + J] = margin;
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---------------------------------------------------------------------------------------
 // Grouped identification (AnchorAttention's step): the keep bits of every query block of a
 // group of `step` become the OR over the group; the compaction then adds each block's forced
 // entries and keeps its causal candidates only.  One workgroup per (b, g, group).
@@ -1144,6 +1470,17 @@ static void launch_step_or(const EstArgs& a, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream_t s) {
+  if (a.estimator == SA_EST_RELATIVE_MXFP4) {
+    const int64_t qchunks = (int64_t)a.B * a.N * a.Hq * (D / 32);
+    const int64_t kchunks = (int64_t)a.B * a.Hkv * a.nKB * 64 * (D / 32);
+    hipLaunchKernelGGL(est_quant_rows_fp4<D>, dim3((unsigned int)((qchunks + 255) / 256)), dim3(256), 0, s, a, 0);
+    hipLaunchKernelGGL(est_quant_rows_fp4<D>, dim3((unsigned int)((kchunks + 255) / 256)), dim3(256), 0, s, a, 1);
+    hipLaunchKernelGGL(est_score_rel_fp4<D>, dim3(a.B * a.Hkv * a.nQB), dim3(256),
+                       (size_t)a.nKB * sizeof(unsigned int), s, a);
+    launch_step_or(a, s);
+    hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, a.bk);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(est_quant_k<D>, dim3(a.nKB, a.Hkv, a.B), dim3(256), 0, s, a);
   if (a.estimator == SA_EST_RELATIVE) {
     const int64_t rows = (int64_t)a.B * a.N * a.Hq;

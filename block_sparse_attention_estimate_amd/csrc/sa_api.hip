@@ -57,8 +57,10 @@ sa_status check_sparse_params(const sa_shape* s, const sa_sparse_params* p, bool
   if (!p) return SA_ERR_NULL;
   if (need_theta && !p->theta) return SA_ERR_NULL;
   if (p->granularity != SA_BLOCK && p->granularity != SA_STRIPE) return SA_ERR_PARAM;
-  if (p->estimator != SA_EST_POOLED && p->estimator != SA_EST_RELATIVE) return SA_ERR_PARAM;
-  if (p->estimator == SA_EST_RELATIVE && p->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
+  if (p->estimator != SA_EST_POOLED && p->estimator != SA_EST_RELATIVE &&
+      p->estimator != SA_EST_RELATIVE_MXFP4)
+    return SA_ERR_PARAM;
+  if (p->estimator != SA_EST_POOLED && p->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
   if (p->step < 0) return SA_ERR_PARAM;
   if (p->sink_tokens < 0 || p->local_tokens < 1) return SA_ERR_PARAM;
   if (p->block_q != 64 && p->block_q != 128) return SA_ERR_UNSUPPORTED;
@@ -71,7 +73,7 @@ sa_status check_sparse_params(const sa_shape* s, const sa_sparse_params* p, bool
 }
 
 struct EstLayout {
-  size_t kq, sk, qq, sq, abar, bits, qr, sr, total;
+  size_t kq, sk, qq, sq, abar, bits, qr, sr, k4, k4s, total;
   int W;
 };
 
@@ -89,9 +91,15 @@ EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p) {
   L.sq = off;   off = align_up(off + (size_t)B * Hq * nQB * sizeof(float));
   L.abar = off; off = align_up(off + (size_t)B * Hq * nQB * sizeof(float));
   L.bits = off; off = align_up(off + (size_t)B * Hkv * nQB * L.W * sizeof(uint32_t));
-  const size_t rows = p->estimator == SA_EST_RELATIVE ? (size_t)B * Hq * N : 0;
-  L.qr = off;   off = align_up(off + rows * D);
-  L.sr = off;   off = align_up(off + rows * sizeof(float));
+  // relative estimators: int8 query rows + fp32 scales, or MXFP4 query rows (D/2 code bytes
+  // and D/32 scale bytes per row, in the same regions) and MXFP4 key rows
+  const size_t rows = p->estimator != SA_EST_POOLED ? (size_t)B * Hq * N : 0;
+  const bool fp4 = p->estimator == SA_EST_RELATIVE_MXFP4;
+  L.qr = off;   off = align_up(off + rows * (fp4 ? D / 2 : D));
+  L.sr = off;   off = align_up(off + rows * (fp4 ? D / 32 : sizeof(float)));
+  const size_t krows = fp4 ? (size_t)B * Hkv * nKB * 64 : 0;
+  L.k4 = off;   off = align_up(off + krows * D / 2);
+  L.k4s = off;  off = align_up(off + krows * D / 32);
   L.total = off;
   return L;
 }
@@ -240,6 +248,8 @@ sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params
   a.bits = (uint32_t*)(base + L.bits);
   a.qr = (int8_t*)(base + L.qr);
   a.sr = (float*)(base + L.sr);
+  a.k4 = (uint8_t*)(base + L.k4);
+  a.k4s = (uint8_t*)(base + L.k4s);
   a.estimator = params->estimator;
   a.step = params->step;
   a.W = L.W;

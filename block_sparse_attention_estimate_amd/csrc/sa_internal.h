@@ -22,7 +22,9 @@ struct EstArgs {
   uint32_t* bits;          // [B, Hkv, nQB, W] keep bits
   int8_t* qr;              // relative estimator: int8 query rows [B, Hq, N, D]
   float* sr;               // and their scales [B, Hq, N]
-  int estimator;           // SA_EST_POOLED or SA_EST_RELATIVE
+  uint8_t* k4;             // MXFP4 estimator: K codes [B, Hkv, nKB * 64, D / 2]
+  uint8_t* k4s;            // and E8M0 scales [B, Hkv, nKB * 64, D / 32]
+  int estimator;           // SA_EST_POOLED, SA_EST_RELATIVE or SA_EST_RELATIVE_MXFP4
   int step;                // query blocks per identification group (<= 1: none)
   int W;                   // words per bit row
   // outputs

@@ -103,7 +103,13 @@ typedef struct {
  *   keys (theta = -ln tau of SALE's relative score).  Block granularity only
  *   (SA_ERR_UNSUPPORTED for stripes); its workspace also holds the int8 queries
  *   (B * seq * n_q_heads * (head_dim + 4) bytes). */
-enum { SA_EST_POOLED = 0, SA_EST_RELATIVE = 1 };
+enum { SA_EST_POOLED = 0, SA_EST_RELATIVE = 1, SA_EST_RELATIVE_MXFP4 = 2 };
+/* SA_EST_RELATIVE_MXFP4: the relative-score estimate with 4-bit operands (the pages' estimate
+ *   is 4-bit): Q and K rows quantised to MXFP4 as the OCP Microscaling (MX) v1.0
+ *   specification defines it (per 32 head dims a shared scale 2^e, e = floor(log2 max|x|) - 2,
+ *   elements E2M1 round-to-nearest-even, saturating at 6), dot products on the block-scaled
+ *   fp4 MFMA, S~ = fp32(dot) * c.  Block granularity only; the workspace holds the 4-bit rows
+ *   (B * seq * (n_q_heads + n_kv_heads) * (head_dim / 2 + head_dim / 32) bytes and more). */
 
 /* Per-row kept lists (the index set I of Eq. (3)), one row per (batch, KV head, query
  * block), rows ordered (b, g, i).  Row r holds counts[r] ascending key-block ids (block

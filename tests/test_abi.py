@@ -89,8 +89,10 @@ def test_validation_codes(lib):
     pq, keep4 = _params(4.0, bq=96)
     assert _est(lib, s, pq, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
     pe, keep6 = _params(4.0)
-    pe.estimator = 2
+    pe.estimator = 3
     assert _est(lib, s, pe, ws_bytes=need) == _lib.SA_ERR_PARAM
+    pe.estimator, pe.granularity = _lib.SA_EST_RELATIVE_MXFP4, _lib.SA_STRIPE
+    assert _est(lib, s, pe, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
     pe.estimator, pe.granularity = _lib.SA_EST_RELATIVE, _lib.SA_STRIPE
     assert _est(lib, s, pe, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
     pe.granularity = _lib.SA_BLOCK

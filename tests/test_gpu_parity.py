@@ -256,12 +256,15 @@ def test_decode_topp_reduced(dev, batch, seq, hq, hkv, d, top_k, bk, top_p, summ
         f"max|dO|={err.max():.2e}")
 
 
+@pytest.mark.parametrize("estimator", ["relative", "relative_mxfp4"])
 @pytest.mark.parametrize("seq,hq,hkv,d,bq", [(4000, 8, 2, 128, 128), (1500, 16, 2, 128, 128),
                                              (1000, 4, 2, 64, 64), (777, 2, 2, 128, 128),
                                              (2100, 4, 1, 64, 128), (200, 4, 1, 128, 64)])
-def test_relative_estimator_reduced(dev, seq, hq, hkv, d, bq):
-    """SALE's element-wise estimate: lists bit-exact outside the band, margins within 1e-3 of
-    the oracle's, at thetas from forced-only to dense; attention under the oracle's lists."""
+def test_relative_estimator_reduced(dev, seq, hq, hkv, d, bq, estimator):
+    """SALE's element-wise estimate (int8 or MXFP4 operands): lists bit-exact outside the band,
+    margins within 1e-3 of the oracle's, at thetas from forced-only to dense; attention under
+    the oracle's lists."""
+    lowbit = "mxfp4" if estimator == "relative_mxfp4" else "int8"
     import torch
     import block_sparse_attention_estimate_amd as sa
     x = synth.make_prefill("llama8b_32k", seq=seq, hq=hq, hkv=hkv, head_dim=d)
@@ -272,10 +275,10 @@ def test_relative_estimator_reduced(dev, seq, hq, hkv, d, bq):
     base = np.repeat(np.array([4.0, 6.0, 8.0, 5.0] * 8, np.float32)[:hkv], grp)
     for theta in [base, np.full(hq, -np.inf, np.float32), np.full(hq, np.inf, np.float32),
                   base + np.linspace(0, 1, hq, dtype=np.float32)]:
-        log(f"relative N={seq} Hq={hq} Hkv={hkv} d={d} bq={bq} theta={np.unique(theta)[:4]}")
-        lists = sa.estimate_mask(q, k, theta, estimator="relative", margins=True, **kw)
+        log(f"{estimator} N={seq} Hq={hq} Hkv={hkv} d={d} bq={bq} theta={np.unique(theta)[:4]}")
+        lists = sa.estimate_mask(q, k, theta, estimator=estimator, margins=True, **kw)
         torch.cuda.synchronize()
-        ref = oracle.estimate_all_sale(x.q, x.k, theta, **kw)
+        ref = oracle.estimate_all_sale(x.q, x.k, theta, lowbit=lowbit, **kw)
         rows, entries, flips = compare_lists(lists, ref)
         mg = lists.margins.cpu().numpy()
         worst = 0.0
