@@ -30,15 +30,17 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _data(dev, seq=4096, hq=8, hkv=2, d=128):
-    x = synth.make_prefill("llama8b_32k", seed=0, seq=seq, hq=hq, hkv=hkv, head_dim=d)
+def _data(dev, seq=4096, hq=8, hkv=2, d=128, batch=1):
+    x = synth.make_prefill("llama8b_32k", seed=0, seq=seq, hq=hq, hkv=hkv, head_dim=d, batch=batch)
     return x, to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
 
 
-def test_calibrate_wiring(dev):
+@pytest.mark.parametrize("batch,seq", [(1, 4096), (2, 2100)])
+def test_calibrate_wiring(dev, batch, seq):
+    """Err_h = sum over batch, rows and dims of |O - O~| / (batch * rows)."""
     import torch
     import block_sparse_attention_estimate_amd as sa
-    x, q, k, v = _data(dev)
+    x, q, k, v = _data(dev, seq=seq, batch=batch)
     kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
     th, err, hv = sa.calibrate_theta(q, k, v, tau0=0.008, err_bound=0.05, max_halvings=0, **kw)
     assert np.all(hv == 0) and np.all(th == np.float32(-math.log(0.008)))

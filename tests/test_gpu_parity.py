@@ -367,3 +367,37 @@ def test_decode_max_cache(dev, top_p, top_k):
     err = np.abs(o.float().cpu().numpy() - O)
     assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
     assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
+
+
+@pytest.mark.parametrize("name,estimator", [("llama8b_32k", "pooled"), ("stripe_64k", "pooled"),
+                                            ("llama8b_32k", "relative"),
+                                            ("llama8b_32k", "relative_mxfp4")])
+def test_batched_prefill(dev, name, estimator):
+    """Batch 3 with a ragged length: every batch entry's lists and attention against the
+    oracle (the batch strides of every estimate and attention kernel)."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill(name, seq=2100, batch=3, hq=8, hkv=2)
+    theta = np.repeat(np.array([6.0, 11.0] if estimator == "pooled" else [4.0, 6.0],
+                               np.float32), 4)
+    log(f"batched {name} {estimator} B=3 N=2100")
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    lists = sa.estimate_mask(q, k, theta, granularity=x.granularity, estimator=estimator,
+                             **kw)
+    torch.cuda.synchronize()
+    if estimator == "pooled":
+        ref = oracle.estimate_all(x.q, x.k, theta, granularity=x.granularity, **kw)
+    else:
+        ref = oracle.estimate_all_sale(x.q, x.k, theta, lowbit="mxfp4" if "mxfp4" in estimator
+                                       else "int8", **kw)
+    rows, entries, flips = compare_lists(lists, ref)
+    assert {b for (b, _, _) in ref} == {0, 1, 2}
+    nqb = -(-2100 // x.block_q)
+    dl = upload_lists(ref, (3, 2, nqb), dev, x.granularity, lists.stride)
+    o, lse = sa.sparse_prefill(q, k, v, dl, **kw)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_all(x.q, x.k, x.v, lists_from_ref(ref), block_q=x.block_q,
+                                  block_k=x.block_k, granularity=x.granularity)
+    mx, mean, lmax = compare_outputs(o, lse, O, LSE)
+    log(f"  batched ok: entries={entries} flips={flips} max|dO|={mx:.2e}")
