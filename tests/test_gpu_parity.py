@@ -401,3 +401,110 @@ def test_batched_prefill(dev, name, estimator):
                                   block_k=x.block_k, granularity=x.granularity)
     mx, mean, lmax = compare_outputs(o, lse, O, LSE)
     log(f"  batched ok: entries={entries} flips={flips} max|dO|={mx:.2e}")
+
+
+def _packed(dev, *parts):
+    """Tensors [B, N, H_i, d] as views into one [B, N, sum H_i, d] buffer (strided heads)."""
+    import torch
+    full = torch.cat([to_dev(p, dev) for p in parts], dim=2)
+    out, h0 = [], 0
+    for p in parts:
+        out.append(full[:, :, h0:h0 + p.shape[2]])
+        h0 += p.shape[2]
+    return out
+
+
+@pytest.mark.parametrize("granularity", ["block", "stripe"])
+def test_packed_qkv_bit_identical(dev, granularity):
+    """Q, K and V as head slices of one packed buffer (row strides of (Hq + 2 Hkv) d): lists,
+    margins, output and LSE bit-identical to the contiguous tensors."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    name = "llama8b_32k" if granularity == "block" else "stripe_64k"
+    x = synth.make_prefill(name, seq=3000, batch=2, hq=8, hkv=2)
+    theta = np.repeat(np.array([4.0, 11.0], np.float32), 4)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    res = []
+    for packed in (False, True):
+        if packed:
+            q, k, v = _packed(dev, x.q, x.k, x.v)
+            assert not q.is_contiguous()
+        else:
+            q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+        lists = sa.estimate_mask(q, k, theta, granularity=granularity, margins=True, **kw)
+        o, lse = sa.sparse_prefill(q, k, v, lists, **kw)
+        torch.cuda.synchronize()
+        res.append((lists.counts.cpu(), lists.idx.cpu(), lists.margins.cpu(), o.cpu(), lse.cpu()))
+    (c0, i0, m0, o0, l0), (c1, i1, m1, o1, l1) = res
+    assert torch.equal(c0, c1)
+    for r in range(c0.numel()):
+        n = int(c0.view(-1)[r])
+        assert torch.equal(i0.view(-1, i0.shape[-1])[r, :n], i1.view(-1, i1.shape[-1])[r, :n])
+    assert torch.equal(torch.nan_to_num(m0, nan=7.0), torch.nan_to_num(m1, nan=7.0))
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
+
+
+def test_softmax_scale_prefill(dev):
+    """A softmax scale other than 1/sqrt(d), against the oracle (estimate and attention)."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill("llama8b_32k", seq=2100, hq=8, hkv=2)
+    scale = 0.05
+    theta = np.repeat(np.array([2.0, 3.0], np.float32), 4)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    lists = sa.estimate_mask(q, k, theta, softmax_scale=scale, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.estimate_all(x.q, x.k, theta, scale=scale, **kw)
+    rows, entries, flips = compare_lists(lists, ref)
+    dl = upload_lists(ref, (1, 2, -(-2100 // x.block_q)), dev, "block", lists.stride)
+    o, lse = sa.sparse_prefill(q, k, v, dl, softmax_scale=scale, **kw)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_all(x.q, x.k, x.v, lists_from_ref(ref), block_q=x.block_q,
+                                  block_k=x.block_k, scale=scale)
+    compare_outputs(o, lse, O, LSE)
+    ref_rel = oracle.estimate_all_sale(x.q, x.k, theta + 2.0, scale=scale, **kw)
+    lr = sa.estimate_mask(q, k, theta + 2.0, softmax_scale=scale, estimator="relative", **kw)
+    torch.cuda.synchronize()
+    compare_lists(lr, ref_rel)
+
+
+def test_decode_packed_cache_and_scale(dev):
+    """A K/V cache packed as [B, L, 2 Hkv, d] (strided heads) gives bit-identical decode
+    results; a custom softmax scale matches the oracle."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_decode(batch=2, seq=5000, hq=8, hkv=2, head_dim=128, top_k=24)
+    x.cache_len[1] = 4000
+    q = to_dev(x.q, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    outs = []
+    for packed in (False, True):
+        if packed:
+            kc, vc = _packed(dev, x.k_cache, x.v_cache)
+        else:
+            kc, vc = to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+        kbar = sa.build_block_summary(kc, cl, block_k=64)
+        o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=64, top_k=24, sink=32,
+                                       local=256, softmax_scale=0.07)
+        torch.cuda.synchronize()
+        outs.append((kbar.cpu(), o.cpu(), lse.cpu(), sel.cpu()))
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_,
+                           b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_)
+    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, 64)
+    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=64, top_k=24, sink=32,
+                               local=256, scale=0.07)
+    s = outs[1][3].numpy()
+    used = {}
+    for (b, g), r in ref.items():
+        k_ = min(24, -(-int(x.cache_len[b]) // 64))
+        got = s[b, g, :k_]
+        diff = set(got.tolist()) ^ set(r["selected"].tolist())
+        assert diff <= set(r["ambiguous"].tolist()), ((b, g), sorted(diff))
+        used[(b, g)] = got
+    O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used, block_k=64,
+                                     scale=0.07)
+    err = np.abs(outs[1][1].float().numpy() - O)
+    assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
+    assert np.abs(outs[1][2].numpy() - LSE).max() < 1e-2
