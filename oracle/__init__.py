@@ -22,6 +22,8 @@ What it computes, in the pages' order and notation:
   L1 output error against full attention meets a bound (theta = -ln tau).
 * ``estimate_sale`` -- SALE's element-wise low-bit estimate with the relative attention
   score (the row's log-sum-exp over its sink-local area as the reference).
+* ``anchor_state`` -- anchor-state reuse: the attention state over each row's anchor region
+  (sink tokens and causal local window) and the sparse pass that resumes from it.
 
 Parity pins: see ``tests/test_oracle_*.py``.  Every function is pinned by brute force,
 closed forms, invariants or an independent library routine; none is "parity unpinned".
@@ -45,3 +47,4 @@ from .decode import (block_summary, decode_select, decode_attention, quantize_su
 from .diagnostics import pruned_mass_fraction, sparsity_from_kept, sale_log_margin  # noqa: F401
 from .calibrate import full_lists, head_l1_error, calibrate_theta  # noqa: F401
 from .estimate_sale import estimate_rows_sale, estimate_all_sale, relative_scores  # noqa: F401
+from .anchor_state import anchor_region, anchor_state_rows, merge_partials, resume_rows  # noqa: F401
