@@ -171,21 +171,33 @@ def bench_prefill(args, dev):
     stride = None
     if x.granularity == "stripe":
         stride = args.stripe_capacity
+    reuse = args.anchor_reuse
+    if reuse and (est != "pooled" or x.granularity != "block"):
+        raise SystemExit("--anchor-reuse needs the pooled estimator and block lists")
     lists = sa.alloc_lists(q, k, block_q=x.block_q, block_k=x.block_k,
                            granularity=x.granularity, stride=stride)
-    ws = torch.empty(sa.workspace_size(sa.SA_OP_ESTIMATE, q=q, k=k, granularity=x.granularity,
+    op = sa.SA_OP_ESTIMATE_STATE if reuse else sa.SA_OP_ESTIMATE
+    ws = torch.empty(sa.workspace_size(op, q=q, k=k, granularity=x.granularity,
                                        estimator=est, **kw), dtype=torch.uint8, device=dev)
+    state = sa.alloc_anchor_state(q) if reuse else None
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        sa.estimate_mask(q, k, x.theta, granularity=x.granularity, estimator=est,
-                         step=args.step, workspace=ws, out=lists, **kw)
+        if reuse:
+            sa.estimate_mask_anchor_state(q, k, v, x.theta, step=args.step, workspace=ws,
+                                          out=lists, state=state, **kw)
+        else:
+            sa.estimate_mask(q, k, x.theta, granularity=x.granularity, estimator=est,
+                             step=args.step, workspace=ws, out=lists, **kw)
         if ev is not None:
             ev[1].record(stream)
-        sa.sparse_prefill(q, k, v, lists, out=o, lse=False, **kw)
+        if reuse:
+            sa.sparse_prefill_resume(q, k, v, lists, state, out=o, lse=False, **kw)
+        else:
+            sa.sparse_prefill(q, k, v, lists, out=o, lse=False, **kw)
         if ev is not None:
             ev[2].record(stream)
 
@@ -220,6 +232,26 @@ def bench_prefill(args, dev):
         flops_per_unit = 4.0 * x.block_q * D
         density = float(counts.sum() / (cands.sum() * B * Hkv))
     kept_flops = kept_units * flops_per_unit
+    units_desc = f"{kept_units} kept (head, {x.block_q}x{x.block_k} tile) x {flops_per_unit / 1e6:.3f} MFLOP"
+    if reuse:
+        # the resuming pass visits, per 64-row work item, the listed tiles that start before
+        # the item's last row's local window and do not lie inside the sink tokens
+        idx = lists.idx.cpu().numpy().reshape(-1, lists.stride).astype(np.int64)
+        cnt = counts.reshape(-1)
+        valid = np.arange(lists.stride)[None, :] < cnt[:, None]
+        iq = np.tile(np.arange(nqb), B * Hkv)
+        visited = 0
+        for tsub in range(x.block_q // 64):
+            r0 = iq * x.block_q + tsub * 64
+            ok_row = r0 < N
+            cut = np.minimum(r0 + 63, N - 1) - x.local + 1
+            vis = valid & (idx * 64 < cut[:, None]) & (idx * 64 + 63 >= x.sink) & ok_row[:, None]
+            visited += int(vis.sum())
+        kept_units = visited * G                                  # visited (head, 64x64 tile)
+        flops_per_unit = 4.0 * 64 * x.block_k * D
+        kept_flops = kept_units * flops_per_unit
+        units_desc = (f"{kept_units} visited (head, 64x{x.block_k} tile) x "
+                      f"{flops_per_unit / 1e6:.3f} MFLOP (the anchor state covers the rest)")
     dense_flops = 2.0 * N * N * D * Hq * B
     att_avg = float(np.mean(att_ms))
     est_avg = float(np.mean(est_ms))
@@ -239,7 +271,8 @@ def bench_prefill(args, dev):
                                f"seq {N}, block {x.block_q}x{x.block_k}, sink {x.sink}, "
                                f"local {x.local}, {x.granularity}, {est} estimator, theta per "
                                f"query head {sorted(set(np.round(x.theta, 3).tolist()))}" +
-                               (f", step {args.step}" if args.step > 1 else ""),
+                               (f", step {args.step}" if args.step > 1 else "") +
+                               (", anchor-state reuse" if reuse else ""),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_step, 3),
         "estimate_ms": round(est_avg, 3), "attention_ms": round(att_avg, 3),
@@ -249,10 +282,11 @@ def bench_prefill(args, dev):
         "kept_tile_frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(f"{kernel}_{args.workload}_traffic", ATTN_SRC),
-                     "kernel": f"{kernel} (sa_sparse_prefill)",
-                     "units": f"{kept_units} kept (head, {x.block_q}x{x.block_k} tile) x "
-                              f"{flops_per_unit / 1e6:.3f} MFLOP"},
+                     "traffic": None if reuse else
+                                traffic_from_profile(f"{kernel}_{args.workload}_traffic", ATTN_SRC),
+                     "kernel": f"{kernel} (sa_sparse_prefill_resume)" if reuse
+                               else f"{kernel} (sa_sparse_prefill)",
+                     "units": units_desc},
     }
     if est != "pooled":
         # the element-wise estimate: 2 d ops per causal (row, key) pair and query head, on
@@ -375,6 +409,8 @@ def main():
                     default="pooled",
                     help="prefill: anchor vs pooled query, or the element-wise relative score "
                          "(int8 or MXFP4 operands)")
+    ap.add_argument("--anchor-reuse", action="store_true",
+                    help="estimate with the anchor state and resume the prefill from it")
     ap.add_argument("--step", type=int, default=1,
                     help="prefill: identify query blocks in groups of STEP (AnchorAttention)")
     ap.add_argument("--theta", type=float, default=None,

@@ -8,6 +8,9 @@ unbuilt library raises.
 Entry points (same names as the C ABI):
   estimate_mask(q, k, theta, ...)       -> Lists     (sa_estimate_mask)
   sparse_prefill(q, k, v, lists, ...)   -> (o, lse)  (sa_sparse_prefill)
+  estimate_mask_anchor_state(q, k, v, theta, ...) -> (Lists, AnchorState)
+                                                     (sa_estimate_mask_anchor_state)
+  sparse_prefill_resume(q, k, v, lists, state, ...) -> (o, lse)  (sa_sparse_prefill_resume)
   build_block_summary(k_cache, ...)     -> kbar      (sa_build_block_summary)
   sparse_decode(q, k_cache, v_cache, kbar, cache_len, ...) -> (o, lse, selected)
   workspace_size(op, ...)                            (sa_workspace_size)
@@ -21,9 +24,10 @@ import torch
 
 from . import _lib
 from ._lib import (SA_BLOCK, SA_STRIPE, SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE,  # noqa: F401
-                   SA_OP_CALIBRATE, SaError)
+                   SA_OP_CALIBRATE, SA_OP_ESTIMATE_STATE, SaError)
 
-__all__ = ["Lists", "estimate_mask", "sparse_prefill", "build_block_summary",
+__all__ = ["Lists", "AnchorState", "alloc_anchor_state", "estimate_mask", "sparse_prefill",
+           "estimate_mask_anchor_state", "sparse_prefill_resume", "build_block_summary",
            "quantize_block_summary", "sparse_decode", "calibrate_theta", "workspace_size",
            "SaError", "load_library"]
 
@@ -121,11 +125,41 @@ class Lists:
         return bool((self.counts > self.stride).any().item())
 
 
+@dataclass
+class AnchorState:
+    """Attention over each row's anchor region (sink tokens and causal local window):
+    o [B, N, Hq, d] bf16 (normalised) and lse [B, Hq, N] fp32 (natural log)."""
+    o: torch.Tensor
+    lse: torch.Tensor
+
+    def c_struct(self) -> _lib.SaAnchorState:
+        st = _lib.SaAnchorState()
+        st.o = _ptr(self.o)
+        st.lse = _ptr(self.lse)
+        return st
+
+
+def _check_state(st: AnchorState, q) -> None:
+    B, N, Hq, D = q.shape
+    _check_bf16("state.o", st.o, 4)
+    if tuple(st.o.shape) != (B, N, Hq, D) or not st.o.is_contiguous():
+        raise ValueError("state.o must be a contiguous [B, N, Hq, d] tensor")
+    if (not isinstance(st.lse, torch.Tensor) or st.lse.dtype != torch.float32 or not st.lse.is_cuda
+            or tuple(st.lse.shape) != (B, Hq, N) or not st.lse.is_contiguous()):
+        raise ValueError("state.lse must be a contiguous CUDA float32 [B, Hq, N] tensor")
+
+
+def alloc_anchor_state(q) -> AnchorState:
+    B, N, Hq, D = q.shape
+    return AnchorState(torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=q.device),
+                       torch.empty((B, Hq, N), dtype=torch.float32, device=q.device))
+
+
 def workspace_size(op, *, q=None, k=None, block_q=128, block_k=64, sink=32, local=256,
                    granularity="block", theta=None, estimator="pooled", shape=None,
                    decode_params=None) -> int:
     lib = _lib.load()
-    if op in (SA_OP_ESTIMATE, SA_OP_CALIBRATE):
+    if op in (SA_OP_ESTIMATE, SA_OP_CALIBRATE, SA_OP_ESTIMATE_STATE):
         s = _prefill_shape(q, k)
         p, keep = _sparse_params(block_q, block_k, sink, local, granularity,
                                  theta if theta is not None else 0.0, 0.0, q.shape[2], estimator)
@@ -198,6 +232,61 @@ def sparse_prefill(q, k, v, lists: Lists, *, block_q=128, block_k=64, sink=32, l
     _lib.check(lib.sa_sparse_prefill(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                      ctypes.byref(ls), _ptr(o), _ptr(lse_t), _stream(stream)),
                "sa_sparse_prefill")
+    del keep
+    return o, lse_t
+
+
+def estimate_mask_anchor_state(q, k, v, theta, *, block_q=128, block_k=64, sink=32, local=256,
+                               softmax_scale=0.0, margins=False, step=1, workspace=None,
+                               out: Lists | None = None, state: AnchorState | None = None,
+                               stream=None):
+    """Estimation pass with the anchor state (sa_estimate_mask_anchor_state; pooled
+    estimator, block lists).  Returns (lists, state): the lists equal estimate_mask's, and
+    the state holds the attention over each row's anchor region for sparse_prefill_resume."""
+    lib = _lib.load()
+    _check_bf16("v", v, 4)
+    s = _prefill_shape(q, k, v)
+    p, keep = _sparse_params(block_q, block_k, sink, local, "block", theta, softmax_scale,
+                             q.shape[2], "pooled", step)
+    lists = out if out is not None else alloc_lists(q, k, block_q=block_q, block_k=block_k,
+                                                    margins=margins)
+    st = state if state is not None else alloc_anchor_state(q)
+    _check_state(st, q)
+    need = int(lib.sa_workspace_size(SA_OP_ESTIMATE_STATE, ctypes.byref(s), ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ls = lists.c_struct()
+    cs = st.c_struct()
+    _lib.check(lib.sa_estimate_mask_anchor_state(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k),
+                                                 _ptr(v), ctypes.byref(ls), ctypes.byref(cs),
+                                                 _ptr(workspace), workspace.numel(), _stream(stream)),
+               "sa_estimate_mask_anchor_state")
+    del keep
+    return lists, st
+
+
+def sparse_prefill_resume(q, k, v, lists: Lists, state: AnchorState, *, block_q=128, block_k=64,
+                          sink=32, local=256, softmax_scale=0.0, out=None, lse=True, stream=None):
+    """Block-sparse attention that starts from the anchor state and skips each row's anchor
+    region (sa_sparse_prefill_resume).  Returns (o [B, N, Hq, d] bf16, lse [B, Hq, N] fp32 or
+    None)."""
+    lib = _lib.load()
+    _check_bf16("v", v, 4)
+    o = out if out is not None else torch.empty_like(q)
+    s = _prefill_shape(q, k, v, o)
+    p, keep = _sparse_params(block_q, block_k, sink, local, lists.granularity, None,
+                             softmax_scale, q.shape[2])
+    lse_t = None
+    if lse:
+        lse_t = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32,
+                            device=q.device)
+    _check_state(state, q)
+    ls = lists.c_struct()
+    cs = state.c_struct()
+    _lib.check(lib.sa_sparse_prefill_resume(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k),
+                                            _ptr(v), ctypes.byref(ls), ctypes.byref(cs), _ptr(o),
+                                            _ptr(lse_t), _stream(stream)),
+               "sa_sparse_prefill_resume")
     del keep
     return o, lse_t
 

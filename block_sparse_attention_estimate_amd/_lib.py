@@ -15,12 +15,13 @@ SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_PARAM, SA_ERR_UNSUPPORTED, SA_ERR_CAPAC
     SA_ERR_WORKSPACE, SA_ERR_DEVICE = range(8)
 SA_BLOCK, SA_STRIPE = 0, 1
 SA_EST_POOLED, SA_EST_RELATIVE, SA_EST_RELATIVE_MXFP4 = 0, 1, 2
-SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE, SA_OP_CALIBRATE = 0, 1, 2, 3
+SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE, SA_OP_CALIBRATE, SA_OP_ESTIMATE_STATE = 0, 1, 2, 3, 4
 SA_MAX_Q_HEADS = 128
 
 EXPORTED = ("sa_workspace_size", "sa_estimate_mask", "sa_sparse_prefill",
             "sa_build_block_summary", "sa_sparse_decode", "sa_quantize_block_summary",
-            "sa_sparse_decode_q4", "sa_calibrate_theta", "sa_status_string")
+            "sa_sparse_decode_q4", "sa_calibrate_theta", "sa_status_string",
+            "sa_estimate_mask_anchor_state", "sa_sparse_prefill_resume")
 
 
 class SaShape(ctypes.Structure):
@@ -42,6 +43,10 @@ class SaSparseParams(ctypes.Structure):
 class SaLists(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_void_p), ("idx", ctypes.c_void_p),
                 ("stride", ctypes.c_int32), ("margins", ctypes.c_void_p)]
+
+
+class SaAnchorState(ctypes.Structure):
+    _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
 class SaDecodeParams(ctypes.Structure):
@@ -75,6 +80,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sa_sparse_prefill.restype = ctypes.c_int
     lib.sa_sparse_prefill.argtypes = [P(SaShape), P(SaSparseParams), vp, vp, vp, P(SaLists), vp,
                                       vp, vp]
+    lib.sa_estimate_mask_anchor_state.restype = ctypes.c_int
+    lib.sa_estimate_mask_anchor_state.argtypes = [P(SaShape), P(SaSparseParams), vp, vp, vp,
+                                                  P(SaLists), P(SaAnchorState), vp,
+                                                  ctypes.c_size_t, vp]
+    lib.sa_sparse_prefill_resume.restype = ctypes.c_int
+    lib.sa_sparse_prefill_resume.argtypes = [P(SaShape), P(SaSparseParams), vp, vp, vp, P(SaLists),
+                                             P(SaAnchorState), vp, vp, vp]
     lib.sa_build_block_summary.restype = ctypes.c_int
     lib.sa_build_block_summary.argtypes = [P(SaShape), ctypes.c_int32, vp, vp, vp, vp]
     lib.sa_sparse_decode.restype = ctypes.c_int

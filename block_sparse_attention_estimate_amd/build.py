@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsa.so")
-SOURCES = ["sa_api.hip", "est_kernels.hip", "attn_kernels.hip", "decode_kernels.hip", "cal_kernels.hip"]
+SOURCES = ["sa_api.hip", "est_kernels.hip", "attn_kernels.hip", "decode_kernels.hip", "cal_kernels.hip",
+           "anchor_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=fast",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,

@@ -408,7 +408,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_sparse(AttnArgs a) {
 //    k0..k0+3 of dim d0 + i -- exactly the 4 keys the P^T register layout pairs with that lane.
 // ---------------------------------------------------------------------------------------
 
-template <int D, int HPW>
+template <int D, int HPW, bool RESUME>
 __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   // The host pass only needs this kernel's signature (for its launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -468,9 +468,22 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   const __attribute__((address_space(4))) int32_t* list =
       (const __attribute__((address_space(4))) int32_t*)(a.idx + lrow * a.stride);
   int n = min(((const __attribute__((address_space(4))) int32_t*)a.counts)[lrow], a.stride);
-  while (n > 0 && list[n - 1] * 64 > r_last) --n;
+  // Tiles past `cut` hold no key this work item needs: causally masked for every row, or (when
+  // resuming) causally masked or inside every row's local window, which the anchor state holds.
+  const int cut = RESUME ? r_last - a.local + 1 : r_last + 1;
+  while (n > 0 && list[n - 1] * 64 >= cut) --n;
+  if (RESUME) {
+    // leading tiles entirely inside the sink tokens are in every row's anchor region too
+    int first = 0;
+    while (first < n && list[first] * 64 + 63 < a.sink) ++first;
+    list += first;
+    n -= first;
+  }
+  // Tiles from n_main on need a mask: they reach past the first row's diagonal (or, resuming,
+  // into the first row's local window) or past the end of the sequence.
+  const int mlim = RESUME ? r0 - a.local + 1 : r0 + 1;
   int n_main = n;
-  while (n_main > 0 && (list[n_main - 1] * 64 + 63 > r0 || list[n_main - 1] * 64 + 63 >= a.N)) --n_main;
+  while (n_main > 0 && (list[n_main - 1] * 64 + 63 >= mlim || list[n_main - 1] * 64 + 63 >= a.N)) --n_main;
 
   bf16x8 qf[KS];
   {
@@ -536,6 +549,24 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   const float sl2 = a.scale_log2;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+  if (RESUME) {
+    // Start from the anchor state: with its log-sum-exp as the reference point the state is
+    // (m = LSE_A in the log2 domain, l = 1, O^T = O_A); l lives in the half-0 lane of the row.
+    const int rowc = min(row, a.N - 1);
+    const uint16_t* sp = a.st_o + (((int64_t)b * a.N + rowc) * a.Hq + h) * D + half * 4;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x2 w2 = *(const u32x2*)(sp + dm * 32 + 8 * q4);
+        oacc[dm][4 * q4 + 0] = __uint_as_float(w2[0] << 16);
+        oacc[dm][4 * q4 + 1] = __uint_as_float(w2[0] & 0xFFFF0000u);
+        oacc[dm][4 * q4 + 2] = __uint_as_float(w2[1] << 16);
+        oacc[dm][4 * q4 + 3] = __uint_as_float(w2[1] & 0xFFFF0000u);
+      }
+    m_run = a.st_lse[((int64_t)b * a.Hq + h) * a.N + rowc] * 1.4426950408889634f;
+    l_run = half == 0 ? 1.f : 0.f;
+  }
 
   // ---- the phases of a tile ----
   // S^T = K Q^T from the stage at sb
@@ -550,7 +581,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
         sacc[mt] = mfma_bf16(kf, qf[ks], sacc[mt]);
       }
   };
-  // entries of tile t past the diagonal or the end of the sequence
+  // entries of tile t past the diagonal or the end of the sequence (resuming: also those in
+  // the row's anchor region, which the state already holds; the window includes the diagonal)
   auto mask = [&](int t, f32x16* sacc) {
     const int Jb = list[t];
 #pragma unroll
@@ -558,7 +590,9 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = Jb * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
-        if (tok > row || tok >= a.N) sacc[mt][r] = NEG_INF;
+        const bool drop = RESUME ? (tok < a.sink || tok >= row - a.local + 1 || tok >= a.N)
+                                 : (tok > row || tok >= a.N);
+        if (drop) sacc[mt][r] = NEG_INF;
       }
   };
   // P^T of key half mt = exp2(S^T scale - m) in bf16 (pf[2 mt], pf[2 mt + 1]); returns this
@@ -631,7 +665,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
     DMA_BARRIER(SLOTS);
     f32x16 sa[2], sbb[2];
     qk(st0, sa);
-    if (n_main == 0) mask(0, sa);
+    if (n_main == 0 || (RESUME && list[0] * 64 < a.sink)) mask(0, sa);
     auto step = [&](unsigned char* sc, unsigned char* sn, unsigned char* sd, int t,
                     f32x16* cur, f32x16* nxt, bool may_mask) {
       const int jd = list[min(t + 3, n - 1)];
@@ -728,7 +762,10 @@ static hipError_t launch_block(const AttnArgs& a0, hipStream_t s) {
   a.n_hp = a.G / HPW;
   a.total = a.B * a.Hkv * a.n_hp * a.nQB * a.tpb;
   if (a.total == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_block<D, HPW>), dim3(a.total), dim3(128 * HPW), 0, s, a);
+  if (a.st_o)
+    hipLaunchKernelGGL((attn_block<D, HPW, true>), dim3(a.total), dim3(128 * HPW), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_block<D, HPW, false>), dim3(a.total), dim3(128 * HPW), 0, s, a);
   return hipGetLastError();
 }
 

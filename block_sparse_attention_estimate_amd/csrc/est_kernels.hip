@@ -120,83 +120,91 @@ __global__ __launch_bounds__(64 * EST_AP_WAVES) void est_anchor_pool(EstArgs a) 
   __shared__ float qbar_s[8][128];
   __shared__ __attribute__((aligned(1024))) unsigned char kw[MAXROWS * KPITCH];
 
-  // ---- the key rows this query block needs, staged once in LDS for all G heads ----
-  // tiles of 32 keys: the sink tiles [0, ceil(min(sink, r1) / 32)), then the window tiles
-  // from the tile holding max(0, r0 - local + 1) (not below the sink tiles) through r1 - 1
-  const int hi_blk = r1 - 1;
-  const int sink_end = min(a.sink, r1);
-  const int n_sink_t = (sink_end + 31) / 32;
-  const int lo_blk = max(0, r0 - a.local + 1);
-  const int win_start = max((lo_blk / 32) * 32, n_sink_t * 32);
-  const int n_win_t = win_start <= hi_blk ? (hi_blk - win_start) / 32 + 1 : 0;
-  const int n_rows = (n_sink_t + n_win_t) * 32;     // <= MAXROWS for local <= 352, bq <= 128
-  auto tile_start = [&](int t) { return t < n_sink_t ? t * 32 : win_start + (t - n_sink_t) * 32; };
-  {
-    const uint16_t* kb = a.k + b * a.ks0 + g * a.ks2;
-    const int nwin = (n_rows * KPITCH + 1023) / 1024;
-    for (int w = wave; w < nwin; w += NW) {
-      const int o = w * 1024 + lane * 16;
-      const int r = min(o / KPITCH, n_rows - 1), cb = o % KPITCH;
-      const int key = min(tile_start(r / 32) + (r % 32), a.N - 1);
-      __builtin_amdgcn_global_load_lds(kb + (int64_t)key * a.ks1 + (cb < ROWB ? cb / 2 : 0),
-                                       LDS_PTR(void, kw + w * 1024), 16, 0, 0);
+  if (a.xa_ready) {
+    // anchors computed by the anchor-state pass (same MFMA sequence, same values)
+    for (int p = tid; p < G * nrows; p += 64 * NW) {
+      const int hg = p / nrows, rr = p % nrows;
+      xa_s[hg][rr] = a.xa[((int64_t)b * a.Hq + g * G + hg) * a.N + r0 + rr];
     }
-    __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
-    __syncthreads();
-  }
-  const int k_rd = l32 * KPITCH + half * 16;
-
-  // Q fragments of this wave's n-tiles (32 rows of one head each), the next one loaded while
-  // the current one's MFMAs run
-  auto load_q = [&](int nt, bf16x8* qf) {
-    const int hg = nt / ntph, tr = nt % ntph;
-    const int rowc = min(r0 + tr * 32 + l32, a.N - 1);
-    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + (g * G + hg) * a.qs2 + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
-  };
-  bf16x8 qn[KS];
-  if (wave < G * ntph) load_q(wave, qn);
-  for (int nt = wave; nt < G * ntph; nt += NW) {
-    const int hg = nt / ntph, tr = nt % ntph;
-    const int ra = r0 + tr * 32;
-    bf16x8 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
-    if (nt + NW < G * ntph) load_q(nt + NW, qn);
-    if (ra >= r1) continue;
-    const int row = ra + l32;
-    float mx = NEG_INF;
-    const int hi = min(ra + 31, a.N - 1);
-    const int lo = max(0, ra - a.local + 1);
-    // this n-tile's tiles: the sink tiles visible to it, then the window tiles from lo to hi
-    for (int t = 0; t < n_sink_t + n_win_t; ++t) {
-      const int ts = tile_start(t);
-      if (ts > hi) break;                              // tiles ascend; later ones are causal-masked
-      if (t >= n_sink_t && ts + 31 < lo) continue;     // window tile entirely before this window
-      f32x16 acc = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(kw + k_rd + t * 32 * KPITCH + ks * 32);
-        acc = mfma_bf16(kf, qf[ks], acc);
+  } else {
+    // ---- the key rows this query block needs, staged once in LDS for all G heads ----
+    // tiles of 32 keys: the sink tiles [0, ceil(min(sink, r1) / 32)), then the window tiles
+    // from the tile holding max(0, r0 - local + 1) (not below the sink tiles) through r1 - 1
+    const int hi_blk = r1 - 1;
+    const int sink_end = min(a.sink, r1);
+    const int n_sink_t = (sink_end + 31) / 32;
+    const int lo_blk = max(0, r0 - a.local + 1);
+    const int win_start = max((lo_blk / 32) * 32, n_sink_t * 32);
+    const int n_win_t = win_start <= hi_blk ? (hi_blk - win_start) / 32 + 1 : 0;
+    const int n_rows = (n_sink_t + n_win_t) * 32;     // <= MAXROWS for local <= 352, bq <= 128
+    auto tile_start = [&](int t) { return t < n_sink_t ? t * 32 : win_start + (t - n_sink_t) * 32; };
+    {
+      const uint16_t* kb = a.k + b * a.ks0 + g * a.ks2;
+      const int nwin = (n_rows * KPITCH + 1023) / 1024;
+      for (int w = wave; w < nwin; w += NW) {
+        const int o = w * 1024 + lane * 16;
+        const int r = min(o / KPITCH, n_rows - 1), cb = o % KPITCH;
+        const int key = min(tile_start(r / 32) + (r % 32), a.N - 1);
+        __builtin_amdgcn_global_load_lds(kb + (int64_t)key * a.ks1 + (cb < ROWB ? cb / 2 : 0),
+                                         LDS_PTR(void, kw + w * 1024), 16, 0, 0);
       }
-      // a tile whose 32 keys are visible to all 32 rows of this n-tile needs no mask
-      const bool all_sink = ts + 31 < a.sink && ts + 31 <= ra;
-      const bool all_win = ts >= ra + 31 - a.local + 1 && ts + 31 <= ra;
-      if (all_sink || all_win) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
-          const bool ok = key <= row && (key < a.sink || key >= row - a.local + 1);
-          if (ok) mx = fmaxf(mx, acc[r]);
+      __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+      __syncthreads();
+    }
+    const int k_rd = l32 * KPITCH + half * 16;
+
+    // Q fragments of this wave's n-tiles (32 rows of one head each), the next one loaded while
+    // the current one's MFMAs run
+    auto load_q = [&](int nt, bf16x8* qf) {
+      const int hg = nt / ntph, tr = nt % ntph;
+      const int rowc = min(r0 + tr * 32 + l32, a.N - 1);
+      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + (g * G + hg) * a.qs2 + half * 8;
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
+    };
+    bf16x8 qn[KS];
+    if (wave < G * ntph) load_q(wave, qn);
+    for (int nt = wave; nt < G * ntph; nt += NW) {
+      const int hg = nt / ntph, tr = nt % ntph;
+      const int ra = r0 + tr * 32;
+      bf16x8 qf[KS];
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
+      if (nt + NW < G * ntph) load_q(nt + NW, qn);
+      if (ra >= r1) continue;
+      const int row = ra + l32;
+      float mx = NEG_INF;
+      const int hi = min(ra + 31, a.N - 1);
+      const int lo = max(0, ra - a.local + 1);
+      // this n-tile's tiles: the sink tiles visible to it, then the window tiles from lo to hi
+      for (int t = 0; t < n_sink_t + n_win_t; ++t) {
+        const int ts = tile_start(t);
+        if (ts > hi) break;                              // tiles ascend; later ones are causal-masked
+        if (t >= n_sink_t && ts + 31 < lo) continue;     // window tile entirely before this window
+        f32x16 acc = {};
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 kf = *(const bf16x8*)(kw + k_rd + t * 32 * KPITCH + ks * 32);
+          acc = mfma_bf16(kf, qf[ks], acc);
+        }
+        // a tile whose 32 keys are visible to all 32 rows of this n-tile needs no mask
+        const bool all_sink = ts + 31 < a.sink && ts + 31 <= ra;
+        const bool all_win = ts >= ra + 31 - a.local + 1 && ts + 31 <= ra;
+        if (all_sink || all_win) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+        } else {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
+            const bool ok = key <= row && (key < a.sink || key >= row - a.local + 1);
+            if (ok) mx = fmaxf(mx, acc[r]);
+          }
         }
       }
+      mx = fmaxf(mx, swap_halves(mx));
+      if (half == 0 && row < r1) xa_s[hg][row - r0] = __fmul_rn(mx, a.c);
     }
-    mx = fmaxf(mx, swap_halves(mx));
-    if (half == 0 && row < r1) xa_s[hg][row - r0] = __fmul_rn(mx, a.c);
   }
 
   // Pooled query: fp64 sum over the block's rows, one rounding to fp32, fp32 division.
@@ -281,65 +289,73 @@ __global__ __launch_bounds__(256) void est_anchor_pool_gl(EstArgs a) {
   __shared__ float xa_s[8][128];
   __shared__ float qbar_s[8][128];
 
-  for (int nt = wave; nt < G * ntph; nt += 4) {
-    const int hg = nt / ntph, tr = nt % ntph;
-    const int h = g * G + hg;
-    const int ra = r0 + tr * 32;
-    if (ra >= r1) continue;
-    const int row = ra + l32;
-    const int rowc = min(row, a.N - 1);
-    bf16x8 qf[KS];
-    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + h * a.qs2 + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
-    float mx = NEG_INF;
-    const int hi = min(ra + 31, a.N - 1);
-    const int sink_end = min(a.sink, hi + 1);
-    const int sink_tiles_end = ((sink_end + 31) / 32) * 32;
-    const int lo = max(0, ra - a.local + 1);
-    const int win_start = max((lo / 32) * 32, sink_tiles_end);
-    const uint16_t* kb = a.k + b * a.ks0 + g * a.ks2 + half * 8;
-    // key tiles: the sink tiles, then the window tiles; fragments of the next tile are
-    // loaded before the current tile's MFMAs
-    const int n_sink_t = sink_tiles_end / 32;
-    const int n_win_t = win_start <= hi ? (hi - win_start) / 32 + 1 : 0;
-    const int n_t = n_sink_t + n_win_t;
-    auto tile_start = [&](int t) { return t < n_sink_t ? t * 32 : win_start + (t - n_sink_t) * 32; };
-    bf16x8 kf[KS], kn[KS];
-    if (n_t > 0) {
-      const uint16_t* kp = kb + (int64_t)min(tile_start(0) + l32, a.N - 1) * a.ks1;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const bf16x8*)(kp + ks * 16);
+  if (a.xa_ready) {
+    // anchors computed by the anchor-state pass (same MFMA sequence, same values)
+    for (int p = tid; p < G * nrows; p += 256) {
+      const int hg = p / nrows, rr = p % nrows;
+      xa_s[hg][rr] = a.xa[((int64_t)b * a.Hq + g * G + hg) * a.N + r0 + rr];
     }
-    for (int t = 0; t < n_t; ++t) {
-      const int ts = tile_start(t);
-      if (t + 1 < n_t) {
-        const uint16_t* kp = kb + (int64_t)min(tile_start(t + 1) + l32, a.N - 1) * a.ks1;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kn[ks] = *(const bf16x8*)(kp + ks * 16);
+  } else {
+    for (int nt = wave; nt < G * ntph; nt += 4) {
+      const int hg = nt / ntph, tr = nt % ntph;
+      const int h = g * G + hg;
+      const int ra = r0 + tr * 32;
+      if (ra >= r1) continue;
+      const int row = ra + l32;
+      const int rowc = min(row, a.N - 1);
+      bf16x8 qf[KS];
+      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + h * a.qs2 + half * 8;
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
+      float mx = NEG_INF;
+      const int hi = min(ra + 31, a.N - 1);
+      const int sink_end = min(a.sink, hi + 1);
+      const int sink_tiles_end = ((sink_end + 31) / 32) * 32;
+      const int lo = max(0, ra - a.local + 1);
+      const int win_start = max((lo / 32) * 32, sink_tiles_end);
+      const uint16_t* kb = a.k + b * a.ks0 + g * a.ks2 + half * 8;
+      // key tiles: the sink tiles, then the window tiles; fragments of the next tile are
+      // loaded before the current tile's MFMAs
+      const int n_sink_t = sink_tiles_end / 32;
+      const int n_win_t = win_start <= hi ? (hi - win_start) / 32 + 1 : 0;
+      const int n_t = n_sink_t + n_win_t;
+      auto tile_start = [&](int t) { return t < n_sink_t ? t * 32 : win_start + (t - n_sink_t) * 32; };
+      bf16x8 kf[KS], kn[KS];
+      if (n_t > 0) {
+        const uint16_t* kp = kb + (int64_t)min(tile_start(0) + l32, a.N - 1) * a.ks1;
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const bf16x8*)(kp + ks * 16);
       }
-      f32x16 acc = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(kf[ks], qf[ks], acc);
-      // a tile whose 32 keys are visible to all 32 rows of this n-tile needs no mask
-      const bool all_sink = ts + 31 < a.sink && ts + 31 <= ra;
-      const bool all_win = ts >= ra + 31 - a.local + 1 && ts + 31 <= ra;
-      if (all_sink || all_win) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
-          const bool ok = key <= row && (key < a.sink || key >= row - a.local + 1);
-          if (ok) mx = fmaxf(mx, acc[r]);
+      for (int t = 0; t < n_t; ++t) {
+        const int ts = tile_start(t);
+        if (t + 1 < n_t) {
+          const uint16_t* kp = kb + (int64_t)min(tile_start(t + 1) + l32, a.N - 1) * a.ks1;
+  #pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kn[ks] = *(const bf16x8*)(kp + ks * 16);
         }
+        f32x16 acc = {};
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(kf[ks], qf[ks], acc);
+        // a tile whose 32 keys are visible to all 32 rows of this n-tile needs no mask
+        const bool all_sink = ts + 31 < a.sink && ts + 31 <= ra;
+        const bool all_win = ts >= ra + 31 - a.local + 1 && ts + 31 <= ra;
+        if (all_sink || all_win) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+        } else {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
+            const bool ok = key <= row && (key < a.sink || key >= row - a.local + 1);
+            if (ok) mx = fmaxf(mx, acc[r]);
+          }
+        }
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
       }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
+      mx = fmaxf(mx, swap_halves(mx));
+      if (half == 0 && row < r1) xa_s[hg][row - r0] = __fmul_rn(mx, a.c);
     }
-    mx = fmaxf(mx, swap_halves(mx));
-    if (half == 0 && row < r1) xa_s[hg][row - r0] = __fmul_rn(mx, a.c);
   }
 
   // Pooled query: fp64 sum over the block's rows, one rounding to fp32, fp32 division.

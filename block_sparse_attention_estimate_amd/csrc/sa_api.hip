@@ -73,11 +73,12 @@ sa_status check_sparse_params(const sa_shape* s, const sa_sparse_params* p, bool
 }
 
 struct EstLayout {
-  size_t kq, sk, qq, sq, abar, bits, qr, sr, k4, k4s, total;
+  size_t kq, sk, qq, sq, abar, bits, qr, sr, k4, k4s, xa, total;
   int W;
 };
 
-EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p) {
+// with_state: room for the per-row anchors the anchor-state pass hands to the estimate
+EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p, bool with_state = false) {
   EstLayout L{};
   const int N = s->seq_q, D = s->head_dim, B = s->batch, Hkv = s->n_kv_heads, Hq = s->n_q_heads;
   const int nQB = ceil_div(N, p->block_q), nKB = ceil_div(N, p->block_k);
@@ -100,6 +101,7 @@ EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p) {
   const size_t krows = fp4 ? (size_t)B * Hkv * nKB * 64 : 0;
   L.k4 = off;   off = align_up(off + krows * D / 2);
   L.k4s = off;  off = align_up(off + krows * D / 32);
+  L.xa = off;   off = align_up(off + (with_state ? (size_t)B * Hq * N * sizeof(float) : 0));
   L.total = off;
   return L;
 }
@@ -190,10 +192,12 @@ const char* sa_status_string(sa_status st) {
 
 size_t sa_workspace_size(int op, const sa_shape* shape, const void* params) {
   if (!shape || !params) return 0;
-  if (op == SA_OP_ESTIMATE) {
+  if (op == SA_OP_ESTIMATE || op == SA_OP_ESTIMATE_STATE) {
     const sa_sparse_params* p = (const sa_sparse_params*)params;
     if (check_prefill_shape(shape) != SA_OK || check_sparse_params(shape, p, true) != SA_OK) return 0;
-    return est_layout(shape, p).total;
+    if (op == SA_OP_ESTIMATE_STATE && (p->estimator != SA_EST_POOLED || p->granularity != SA_BLOCK))
+      return 0;
+    return est_layout(shape, p, op == SA_OP_ESTIMATE_STATE).total;
   }
   if (op == SA_OP_CALIBRATE) {
     const sa_sparse_params* p = (const sa_sparse_params*)params;
@@ -210,20 +214,30 @@ size_t sa_workspace_size(int op, const sa_shape* shape, const void* params) {
   return 0;
 }
 
-sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params, const void* q,
-                           const void* k, const sa_lists* out, void* ws, size_t ws_bytes,
-                           hipStream_t stream) {
+}  // extern "C"
+
+// The estimate, optionally preceded by the anchor-state pass (v and state non-null).
+static sa_status estimate_impl(const sa_shape* shape, const sa_sparse_params* params, const void* q,
+                               const void* k, const void* v, const sa_lists* out,
+                               const sa_anchor_state* state, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
   sa_status st = check_prefill_shape(shape);
   if (st != SA_OK) return st;
   st = check_sparse_params(shape, params, true);
   if (st != SA_OK) return st;
   if (!q || !k || !out || !out->counts || !out->idx) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k)) return SA_ERR_SHAPE;
+  const bool with_state = state != nullptr;
+  if (with_state) {
+    if (params->estimator != SA_EST_POOLED || params->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
+    if (!v || !state->o || !state->lse) return SA_ERR_NULL;
+    if (!aligned16(v) || !aligned16(state->o) || ((uintptr_t)state->lse & 3u) != 0) return SA_ERR_SHAPE;
+  }
   const int N = shape->seq_q;
   const int nKB = ceil_div(N, params->block_k), nQB = ceil_div(N, params->block_q);
   if (out->stride < 1) return SA_ERR_CAPACITY;
   if (params->granularity == SA_BLOCK && out->stride < nKB) return SA_ERR_CAPACITY;
-  const EstLayout L = est_layout(shape, params);
+  const EstLayout L = est_layout(shape, params, with_state);
   if (!ws) return SA_ERR_WORKSPACE;
   if (ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0) return SA_ERR_WORKSPACE;
 
@@ -258,19 +272,34 @@ sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params
   a.stride = out->stride;
   a.margins = out->margins;
   for (int h = 0; h < a.Hq; ++h) a.theta[h] = params->theta[h];
+  if (with_state) {
+    a.v = (const uint16_t*)v;
+    a.vs0 = shape->v_stride[0]; a.vs1 = shape->v_stride[1]; a.vs2 = shape->v_stride[2];
+    a.st_o = (uint16_t*)state->o;
+    a.st_lse = state->lse;
+    a.xa = (float*)(base + L.xa);
+    a.xa_ready = 1;
+    if (launch_anchor_state(a, stream) != hipSuccess) return SA_ERR_DEVICE;
+  }
   if (launch_estimate(a, params->granularity, stream) != hipSuccess) return SA_ERR_DEVICE;
   return SA_OK;
 }
 
-sa_status sa_sparse_prefill(const sa_shape* shape, const sa_sparse_params* params, const void* q,
-                            const void* k, const void* v, const sa_lists* lists, void* o,
-                            float* lse, hipStream_t stream) {
+// The computation pass, optionally resuming from an anchor state.
+static sa_status prefill_impl(const sa_shape* shape, const sa_sparse_params* params, const void* q,
+                              const void* k, const void* v, const sa_lists* lists,
+                              const sa_anchor_state* state, void* o, float* lse, hipStream_t stream) {
   sa_status st = check_prefill_shape(shape);
   if (st != SA_OK) return st;
   st = check_sparse_params(shape, params, false);
   if (st != SA_OK) return st;
   if (!q || !k || !v || !o || !lists || !lists->counts || !lists->idx) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SA_ERR_SHAPE;
+  if (state) {
+    if (params->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
+    if (!state->o || !state->lse) return SA_ERR_NULL;
+    if (!aligned16(state->o) || ((uintptr_t)state->lse & 3u) != 0) return SA_ERR_SHAPE;
+  }
   const int N = shape->seq_q;
   const int nKB = ceil_div(N, params->block_k), nQB = ceil_div(N, params->block_q);
   if (lists->stride < 1) return SA_ERR_CAPACITY;
@@ -289,9 +318,45 @@ sa_status sa_sparse_prefill(const sa_shape* shape, const sa_sparse_params* param
   a.G = a.Hq / a.Hkv; a.N = N; a.bq = params->block_q; a.nQB = nQB;
   a.tpb = params->block_q / 64;
   a.scale_log2 = resolve_scale(params->softmax_scale, shape->head_dim) * 1.4426950408889634f;
+  if (state) {
+    a.st_o = (const uint16_t*)state->o;
+    a.st_lse = state->lse;
+    a.sink = params->sink_tokens;
+    a.local = params->local_tokens;
+  }
   if (launch_prefill(a, shape->head_dim, params->granularity, stream) != hipSuccess)
     return SA_ERR_DEVICE;
   return SA_OK;
+}
+
+extern "C" {
+
+sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params, const void* q,
+                           const void* k, const sa_lists* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  return estimate_impl(shape, params, q, k, nullptr, out, nullptr, ws, ws_bytes, stream);
+}
+
+sa_status sa_estimate_mask_anchor_state(const sa_shape* shape, const sa_sparse_params* params,
+                                        const void* q, const void* k, const void* v,
+                                        const sa_lists* out, const sa_anchor_state* state, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  if (!state) return SA_ERR_NULL;
+  return estimate_impl(shape, params, q, k, v, out, state, ws, ws_bytes, stream);
+}
+
+sa_status sa_sparse_prefill(const sa_shape* shape, const sa_sparse_params* params, const void* q,
+                            const void* k, const void* v, const sa_lists* lists, void* o,
+                            float* lse, hipStream_t stream) {
+  return prefill_impl(shape, params, q, k, v, lists, nullptr, o, lse, stream);
+}
+
+sa_status sa_sparse_prefill_resume(const sa_shape* shape, const sa_sparse_params* params,
+                                   const void* q, const void* k, const void* v,
+                                   const sa_lists* lists, const sa_anchor_state* state, void* o,
+                                   float* lse, hipStream_t stream) {
+  if (!state) return SA_ERR_NULL;
+  return prefill_impl(shape, params, q, k, v, lists, state, o, lse, stream);
 }
 
 static void fill_dec_args(DecArgs& a, const sa_shape* s, int block_k) {

@@ -27,6 +27,13 @@ struct EstArgs {
   int estimator;           // SA_EST_POOLED, SA_EST_RELATIVE or SA_EST_RELATIVE_MXFP4
   int step;                // query blocks per identification group (<= 1: none)
   int W;                   // words per bit row
+  // anchor-state reuse (null / 0 otherwise)
+  const uint16_t* v;       // values, read by the anchor-state pass
+  int64_t vs0, vs1, vs2;
+  uint16_t* st_o;          // [B, N, Hq, D] bf16 normalised output over each row's anchor region
+  float* st_lse;           // [B, Hq, N] its log-sum-exp (natural log)
+  float* xa;               // [B, Hq, N] per-row anchors c * max q.k (workspace)
+  int xa_ready;            // 1: the anchor pass reads xa instead of computing it
   // outputs
   int32_t* counts;
   int32_t* idx;
@@ -48,6 +55,11 @@ struct AttnArgs {
   int B, Hq, Hkv, G, N, bq, nQB, tpb, n_hp;
   float scale_log2;
   int total;
+  // resuming from an anchor state (null otherwise): the sparse pass skips each row's anchor
+  // region A(r) = {j <= r : j < sink or j >= r - local + 1} and starts from its output
+  const uint16_t* st_o;    // [B, N, Hq, D] bf16
+  const float* st_lse;     // [B, Hq, N] natural log
+  int sink, local;
 };
 
 struct DecArgs {
@@ -71,6 +83,7 @@ struct DecArgs {
 };
 
 hipError_t launch_estimate(const EstArgs& a, int granularity, hipStream_t s);
+hipError_t launch_anchor_state(const EstArgs& a, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs& a, int D, int granularity, hipStream_t s);
 hipError_t launch_block_summary(const DecArgs& a, hipStream_t s);
 hipError_t launch_summary_q4(const uint16_t* ksum, uint8_t* codes, uint16_t* scales, int64_t n_groups,

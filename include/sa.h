@@ -59,7 +59,8 @@ typedef enum {
 } sa_status;
 
 enum { SA_BLOCK = 0, SA_STRIPE = 1 };
-enum { SA_OP_ESTIMATE = 0, SA_OP_PREFILL = 1, SA_OP_DECODE = 2, SA_OP_CALIBRATE = 3 };
+enum { SA_OP_ESTIMATE = 0, SA_OP_PREFILL = 1, SA_OP_DECODE = 2, SA_OP_CALIBRATE = 3,
+       SA_OP_ESTIMATE_STATE = 4 };
 
 #define SA_MAX_Q_HEADS 128
 
@@ -141,8 +142,9 @@ typedef struct {
   float top_p;
 } sa_decode_params;
 
-/* Workspace bytes an operation needs (op = SA_OP_ESTIMATE or SA_OP_CALIBRATE with
- * sa_sparse_params, or SA_OP_DECODE with sa_decode_params; SA_OP_PREFILL needs none).
+/* Workspace bytes an operation needs (op = SA_OP_ESTIMATE, SA_OP_ESTIMATE_STATE or
+ * SA_OP_CALIBRATE with sa_sparse_params, or SA_OP_DECODE with sa_decode_params;
+ * SA_OP_PREFILL needs none).
  * Returns 0 for an invalid request. */
 size_t sa_workspace_size(int op, const sa_shape* shape, const void* params);
 
@@ -173,6 +175,44 @@ sa_status sa_estimate_mask(const sa_shape* shape, const sa_sparse_params* params
 sa_status sa_sparse_prefill(const sa_shape* shape, const sa_sparse_params* params /* theta unused, may be NULL */,
                             const void* q, const void* k, const void* v,
                             const sa_lists* lists, void* o, float* lse, hipStream_t stream);
+
+/* Anchor-state reuse (AnchorAttention, "What carries the argument": the anchor kernel's
+ * intermediates are kept for the sparse kernel; referee major comment 1: per query row the
+ * anchor kernel holds the running max M and the p.V accumulator Acc; referee minor comment 2:
+ * the sparse loop starts past the initial block, which the anchor covers).  The state of row r
+ * of query head h is the softmax attention over its anchor region
+ * A(r) = {j <= r : j < sink or j >= r - local + 1} (the token set of Eq. (1)'s max), kept as
+ *   o   device bf16 [B, seq, Hq, d], contiguous: the normalised output over A(r), i.e. Acc / l;
+ *   lse device fp32 [B, Hq, seq]: its log-sum-exp, natural log (M + ln l).
+ * Both buffers are owned by the caller (B * seq * Hq * (2 d + 4) bytes). */
+typedef struct {
+  void* o;
+  float* lse;
+} sa_anchor_state;
+
+/* sa_estimate_mask (pooled estimator, block granularity only; SA_ERR_UNSUPPORTED otherwise)
+ * preceded by the anchor-state pass: one bf16 MFMA online softmax over each row's anchor
+ * region writes `state` and hands the per-row anchors x_a (the same MFMA sequence, so the
+ * same values and the same lists as sa_estimate_mask) to the estimate.  v: device bf16
+ * [B, seq, Hkv, d] (v_stride).  ws: at least sa_workspace_size(SA_OP_ESTIMATE_STATE, ...)
+ * bytes (the estimate's workspace plus B * seq * Hq * 4 bytes of anchors). */
+sa_status sa_estimate_mask_anchor_state(const sa_shape* shape, const sa_sparse_params* params,
+                                        const void* q, const void* k, const void* v,
+                                        const sa_lists* out, const sa_anchor_state* state,
+                                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* sa_sparse_prefill resuming from an anchor state (block granularity only): row r starts
+ * from state (o, lse) and adds the listed tokens j <= r outside A(r) (sink_tokens and
+ * local_tokens of params define A(r); they and softmax_scale must be the ones the state was
+ * made with); tiles of the list that lie wholly inside every row's anchor region are
+ * skipped.  The result is the
+ * attention over A(r) and the listed causal tokens, which for lists of the estimate (they
+ * hold the forced blocks, a superset of A(r)) is sa_sparse_prefill's result.  o, lse as in
+ * sa_sparse_prefill; the state is read only. */
+sa_status sa_sparse_prefill_resume(const sa_shape* shape, const sa_sparse_params* params,
+                                   const void* q, const void* k, const void* v,
+                                   const sa_lists* lists, const sa_anchor_state* state, void* o,
+                                   float* lse, hipStream_t stream);
 
 /* Block summaries for decode (SALE "The reading": one representative per key block):
  * kbar[b, J, g, :] = mean of the cached keys of block J (fp64 sum and divide, rounded to

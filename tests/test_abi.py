@@ -171,3 +171,45 @@ def test_empty_problems_rejected(lib):
     big.seq_q = 1
     assert lib.sa_sparse_decode(ctypes.byref(big), ctypes.byref(dp), FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, None, None, FAKE, 1 << 30, None) == _lib.SA_ERR_UNSUPPORTED
+
+
+def test_anchor_state_validation(lib):
+    s = _shape()
+    p, keep = _params(4.0)
+    need = lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(p))
+    need_st = lib.sa_workspace_size(_lib.SA_OP_ESTIMATE_STATE, ctypes.byref(s), ctypes.byref(p))
+    assert need_st >= need + 4 * 256 * 4                 # + one fp32 anchor per (head, row)
+    ls = _lib.SaLists()
+    ls.counts, ls.idx, ls.stride, ls.margins = FAKE, FAKE, 4, None
+    st = _lib.SaAnchorState()
+    st.o, st.lse = FAKE, FAKE
+
+    def est(state=ctypes.byref(st), v=FAKE, ws_bytes=need_st, pp=p):
+        return lib.sa_estimate_mask_anchor_state(ctypes.byref(s), ctypes.byref(pp), FAKE, FAKE, v,
+                                                 ctypes.byref(ls), state, FAKE, ws_bytes, None)
+
+    assert est(state=None) == _lib.SA_ERR_NULL
+    assert est(v=None) == _lib.SA_ERR_NULL
+    assert est(ws_bytes=need_st - 1) == _lib.SA_ERR_WORKSPACE
+    st.lse = FAKE + 2                                     # fp32 buffer not 4-byte aligned
+    assert est() == _lib.SA_ERR_SHAPE
+    st.lse = None
+    assert est() == _lib.SA_ERR_NULL
+    st.lse = FAKE
+    pr, keep2 = _params(4.0)
+    pr.estimator = _lib.SA_EST_RELATIVE
+    assert est(pp=pr) == _lib.SA_ERR_UNSUPPORTED
+    assert lib.sa_workspace_size(_lib.SA_OP_ESTIMATE_STATE, ctypes.byref(s), ctypes.byref(pr)) == 0
+    pst, keep3 = _params(4.0, gran=_lib.SA_STRIPE)
+    assert est(pp=pst) == _lib.SA_ERR_UNSUPPORTED
+    # resume validation
+    def resume(state=ctypes.byref(st), pp=p):
+        return lib.sa_sparse_prefill_resume(ctypes.byref(s), ctypes.byref(pp), FAKE, FAKE, FAKE,
+                                            ctypes.byref(ls), state, FAKE, None, None)
+    assert resume(state=None) == _lib.SA_ERR_NULL
+    assert resume(pp=pst) == _lib.SA_ERR_UNSUPPORTED
+    st.o = FAKE + 8
+    assert resume() == _lib.SA_ERR_SHAPE
+    st.o = FAKE
+    ls.stride = 3
+    assert resume() == _lib.SA_ERR_CAPACITY

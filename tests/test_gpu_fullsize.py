@@ -22,7 +22,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled"):
+def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled", reuse=False):
     import torch
     import block_sparse_attention_estimate_amd as sa
     log(f"generating {name}")
@@ -34,9 +34,13 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled
     q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
     kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
     stride = 8192 if x.granularity == "stripe" else None
-    lists = sa.estimate_mask(q, k, x.theta, granularity=x.granularity, stride=stride,
-                             estimator=estimator, **kw)
-    o, lse = sa.sparse_prefill(q, k, v, lists, **kw)
+    if reuse:
+        lists, st = sa.estimate_mask_anchor_state(q, k, v, x.theta, **kw)
+        o, lse = sa.sparse_prefill_resume(q, k, v, lists, st, **kw)
+    else:
+        lists = sa.estimate_mask(q, k, x.theta, granularity=x.granularity, stride=stride,
+                                 estimator=estimator, **kw)
+        o, lse = sa.sparse_prefill(q, k, v, lists, **kw)
     torch.cuda.synchronize()
     assert not lists.overflowed()
     rng = np.random.default_rng(seed + 7)
@@ -88,6 +92,20 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled
     log(f"  attention: max|dO|={err.max():.2e} mean={err.mean():.2e} max|dLSE|={lerr.max():.2e}")
     assert err.max() < MAX_ABS and err.mean() < MEAN_ABS and lerr.max() < 1e-2
     assert flips <= max(2, entries // 1000)
+    if reuse:
+        sref = oracle.anchor_state_rows(x.q, x.k, x.v, block_q=x.block_q, sink=x.sink,
+                                        local=x.local, rows=arows)
+        so = st.o.float().cpu().numpy()
+        sl = st.lse.cpu().numpy()
+        e1, e2 = [], []
+        for (b, h, i), (oa, la) in sref.items():
+            r0 = i * x.block_q
+            r1 = min(N, r0 + x.block_q)
+            e1.append(np.abs(so[b, r0:r1, h, :] - oa).ravel())
+            e2.append(np.abs(sl[b, h, r0:r1] - la))
+        e1, e2 = np.concatenate(e1), np.concatenate(e2)
+        log(f"  anchor state: max|dO|={e1.max():.2e} mean={e1.mean():.2e} max|dLSE|={e2.max():.2e}")
+        assert e1.max() < MAX_ABS and e1.mean() < MEAN_ABS and e2.max() < 1e-2
 
 
 def test_llama8b_32k_every_row(dev):
@@ -102,6 +120,12 @@ def test_llama8b_32k_relative_sampled(dev):
 
 def test_llama8b_128k_sampled(dev):
     _prefill_parity(dev, "llama8b_128k", n_rows=40, n_attn=12)
+
+
+@pytest.mark.parametrize("name", ["llama8b_32k", "llama8b_128k"])
+def test_anchor_reuse_sampled(dev, name):
+    """Anchor-state reuse in the launch configuration bench.py --anchor-reuse times."""
+    _prefill_parity(dev, name, n_rows=24, n_attn=10, reuse=True)
 
 
 def test_stripe_64k_sampled(dev):

@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import (check_topp_selection, compare_lists, compare_outputs, log, lists_from_ref,
+from helpers import (MAX_ABS, MEAN_ABS, check_topp_selection, compare_lists, compare_outputs, log,
+                     lists_from_ref,
                      oracle_estimate_for, to_dev, upload_lists)
 
 pytestmark = pytest.mark.gpu
@@ -508,3 +509,80 @@ def test_decode_packed_cache_and_scale(dev):
     err = np.abs(outs[1][1].float().numpy() - O)
     assert err.max() < 2e-2 and err.mean() < 2e-3, (err.max(), err.mean())
     assert np.abs(outs[1][2].numpy() - LSE).max() < 1e-2
+
+
+@pytest.mark.parametrize("seq,hq,hkv,d,bq,sink,local", [
+    (3000, 8, 2, 128, 128, 32, 256),     # the workloads' sink and window, ragged tail
+    (1000, 4, 2, 64, 64, 32, 256),
+    (777, 2, 2, 128, 128, 100, 64),      # sink past one key block, window under one block
+    (1500, 8, 1, 128, 128, 0, 300),      # no sink; 8 heads per KV head (two rounds per block)
+    (900, 4, 1, 64, 128, 5, 600),        # regions of up to 800 rows (four staged chunks)
+    (65, 4, 1, 128, 128, 32, 256),       # one query block, ragged
+])
+def test_anchor_state_reduced(dev, seq, hq, hkv, d, bq, sink, local):
+    """Anchor-state reuse: the estimate with the state gives the plain estimate's lists bit for
+    bit, the state matches the oracle's attention over each row's anchor region, and the
+    resuming prefill under the oracle's lists matches attention over those lists."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill("llama8b_32k", seq=seq, hq=hq, hkv=hkv, head_dim=d)
+    x.block_q, x.sink, x.local = bq, sink, local
+    B, N, Hq, D = x.q.shape
+    grp = hq // hkv
+    theta = np.repeat(np.array([2.0, 3.0, 4.0, 6.0] * 8, np.float32)[:hkv], grp)
+    log(f"anchor state N={N} Hq={Hq} Hkv={hkv} d={D} bq={bq} sink={sink} local={local}")
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=bq, block_k=64, sink=sink, local=local)
+    plain = sa.estimate_mask(q, k, theta, **kw)
+    lists, st = sa.estimate_mask_anchor_state(q, k, v, theta, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.counts, lists.counts)
+    c = plain.counts.cpu().numpy().reshape(-1)
+    i0 = plain.idx.cpu().numpy().reshape(c.size, -1)
+    i1 = lists.idx.cpu().numpy().reshape(c.size, -1)
+    for r in range(c.size):
+        assert np.array_equal(i0[r, :c[r]], i1[r, :c[r]])
+    ref = oracle_estimate_for(x, theta)
+    rows_l, entries, flips = compare_lists(lists, ref)
+    nqb = -(-N // bq)
+    rows = [(0, h, i) for h in range(Hq) for i in range(nqb)]
+    sref = oracle.anchor_state_rows(x.q, x.k, x.v, block_q=bq, sink=sink, local=local, rows=rows)
+    so = st.o.float().cpu().numpy()
+    sl = st.lse.cpu().numpy()
+    errs, lerrs = [], []
+    for (b, h, i), (oa, la) in sref.items():
+        r0, r1 = i * bq, min(N, (i + 1) * bq)
+        errs.append(np.abs(so[b, r0:r1, h, :] - oa).ravel())
+        lerrs.append(np.abs(sl[b, h, r0:r1] - la))
+    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
+    log(f"  lists equal the plain estimate ({rows_l} rows, {flips} ambiguous flips vs oracle); "
+        f"state max|dO|={err.max():.2e} mean={err.mean():.2e} max|dLSE|={lerr.max():.2e}")
+    assert err.max() < MAX_ABS and err.mean() < MEAN_ABS and lerr.max() < 1e-2
+    dl = upload_lists(ref, (B, hkv, nqb), dev, "block", lists.stride)
+    o, lse = sa.sparse_prefill_resume(q, k, v, dl, st, **kw)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_all(x.q, x.k, x.v, lists_from_ref(ref), block_q=bq, block_k=64)
+    mx, mean, lmax = compare_outputs(o, lse, O, LSE)
+    log(f"  resumed attention ok: max|dO|={mx:.2e} mean={mean:.2e} max|dLSE|={lmax:.2e}")
+
+
+def test_anchor_state_resume_without_rest(dev):
+    """Lists of only the forced blocks with local >= N and no sink: every listed causal token is
+    in the anchor region, so the resumed prefill returns the state itself."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill("llama8b_32k", seq=700, hq=4, hkv=1, head_dim=128)
+    N = 700
+    kw = dict(block_q=128, block_k=64, sink=0, local=N)
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    lists, st = sa.estimate_mask_anchor_state(q, k, v, -np.inf, **kw)
+    o, lse = sa.sparse_prefill_resume(q, k, v, lists, st, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), st.o.view(torch.int16))
+    assert torch.allclose(lse, st.lse, rtol=0, atol=1e-5)
+    # and the state is dense causal attention here
+    O, LSE = oracle.attention_all(x.q, x.k, x.v, {(0, 0, i): np.arange(-(-min(N, (i + 1) * 128) // 64))
+                                                  for i in range(-(-N // 128))},
+                                  block_q=128, block_k=64)
+    mx, mean, lmax = compare_outputs(o, lse, O, LSE)
+    log(f"  state = dense causal attention: max|dO|={mx:.2e} mean={mean:.2e} max|dLSE|={lmax:.2e}")
