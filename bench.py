@@ -36,9 +36,9 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile(name, src):
-    """HBM bytes per launch recorded in profiles/<name>.txt, or None when missing or taken
-    on a different kernel source."""
+def traffic_from_profile(name, src, key="hbm_bytes_per_launch"):
+    """A figure recorded in profiles/<name>.txt (HBM bytes per launch by default), or None
+    when missing or taken on a different kernel source."""
     path = os.path.join(PROFILES, name + ".txt")
     if not os.path.exists(path):
         return None
@@ -50,7 +50,7 @@ def traffic_from_profile(name, src):
     if kv.get("kernel_source_sha256_16") != source_hash(src):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -91,6 +91,67 @@ def summarize_pmc(fetch_dir, write_dir, kernel, workload, src, command):
              f"fetch_scale: {f_scale:.4f}",
              f"write_scale: {w_scale:.4f}",
              f"hbm_bytes_per_launch: {total:.0f}"]
+    return "\n".join(lines)
+
+
+def _pmc_values(d, counter, kernel):
+    """Per-dispatch values of `counter` for dispatches whose name contains `kernel`, from the
+    counter_collection CSVs of a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_mfma(util_dir, raw_dir, kernel, workload, src, command):
+    """MFMA counters of `kernel`: the derived MfmaUtil (MFMA-busy cycles summed over SIMDs over
+    GPU-active cycles times the SIMD count) from one pass, and the bf16 / int8 MFMA operation
+    counts (units of 512 flops) and busy cycles from another."""
+    util = _pmc_values(util_dir, "MfmaUtil", kernel)
+    mops = _pmc_values(raw_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kernel)
+    mops8 = _pmc_values(raw_dir, "SQ_INSTS_VALU_MFMA_MOPS_I8", kernel)
+    busy = _pmc_values(raw_dir, "SQ_VALU_MFMA_BUSY_CYCLES", kernel)
+    avg = lambda v: sum(v) / len(v) if v else float("nan")
+    lines = [f"# MFMA counters of {kernel} on {workload}",
+             f"command: {command}",
+             f"kernel_source_sha256_16: {source_hash(src)}",
+             f"dispatches: util {len(util)}, raw {len(mops)}",
+             f"mfma_util_percent: {avg(util):.2f}",
+             f"mfma_bf16_flops_per_dispatch: {avg(mops) * 512:.4e}",
+             f"mfma_i8_ops_per_dispatch: {avg(mops8) * 512:.4e}",
+             f"mfma_busy_cycles_sum_over_simds: {avg(busy):.4e}"]
+    return "\n".join(lines)
+
+
+def summarize_kernels(fetch_dir, write_dir, stats_csv, kernels, workload, command):
+    """Per-kernel HBM bytes (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the same counters
+    on the calibration copy) over the kernel's average duration from a kernel-trace run."""
+    import csv
+    dur = {}
+    for r in csv.DictReader(open(stats_csv)):
+        dur[r["Name"]] = float(r["AverageNs"])
+    fc = max(_pmc_values(fetch_dir, "FETCH_SIZE", "copyBuffer") or [float("nan")])
+    wc = max(_pmc_values(write_dir, "WRITE_SIZE", "copyBuffer") or [float("nan")])
+    fs, ws = COPY_BYTES / (fc * 1024.0), COPY_BYTES / (wc * 1024.0)
+    lines = [f"# HBM bytes and achieved GB/s per kernel on {workload}",
+             f"command: {command}",
+             f"fetch_scale: {fs:.4f}  write_scale: {ws:.4f}  (1 GiB copy calibration)",
+             f"{'kernel':44s} {'fetch_MB':>10s} {'write_MB':>10s} {'avg_us':>10s} {'GB/s':>8s}"]
+    for k in kernels:
+        f = _pmc_values(fetch_dir, "FETCH_SIZE", k)
+        w = _pmc_values(write_dir, "WRITE_SIZE", k)
+        if not f or not w:
+            continue
+        fb = sum(f) / len(f) * 1024.0 * fs
+        wb = sum(w) / len(w) * 1024.0 * ws
+        names = [n for n in dur if k in n]
+        us = dur[names[0]] / 1e3 if names else float("nan")
+        lines.append(f"{k:44s} {fb / 1e6:10.1f} {wb / 1e6:10.1f} {us:10.1f} "
+                     f"{(fb + wb) / (us * 1e3):8.0f}")
     return "\n".join(lines)
 
 
@@ -284,6 +345,9 @@ def bench_prefill(args, dev):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if reuse else
                                 traffic_from_profile(f"{kernel}_{args.workload}_traffic", ATTN_SRC),
+                     "mfma_util_percent_counter": None if reuse else
+                                traffic_from_profile(f"{kernel}_{args.workload}_mfma", ATTN_SRC,
+                                                     "mfma_util_percent"),
                      "kernel": f"{kernel} (sa_sparse_prefill_resume)" if reuse
                                else f"{kernel} (sa_sparse_prefill)",
                      "units": units_desc},
@@ -402,6 +466,11 @@ def main():
                     help="after timing, run one plain 1 GiB device copy (byte-counter scale)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("UTIL_DIR", "RAW_DIR"),
+                    help="print the MFMA counter summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-kernels", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_CSV"),
+                    help="print per-kernel HBM bytes and GB/s for --kernels and exit")
+    ap.add_argument("--kernels", default="est_quant_k,est_anchor_pool,est_score_block,est_compact")
     ap.add_argument("--kernel", default="attn_block")
     ap.add_argument("--summary", choices=["bf16", "q4"], default="bf16",
                     help="decode: block summaries in bf16 or 4-bit codes + bf16 scales")
@@ -428,6 +497,14 @@ def main():
     if args.summarize_pmc:
         src = DEC_SRC if args.kernel.startswith("dec_") else ATTN_SRC
         print(summarize_pmc(*args.summarize_pmc, args.kernel, args.workload, src, args.command))
+        return
+    if args.summarize_mfma:
+        src = DEC_SRC if args.kernel.startswith("dec_") else ATTN_SRC
+        print(summarize_mfma(*args.summarize_mfma, args.kernel, args.workload, src, args.command))
+        return
+    if args.summarize_kernels:
+        print(summarize_kernels(*args.summarize_kernels, args.kernels.split(","), args.workload,
+                                args.command))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the workload "
