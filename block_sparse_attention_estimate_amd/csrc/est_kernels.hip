@@ -583,17 +583,19 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
 // ballot that holds, per row pair, the keep bits of 32 consecutive columns.
 // Workgroup = 4 waves x 64 rows, 32 key tiles of 64 columns.
 // ---------------------------------------------------------------------------------------
-template <int D, bool MARGINS>
-__global__ __launch_bounds__(256) void est_score_stripe(EstArgs a, int n_rt, int n_jc) {
+template <int D, int G, bool MARGINS>
+__global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, int n_jc) {
+  // The host pass only needs this kernel's signature (for its launch stub).
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KS = D / 32;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
   const int lin = blockIdx.x;
   const int jc = lin % n_jc;
   const int rt = (lin / n_jc) % n_rt;
   const int bg = lin / (n_jc * n_rt);
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int G = a.G;
-  const int rows_total = a.nQB * G;
+  const int g = bg % a.Hkv;
+  const int rows_total = a.nQB * G;                    // G: query heads per KV head (1, 2, 4, 8)
   const int R_last = min(rt * 128 + 127, rows_total - 1);
   const int e_last = min(a.N, (R_last / G + 1) * a.bq) - 1;
   const int J0 = jc * 32;
@@ -601,149 +603,174 @@ __global__ __launch_bounds__(256) void est_score_stripe(EstArgs a, int n_rt, int
   const int J_end = min(J0 + 32, e_last / 64 + 1);
   const int64_t row_base = (int64_t)bg * a.nQB * G;
   const int Rw = rt * 128 + wave * 32;                  // first row of this wave
-  if (Rw >= rows_total) return;
+  const bool wave_live = Rw < rows_total;               // waves past the rows only stage keys
 
-  // A operand: pooled query rows Rw + mt*32 + l32
-  i32x4 qf[1][KS];
-  for (int mt = 0; mt < 1; ++mt) {
-    const int Rc = min(Rw + mt * 32 + l32, rows_total - 1);
+  // A operand: pooled query rows Rw + l32
+  i32x4 qf[KS];
+  {
+    const int Rc = min(Rw + l32, rows_total - 1);
     const int8_t* qp = a.qq + (row_base + Rc) * D + half * 16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[mt][ks] = *(const i32x4*)(qp + ks * 32);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const i32x4*)(qp + ks * 32);
   }
-  // Per-register row data: register r of m-tile mt holds row Rw + mt*32 + half*4 + 8(r/4) + r%4
-  float thr[1][16], sqv[1][16];
-  int erow[1][16];
+  // Per-register row data: register r holds row Rw + half*4 + 8(r/4) + r%4; rows past the end
+  // never pass (threshold +inf)
+  float thr[16], sqv[16];
 #pragma unroll
-  for (int mt = 0; mt < 1; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int R = Rw + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
-      const int Rc = min(R, rows_total - 1);
-      const int hg = Rc % G;
-      thr[mt][r] = a.abar[row_base + Rc] - a.theta[g * G + hg];
-      sqv[mt][r] = a.sq[row_base + Rc];
-      erow[mt][r] = R < rows_total ? min(a.N, (Rc / G + 1) * a.bq) - 1 : -1;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int R = Rw + half * 4 + 8 * (r >> 2) + (r & 3);
+    const int Rc = min(R, rows_total - 1);
+    thr[r] = R < rows_total ? a.abar[row_base + Rc] - a.theta[g * G + Rc % G] : __builtin_huge_valf();
+    sqv[r] = a.sq[row_base + Rc];
+  }
+  // last causal key of row R's query block (-1 past the rows)
+  auto erow = [&](int R) { return R < rows_total ? min(a.N, (R / G + 1) * a.bq) - 1 : -1; };
   const int e_min = min(a.N, (Rw / G + 1) * a.bq) - 1;
-  // rows past the end never pass: their threshold is +inf
+
+  // K tiles go HBM -> LDS with direct loads into four stages shared by the four waves (rows
+  // padded to D + 16 bytes, so the 16 rows one quarter-wave reads land on distinct banks)
+  constexpr int KP = D + 16;
+  constexpr int WIN = (64 * KP + 1023) / 1024;       // 1 KB windows per tile
+  constexpr int SL = (WIN + 3) / 4;                   // windows per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks2[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks3[WIN * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D;
+  int s_off[SL];                                      // byte offset in a tile of this lane's 16 bytes
 #pragma unroll
-  for (int mt = 0; mt < 1; ++mt)
+  for (int k = 0; k < SL; ++k) {
+    const int o = min(wave + 4 * k, WIN - 1) * 1024 + lane * 16;
+    const int r = min(o / KP, 63), c = o % KP;
+    s_off[k] = r * D + (c < D ? c : 0);               // pads and the tail get a harmless copy
+  }
+  auto issue = [&](unsigned char* st, int J) {
+    const int8_t* tb = kbase + (int64_t)J * 64 * D;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (erow[mt][r] < 0) thr[mt][r] = __builtin_huge_valf();
-  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
-  i32x4 kf[2][KS], kn[2][KS];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+    for (int k = 0; k < SL; ++k) {
+      const int wdw = wave + 4 * k;
+      __builtin_amdgcn_global_load_lds(tb + s_off[k], LDS_PTR(void, wdw < WIN ? st + wdw * 1024 : kspare), 16, 0, 0);
+    }
+  };
+  const int k_rd = l32 * KP + half * 16;
+
+  // one key tile: D = qbar K^T on int8 MFMA (a lane owns one key column and 16 rows), then one
+  // compare per element, turned into keep-bit words by wave ballots
+  auto tile = [&](const unsigned char* st, int J) {
+    i32x16 acc[2] = {(i32x16){}, (i32x16){}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kf[nt][ks] = *(const i32x4*)(kbase + (int64_t)(J0 * 64 + nt * 32 + l32) * D + ks * 32);
-  for (int J = J0; J < J_end; ++J) {
-    if (J + 1 < J_end) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kn[nt][ks] = *(const i32x4*)(kbase + (int64_t)((J + 1) * 64 + nt * 32 + l32) * D + ks * 32);
-    }
-    i32x16 acc[1][2];
-#pragma unroll
-    for (int mt = 0; mt < 1; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (i32x16){};
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mt = 0; mt < 1; ++mt) acc[mt][nt] = mfma_i8(qf[mt][ks], kf[nt][ks], acc[mt][nt]);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[nt][ks] = kn[nt][ks];
+      for (int nt = 0; nt < 2; ++nt) {
+        const i32x4 kf = *(const i32x4*)(st + k_rd + nt * 32 * KP + ks * 32);
+        acc[nt] = mfma_i8(qf[ks], kf, acc[nt]);
+      }
     const float skv = a.sk[(int64_t)bg * a.nKB + J];
     // keep <=> fp32(fp32(D) * m) - (abar - theta) >= 0 <=> fp32(fp32(D) * m) >= (abar - theta)
-    float mult[1][16];
+    float mult[16];
 #pragma unroll
-    for (int mt = 0; mt < 1; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mult[mt][r] = __fmul_rn(__fmul_rn(sqv[mt][r], skv), a.c);
+    for (int r = 0; r < 16; ++r) mult[r] = __fmul_rn(__fmul_rn(sqv[r], skv), a.c);
     const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int key = J * 64 + nt * 32 + l32;
       const int wi = J * 2 + nt;                         // bit word of columns [key - l32, +32)
+      // register r = 4*ag + bb is row Rw + half*4 + 8*ag + bb
 #pragma unroll
-      for (int mt = 0; mt < 1; ++mt) {
-        // register r = 4*ag + bb of this m-tile is row Rw + mt*32 + half*4 + 8*ag + bb
+      for (int ag = 0; ag < 4; ++ag) {
+        unsigned long long bal[4];
 #pragma unroll
-        for (int ag = 0; ag < 4; ++ag) {
-          unsigned long long bal[4];
+        for (int bb = 0; bb < 4; ++bb) {
+          const int r = 4 * ag + bb;
+          const float y = __fmul_rn((float)acc[nt][r], mult[r]);
+          bool keep = y >= thr[r];
+          if (need_mask) keep = keep && key <= erow(Rw + half * 4 + 8 * ag + bb);
+          bal[bb] = __ballot(keep);
+        }
+        const int Rg = Rw + 8 * ag;                      // first row of this 8-row group
+        if (lane == 0) {
+          if (G <= 4) {
+            // G consecutive rows (same half) form one query block: OR their ballots
+            unsigned long long word = 0ull;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              word |= bal[bb];
+              if (((bb + 1) % G) == 0) {
+                const int R_lo = Rg + bb + 1 - G, R_hi = R_lo + 4;
+                if (R_lo < rows_total) a.bits[(row_base / G + R_lo / G) * a.W + wi] = (unsigned int)word;
+                if (R_hi < rows_total) a.bits[(row_base / G + R_hi / G) * a.W + wi] = (unsigned int)(word >> 32);
+                word = 0ull;
+              }
+            }
+          } else {
+            // G == 8: rows Rg .. Rg+7 (both halves) are one query block
+            const unsigned long long word = bal[0] | bal[1] | bal[2] | bal[3];
+            if (Rg < rows_total)
+              a.bits[(row_base / G + Rg / G) * a.W + wi] = (unsigned int)word | (unsigned int)(word >> 32);
+          }
+        }
+        if (MARGINS) {
+          // diagnostic output: max over the group's heads of score - (anchor - theta)
+          float mv[4];
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
             const int r = 4 * ag + bb;
-            const float y = __fmul_rn((float)acc[mt][nt][r], mult[mt][r]);
-            bool keep = y >= thr[mt][r];
-            if (need_mask) keep = keep && key <= erow[mt][r];
-            bal[bb] = __ballot(keep);
+            const int er = erow(Rw + half * 4 + 8 * ag + bb);
+            float m = __fmul_rn((float)acc[nt][r], mult[r]) - thr[r];
+            if (key > er || er < 0) m = NEG_INF;
+            mv[bb] = m;
           }
-          const int Rg = Rw + mt * 32 + 8 * ag;        // first row of this 8-row group
-          if (lane == 0) {
-            if (G <= 4) {
-              // G consecutive rows (same half) form one query block: OR their ballots
-              unsigned long long word = 0ull;
-#pragma unroll
-              for (int bb = 0; bb < 4; ++bb) {
-                word |= bal[bb];
-                if (((bb + 1) % G) == 0) {
-                  const int R_lo = Rg + bb + 1 - G, R_hi = R_lo + 4;
-                  if (R_lo < rows_total) a.bits[(row_base / G + R_lo / G) * a.W + wi] = (unsigned int)word;
-                  if (R_hi < rows_total) a.bits[(row_base / G + R_hi / G) * a.W + wi] = (unsigned int)(word >> 32);
-                  word = 0ull;
-                }
-              }
-            } else {
-              // G == 8: rows Rg .. Rg+7 (both halves) are one query block
-              const unsigned long long word = bal[0] | bal[1] | bal[2] | bal[3];
-              if (Rg < rows_total)
-                a.bits[(row_base / G + Rg / G) * a.W + wi] = (unsigned int)word | (unsigned int)(word >> 32);
-            }
-          }
-          if (MARGINS) {
-            // diagnostic output: max over the group's heads of score - (anchor - theta)
-            float mv[4];
+          if (G <= 4) {
+            float mg = NEG_INF;
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
-              const int r = 4 * ag + bb;
-              float m = __fmul_rn((float)acc[mt][nt][r], mult[mt][r]) - thr[mt][r];
-              if (key > erow[mt][r] || erow[mt][r] < 0) m = NEG_INF;
-              mv[bb] = m;
-            }
-            if (G <= 4) {
-              float mg = NEG_INF;
-#pragma unroll
-              for (int bb = 0; bb < 4; ++bb) {
-                mg = fmaxf(mg, mv[bb]);
-                if (((bb + 1) % G) == 0) {
-                  const int b0 = bb + 1 - G;
-                  const int R = Rg + half * 4 + b0;
-                  if (R < rows_total && key <= erow[mt][4 * ag + b0])
-                    a.margins[((int64_t)bg * a.nQB + R / G) * a.N + key] = mg;
-                  mg = NEG_INF;
-                }
+              mg = fmaxf(mg, mv[bb]);
+              if (((bb + 1) % G) == 0) {
+                const int b0 = bb + 1 - G;
+                const int R = Rg + half * 4 + b0;
+                if (R < rows_total && key <= erow(R))
+                  a.margins[((int64_t)bg * a.nQB + R / G) * a.N + key] = mg;
+                mg = NEG_INF;
               }
-            } else {
-              float mg = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));
-              mg = fmaxf(mg, swap_halves(mg));
-              if (half == 0 && Rg < rows_total && key <= erow[mt][4 * ag])
-                a.margins[((int64_t)bg * a.nQB + Rg / G) * a.N + key] = mg;
             }
+          } else {
+            float mg = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));
+            mg = fmaxf(mg, swap_halves(mg));
+            if (half == 0 && Rg < rows_total && key <= erow(Rg))
+              a.margins[((int64_t)bg * a.nQB + Rg / G) * a.N + key] = mg;
           }
         }
       }
     }
+  };
+
+  // Tile J0 + j is in stage j % 4; tiles j+1 and j+2 are loaded or in flight.  Step j
+  // computes tile j, issues tile j+3 (clamped to the last tile, so every wave issues SL loads
+  // per step) into the stage of tile j-1 and waits until tile j+1 has landed.
+  const int nt_ = J_end - J0;
+  issue(ks0, J0);
+  issue(ks1, J0 + min(1, nt_ - 1));
+  issue(ks2, J0 + min(2, nt_ - 1));
+  DMA_BARRIER(2 * SL);
+  auto step = [&](const unsigned char* sc, unsigned char* sd, int j) {
+    if (wave_live) tile(sc, J0 + j);
+    issue(sd, J0 + min(j + 3, nt_ - 1));
+    DMA_BARRIER(2 * SL);
+  };
+  int j = 0;
+  for (; j + 4 <= nt_; j += 4) {
+    step(ks0, ks3, j);
+    step(ks1, ks0, j + 1);
+    step(ks2, ks1, j + 2);
+    step(ks3, ks2, j + 3);
   }
+  if (j < nt_) step(ks0, ks3, j);
+  if (j + 1 < nt_) step(ks1, ks0, j + 1);
+  if (j + 2 < nt_) step(ks2, ks1, j + 2);
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1521,12 +1548,22 @@ static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream
   if (granularity == SA_STRIPE) {
     const int n_rt_s = (rows_total + 127) / 128;
     // the instance without the diagnostic margins output keeps its registers for the hot loop
-    if (a.margins)
-      hipLaunchKernelGGL((est_score_stripe<D, true>), dim3(a.B * a.Hkv * n_rt_s * n_jc), dim3(256), 0,
-                         s, a, n_rt_s, n_jc);
-    else
-      hipLaunchKernelGGL((est_score_stripe<D, false>), dim3(a.B * a.Hkv * n_rt_s * n_jc), dim3(256), 0,
-                         s, a, n_rt_s, n_jc);
+    const dim3 sgrid(a.B * a.Hkv * n_rt_s * n_jc);
+#define SA_STRIPE_LAUNCH(GG)                                                                  \
+  if (a.margins)                                                                              \
+    hipLaunchKernelGGL((est_score_stripe<D, GG, true>), sgrid, dim3(256), 0, s, a, n_rt_s, n_jc); \
+  else                                                                                        \
+    hipLaunchKernelGGL((est_score_stripe<D, GG, false>), sgrid, dim3(256), 0, s, a, n_rt_s, n_jc);
+    if (a.G == 1) {
+      SA_STRIPE_LAUNCH(1)
+    } else if (a.G == 2) {
+      SA_STRIPE_LAUNCH(2)
+    } else if (a.G == 4) {
+      SA_STRIPE_LAUNCH(4)
+    } else {
+      SA_STRIPE_LAUNCH(8)
+    }
+#undef SA_STRIPE_LAUNCH
     launch_step_or(a, s);
     hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, 1);
   } else {

@@ -586,3 +586,56 @@ def test_anchor_state_resume_without_rest(dev):
                                   block_q=128, block_k=64)
     mx, mean, lmax = compare_outputs(o, lse, O, LSE)
     log(f"  state = dense causal attention: max|dO|={mx:.2e} mean={mean:.2e} max|dLSE|={lmax:.2e}")
+
+
+def test_anchor_state_batched_packed_scale(dev):
+    """Anchor-state reuse with batch 3, a ragged length, Q/K/V as head slices of one packed
+    buffer and a custom softmax scale: state and resumed output against the oracle, and both
+    bit-identical to the run on contiguous tensors."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill("llama8b_32k", seq=2100, batch=3, hq=8, hkv=2)
+    N, Hq = 2100, 8
+    theta = np.repeat(np.array([6.0, 11.0], np.float32), 4)
+    scale = 0.07
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local,
+              softmax_scale=scale)
+    log("anchor state B=3 N=2100 packed, scale 0.07")
+    res = []
+    for packed in (False, True):
+        if packed:
+            q, k, v = _packed(dev, x.q, x.k, x.v)
+            assert not q.is_contiguous()
+        else:
+            q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+        lists, st = sa.estimate_mask_anchor_state(q, k, v, theta, **kw)
+        o, lse = sa.sparse_prefill_resume(q, k, v, lists, st, **kw)
+        torch.cuda.synchronize()
+        res.append((lists, st, o, lse))
+    (l0, s0, o0, e0), (l1, s1, o1, e1) = res
+    assert torch.equal(l0.counts, l1.counts)
+    assert torch.equal(s0.o.view(torch.int16), s1.o.view(torch.int16)) and torch.equal(s0.lse, s1.lse)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(e0, e1)
+    ekw = {key: val for key, val in kw.items() if key != "softmax_scale"}
+    ref = oracle.estimate_all(x.q, x.k, theta, granularity="block", scale=scale, **ekw)
+    compare_lists(l0, ref)
+    nqb = -(-N // x.block_q)
+    rows = [(b, h, i) for b in range(3) for h in range(Hq) for i in range(nqb)]
+    sref = oracle.anchor_state_rows(x.q, x.k, x.v, block_q=x.block_q, sink=x.sink, local=x.local,
+                                    rows=rows, scale=scale)
+    so, sl = s0.o.float().cpu().numpy(), s0.lse.cpu().numpy()
+    err = max(float(np.abs(so[b, i * 128:min(N, i * 128 + 128), h, :] - oa).max())
+              for (b, h, i), (oa, la) in sref.items())
+    lerr = max(float(np.abs(sl[b, h, i * 128:min(N, i * 128 + 128)] - la).max())
+               for (b, h, i), (oa, la) in sref.items())
+    assert err < MAX_ABS and lerr < 1e-2
+    # resumed output (the GPU's lists, which match the oracle's outside the band) vs the plain
+    # definition over those lists
+    counts = l0.counts.cpu().numpy()
+    idx = l0.idx.cpu().numpy()
+    glists = {(b, g, i): idx[b, g, i, :counts[b, g, i]] for b in range(3) for g in range(2)
+              for i in range(nqb)}
+    O, LSE = oracle.attention_all(x.q, x.k, x.v, glists, block_q=x.block_q, block_k=x.block_k,
+                                  scale=scale)
+    mx, mean, lmax = compare_outputs(o0, e0, O, LSE)
+    log(f"  state max|dO|={err:.2e}; resumed max|dO|={mx:.2e} mean={mean:.2e} max|dLSE|={lmax:.2e}")
