@@ -293,7 +293,9 @@ def bench_prefill(args, dev):
         flops_per_unit = 4.0 * x.block_q * D
         density = float(counts.sum() / (cands.sum() * B * Hkv))
     kept_flops = kept_units * flops_per_unit
-    units_desc = f"{kept_units} kept (head, {x.block_q}x{x.block_k} tile) x {flops_per_unit / 1e6:.3f} MFLOP"
+    unit_name = f"(head, {x.block_q}x{x.block_k} tile)" if x.granularity == "block" else \
+        f"(head, {x.block_q}-row column)"
+    units_desc = f"{kept_units} kept {unit_name} x {flops_per_unit / 1e6:.3f} MFLOP"
     if reuse:
         # the resuming pass visits, per 64-row work item, the listed tiles that start before
         # the item's last row's local window and do not lie inside the sink tokens
@@ -319,7 +321,7 @@ def bench_prefill(args, dev):
     achieved = kept_flops / (att_avg * 1e-3) / 1e12
     per_group = (counts.sum(axis=(0, 2)) / (cands.sum() * B)).round(4).tolist()
     # the attention kernel the library launches for these lists
-    kernel = "attn_block" if x.granularity == "block" else "attn_sparse"
+    kernel = "attn_block"
     out = {
         "metric": "ms/layer & dense-equiv TFLOP/s (fraction of MFMA peak) for sparse prefill @128K",
         "value": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),

@@ -318,6 +318,7 @@ static sa_status prefill_impl(const sa_shape* shape, const sa_sparse_params* par
   a.G = a.Hq / a.Hkv; a.N = N; a.bq = params->block_q; a.nQB = nQB;
   a.tpb = params->block_q / 64;
   a.scale_log2 = resolve_scale(params->softmax_scale, shape->head_dim) * 1.4426950408889634f;
+  a.stripe = params->granularity == SA_STRIPE;
   if (state) {
     a.st_o = (const uint16_t*)state->o;
     a.st_lse = state->lse;

@@ -60,6 +60,7 @@ struct AttnArgs {
   const uint16_t* st_o;    // [B, N, Hq, D] bf16
   const float* st_lse;     // [B, Hq, N] natural log
   int sink, local;
+  int stripe;              // 1: the lists name key columns (gathered rows), 0: key blocks
 };
 
 struct DecArgs {
