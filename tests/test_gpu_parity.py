@@ -93,6 +93,18 @@ def test_stripe_reduced(dev, seq, theta):
     _run_prefill_case(dev, x, np.full(8, theta, np.float32))
 
 
+@pytest.mark.parametrize("seq,hq,hkv,d,bq", [(1500, 2, 2, 128, 128), (1300, 4, 2, 64, 64),
+                                             (1100, 8, 1, 64, 128), (777, 2, 1, 128, 64)])
+def test_stripe_shapes(dev, seq, hq, hkv, d, bq):
+    """Column lists with 1, 2 and 8 query heads per KV head, head_dim 64 and 128, 64- and
+    128-row query blocks (every instance of the gathered-row attention)."""
+    x = synth.make_prefill("stripe_64k", seq=seq, hq=hq, hkv=hkv, head_dim=d)
+    x.block_q = bq
+    grp = hq // hkv
+    theta = np.repeat(np.array([3.0, 5.0], np.float32)[:hkv], grp)
+    _run_prefill_case(dev, x, theta)
+
+
 def test_stripe_capacity_overflow_reported(dev):
     import torch
     import block_sparse_attention_estimate_amd as sa
