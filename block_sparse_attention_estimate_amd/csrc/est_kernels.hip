@@ -506,7 +506,7 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_i8(kf, qf[nt][ks], acc[mt][nt]);
       }
-    const float skv = a.sk[(int64_t)bg * a.nKB + J];
+    const float skv = load_uniform(a.sk + (int64_t)bg * a.nKB + J);
     const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -578,6 +578,40 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
 }
 
 // ---------------------------------------------------------------------------------------
+// The 2*KS int8 key fragments of a tile (B operand: key row nt*32 + lane%32, bytes ks*32 +
+// (lane/32)*16, rows KP bytes apart) read from LDS in one block that also waits for them.  The
+// compiler sees no LDS read here, so it does not order the reads after the direct loads in
+// flight into other stages; the explicit waits and barriers around the tiles order them.
+template <int KS, int KP>
+SA_DEV void read_key_fragments(unsigned int addr, i32x4 (&kf)[2][KS]);
+template <>
+SA_DEV void read_key_fragments<4, 144>(unsigned int addr, i32x4 (&kf)[2][4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:0\n\t"
+      "ds_read_b128 %1, %8 offset:32\n\t"
+      "ds_read_b128 %2, %8 offset:64\n\t"
+      "ds_read_b128 %3, %8 offset:96\n\t"
+      "ds_read_b128 %4, %8 offset:4608\n\t"
+      "ds_read_b128 %5, %8 offset:4640\n\t"
+      "ds_read_b128 %6, %8 offset:4672\n\t"
+      "ds_read_b128 %7, %8 offset:4704\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0][0]), "=&v"(kf[0][1]), "=&v"(kf[0][2]), "=&v"(kf[0][3]),
+        "=&v"(kf[1][0]), "=&v"(kf[1][1]), "=&v"(kf[1][2]), "=&v"(kf[1][3])
+      : "v"(addr));
+}
+template <>
+SA_DEV void read_key_fragments<2, 80>(unsigned int addr, i32x4 (&kf)[2][2]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:0\n\t"
+      "ds_read_b128 %1, %4 offset:32\n\t"
+      "ds_read_b128 %2, %4 offset:2560\n\t"
+      "ds_read_b128 %3, %4 offset:2592\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0][0]), "=&v"(kf[0][1]), "=&v"(kf[1][0]), "=&v"(kf[1][1])
+      : "v"(addr));
+}
+
 // Stripe scores.  D[row][key] = qbar_q . K_q^T: rows are the A operand, keys the B operand,
 // so a lane owns one key column and 16 rows; one compare per element becomes a wave
 // ballot that holds, per row pair, the keep bits of 32 consecutive columns.
@@ -623,20 +657,23 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
     thr[r] = R < rows_total ? a.abar[row_base + Rc] - a.theta[g * G + Rc % G] : __builtin_huge_valf();
     sqv[r] = a.sq[row_base + Rc];
   }
-  // last causal key of row R's query block (-1 past the rows)
+  // last causal key of row R's query block (-1 past the rows), per register
   auto erow = [&](int R) { return R < rows_total ? min(a.N, (R / G + 1) * a.bq) - 1 : -1; };
-  const int e_min = min(a.N, (Rw / G + 1) * a.bq) - 1;
+  int erw[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) erw[r] = erow(Rw + half * 4 + 8 * (r >> 2) + (r & 3));
 
-  // K tiles go HBM -> LDS with direct loads into four stages shared by the four waves (rows
-  // padded to D + 16 bytes, so the 16 rows one quarter-wave reads land on distinct banks)
+  // K tiles go HBM -> LDS with direct loads into six stages shared by the four waves (rows
+  // padded to D + 16 bytes, so the 16 rows one quarter-wave reads land on distinct banks);
+  // a step is short here (8 MFMAs), so four tiles are kept in flight.  The stages are one
+  // array indexed at run time, so the loop body (and the kernel's code) exists once.
   constexpr int KP = D + 16;
   constexpr int WIN = (64 * KP + 1023) / 1024;       // 1 KB windows per tile
   constexpr int SL = (WIN + 3) / 4;                   // windows per wave
-  __shared__ __attribute__((aligned(1024))) unsigned char ks0[WIN * 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char ks1[WIN * 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char ks2[WIN * 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char ks3[WIN * 1024];
+  constexpr int NST = 6;
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[NST * WIN * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
+  auto stage = [&](int j) { return kst + (j % NST) * (WIN * 1024); };
   const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D;
   int s_off[SL];                                      // byte offset in a tile of this lane's 16 bytes
 #pragma unroll
@@ -654,24 +691,28 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
     }
   };
   const int k_rd = l32 * KP + half * 16;
+  // The workgroup's keep-bit words ([query block of its 128 rows][64 words of its 32 key
+  // tiles]) collect in LDS and go out in one coalesced copy at the end: global stores inside
+  // the loop would count in vmcnt and hold up the direct-load waits.
+  constexpr int QBW = 128 / G;                        // query blocks per workgroup
+  __shared__ unsigned int sbits[QBW * 64];
+  const int R0 = rt * 128;                            // first row of the workgroup
 
   // one key tile: D = qbar K^T on int8 MFMA (a lane owns one key column and 16 rows), then one
   // compare per element, turned into keep-bit words by wave ballots
   auto tile = [&](const unsigned char* st, int J) {
+    i32x4 kf[2][KS];
+    read_key_fragments<KS, KP>((unsigned int)(uintptr_t)LDS_PTR(const unsigned char, st + k_rd), kf);
     i32x16 acc[2] = {(i32x16){}, (i32x16){}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const i32x4 kf = *(const i32x4*)(st + k_rd + nt * 32 * KP + ks * 32);
-        acc[nt] = mfma_i8(qf[ks], kf, acc[nt]);
-      }
-    const float skv = a.sk[(int64_t)bg * a.nKB + J];
+      for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma_i8(qf[ks], kf[nt][ks], acc[nt]);
+    const float skv = load_uniform(a.sk + (int64_t)bg * a.nKB + J);
     // keep <=> fp32(fp32(D) * m) - (abar - theta) >= 0 <=> fp32(fp32(D) * m) >= (abar - theta)
     float mult[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) mult[r] = __fmul_rn(__fmul_rn(sqv[r], skv), a.c);
-    const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int key = J * 64 + nt * 32 + l32;
@@ -684,9 +725,7 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
         for (int bb = 0; bb < 4; ++bb) {
           const int r = 4 * ag + bb;
           const float y = __fmul_rn((float)acc[nt][r], mult[r]);
-          bool keep = y >= thr[r];
-          if (need_mask) keep = keep && key <= erow(Rw + half * 4 + 8 * ag + bb);
-          bal[bb] = __ballot(keep);
+          bal[bb] = __ballot(y >= thr[r] && key <= erw[r]);
         }
         const int Rg = Rw + 8 * ag;                      // first row of this 8-row group
         if (lane == 0) {
@@ -698,16 +737,15 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
               word |= bal[bb];
               if (((bb + 1) % G) == 0) {
                 const int R_lo = Rg + bb + 1 - G, R_hi = R_lo + 4;
-                if (R_lo < rows_total) a.bits[(row_base / G + R_lo / G) * a.W + wi] = (unsigned int)word;
-                if (R_hi < rows_total) a.bits[(row_base / G + R_hi / G) * a.W + wi] = (unsigned int)(word >> 32);
+                sbits[((R_lo - R0) / G) * 64 + wi - 2 * J0] = (unsigned int)word;
+                sbits[((R_hi - R0) / G) * 64 + wi - 2 * J0] = (unsigned int)(word >> 32);
                 word = 0ull;
               }
             }
           } else {
             // G == 8: rows Rg .. Rg+7 (both halves) are one query block
             const unsigned long long word = bal[0] | bal[1] | bal[2] | bal[3];
-            if (Rg < rows_total)
-              a.bits[(row_base / G + Rg / G) * a.W + wi] = (unsigned int)word | (unsigned int)(word >> 32);
+            sbits[((Rg - R0) / G) * 64 + wi - 2 * J0] = (unsigned int)word | (unsigned int)(word >> 32);
           }
         }
         if (MARGINS) {
@@ -716,9 +754,8 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
             const int r = 4 * ag + bb;
-            const int er = erow(Rw + half * 4 + 8 * ag + bb);
             float m = __fmul_rn((float)acc[nt][r], mult[r]) - thr[r];
-            if (key > er || er < 0) m = NEG_INF;
+            if (key > erw[r] || erw[r] < 0) m = NEG_INF;
             mv[bb] = m;
           }
           if (G <= 4) {
@@ -729,7 +766,7 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
               if (((bb + 1) % G) == 0) {
                 const int b0 = bb + 1 - G;
                 const int R = Rg + half * 4 + b0;
-                if (R < rows_total && key <= erow(R))
+                if (R < rows_total && key <= erw[4 * ag + b0])
                   a.margins[((int64_t)bg * a.nQB + R / G) * a.N + key] = mg;
                 mg = NEG_INF;
               }
@@ -737,7 +774,7 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
           } else {
             float mg = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));
             mg = fmaxf(mg, swap_halves(mg));
-            if (half == 0 && Rg < rows_total && key <= erow(Rg))
+            if (half == 0 && Rg < rows_total && key <= erw[4 * ag])
               a.margins[((int64_t)bg * a.nQB + Rg / G) * a.N + key] = mg;
           }
         }
@@ -745,31 +782,29 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
     }
   };
 
-  // Tile J0 + j is in stage j % 4; tiles j+1 and j+2 are loaded or in flight.  Step j
-  // computes tile j, issues tile j+3 (clamped to the last tile, so every wave issues SL loads
-  // per step) into the stage of tile j-1 and waits until tile j+1 has landed.
+  // Tile J0 + j is in stage j % 6; tiles j+1 .. j+4 are loaded or in flight.  Step j computes
+  // tile j, issues tile j+5 (clamped to the last tile, so every wave issues SL loads per step)
+  // into the stage of tile j-1 and waits until tile j+1 has landed.
   const int nt_ = J_end - J0;
-  issue(ks0, J0);
-  issue(ks1, J0 + min(1, nt_ - 1));
-  issue(ks2, J0 + min(2, nt_ - 1));
-  DMA_BARRIER(2 * SL);
-  auto step = [&](const unsigned char* sc, unsigned char* sd, int j) {
-    if (wave_live) tile(sc, J0 + j);
-    issue(sd, J0 + min(j + 3, nt_ - 1));
-    DMA_BARRIER(2 * SL);
-  };
-  int j = 0;
-  for (; j + 4 <= nt_; j += 4) {
-    step(ks0, ks3, j);
-    step(ks1, ks0, j + 1);
-    step(ks2, ks1, j + 2);
-    step(ks3, ks2, j + 3);
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p) issue(stage(p), J0 + min(p, nt_ - 1));
+  DMA_BARRIER((NST - 2) * SL);
+  for (int j = 0; j < nt_; ++j) {
+    if (wave_live) tile(stage(j), J0 + j);
+    issue(stage(j + NST - 1), J0 + min(j + NST - 1, nt_ - 1));
+    DMA_BARRIER((NST - 2) * SL);
   }
-  if (j < nt_) step(ks0, ks3, j);
-  if (j + 1 < nt_) step(ks1, ks0, j + 1);
-  if (j + 2 < nt_) step(ks2, ks1, j + 2);
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
+  __syncthreads();
+  // the words of the tiles this workgroup computed, for its query blocks that exist
+  const int qb0 = R0 / G;
+  const int nwords = 2 * nt_;
+  for (int p = tid; p < QBW * 64; p += 256) {
+    const int qb = p / 64, wd = p % 64;
+    if (wd < nwords && qb0 + qb < a.nQB)
+      a.bits[(row_base / G + qb0 + qb) * a.W + 2 * J0 + wd] = sbits[p];
+  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -957,7 +992,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
       if (J > sink_last && J < wlo) J = wlo;           // skip the tiles between the areas
       i32x4 kf[2][KS];
       load_k(J, kf);
-      const float skv = skb[J];
+      const float skv = load_uniform(skb + J);
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
         if (uu == 1 && !two) break;
@@ -1003,7 +1038,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
 
     // 2. every causal key tile: best (S~ - LSE + theta) over the wave's rows and units
     auto tile = [&](const unsigned char* st, int J) {
-      const float skv = skb[J];
+      const float skv = load_uniform(skb + J);
       float best = NEG_INF;
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
@@ -1050,7 +1085,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
         }
       }
       best = wave_max(best);
-      if (lane == 0 && best > NEG_INF) atomicMax(&mkey[J], float_order_key(best));
+      if (lane == 0 && best > NEG_INF) lds_max_u32(&mkey[J], float_order_key(best));
     };
     // Tile j is in stage j % 4; tiles j+1 and j+2 are loaded or in flight.  Step j computes
     // tile j (waves with units), issues tile j+3 (clamped to the last tile, so every wave
@@ -1380,7 +1415,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel_fp4(EstArgs a) {
         }
       }
       best = wave_max(best);
-      if (lane == 0 && best > NEG_INF) atomicMax(&mkey[J], float_order_key(best));
+      if (lane == 0 && best > NEG_INF) lds_max_u32(&mkey[J], float_order_key(best));
     };
     issue(ks0, 0);
     issue(ks1, min(1, Jn - 1));

@@ -113,6 +113,22 @@ SA_DEV int wave_uniform(int v) {
     asm volatile("" ::: "memory");                       \
   } while (0)
 
+// A wave-uniform value of data the kernel only reads, loaded through the constant address
+// space: a scalar load, which the compiler waits for with lgkmcnt.  A vector load would be
+// waited for with vmcnt, and so behind every direct-to-LDS load in flight.
+template <typename T>
+SA_DEV T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// LDS atomic max without a returned value, as one instruction the compiler does not order
+// against the direct-to-LDS loads in flight (it cannot tell the target from their stages).
+// Completion is the caller's: an lgkmcnt(0) wait (DMA_BARRIER has one) before the value is
+// read by any wave.
+SA_DEV void lds_max_u32(unsigned int* p, unsigned int v) {
+  asm volatile("ds_max_u32 %0, %1" : : "v"((unsigned int)(uintptr_t)LDS_PTR(unsigned int, p)), "v"(v));
+}
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger unsigned).
 SA_DEV unsigned int float_order_key(float f) {
   unsigned int u = __float_as_uint(f);
