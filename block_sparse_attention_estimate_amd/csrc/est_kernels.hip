@@ -913,11 +913,12 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
   constexpr int KP = D + 16;
   constexpr int WIN = (64 * KP + 1023) / 1024;
   constexpr int SL = (WIN + 3) / 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char ks0[WIN * 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char ks1[WIN * 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char ks2[WIN * 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char ks3[WIN * 1024];
+  // the four stages are one array indexed at run time, so the main loop's body exists once
+  // (its key fragments are read by read_key_fragments, which the compiler does not order
+  // behind the loads in flight)
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[4 * WIN * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
+  auto stage = [&](int j) { return kst + (j & 3) * (WIN * 1024); };
   const int8_t* ktile0 = a.kq + ((int64_t)bg * a.nKB * 64) * D;
   int s_off[SL];
 #pragma unroll
@@ -1049,14 +1050,14 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (i32x16){};
+        i32x4 kf[2][KS];
+        read_key_fragments<KS, KP>((unsigned int)(uintptr_t)LDS_PTR(const unsigned char, st + k_rd), kf);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const i32x4 kf = *(const i32x4*)(st + k_rd + mt * 32 * KP + ks * 32);
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_i8(kf, qf[uu][nt][ks], acc[mt][nt]);
-          }
+            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_i8(kf[mt][ks], qf[uu][nt][ks], acc[mt][nt]);
         const bool need_mask = J * 64 + 63 > rmin[uu] || J * 64 + 63 >= a.N;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -1090,25 +1091,15 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
     // Tile j is in stage j % 4; tiles j+1 and j+2 are loaded or in flight.  Step j computes
     // tile j (waves with units), issues tile j+3 (clamped to the last tile, so every wave
     // issues SL loads per step) into the stage of tile j-1 and waits until tile j+1 landed.
-    issue(ks0, 0);
-    issue(ks1, min(1, Jn - 1));
-    issue(ks2, min(2, Jn - 1));
+    issue(stage(0), 0);
+    issue(stage(1), min(1, Jn - 1));
+    issue(stage(2), min(2, Jn - 1));
     DMA_BARRIER(2 * SL);
-    auto step = [&](const unsigned char* sc, unsigned char* sd, int J) {
-      if (nu > 0) tile(sc, J);
-      issue(sd, min(J + 3, Jn - 1));
+    for (int J = 0; J < Jn; ++J) {
+      if (nu > 0) tile(stage(J), J);
+      issue(stage(J + 3), min(J + 3, Jn - 1));
       DMA_BARRIER(2 * SL);
-    };
-    int J = 0;
-    for (; J + 4 <= Jn; J += 4) {
-      step(ks0, ks3, J);
-      step(ks1, ks0, J + 1);
-      step(ks2, ks1, J + 2);
-      step(ks3, ks2, J + 3);
     }
-    if (J < Jn) step(ks0, ks3, J);
-    if (J + 1 < Jn) step(ks1, ks0, J + 1);
-    if (J + 2 < Jn) step(ks2, ks1, J + 2);
     // the stages are reused by the next pass: every load has landed and every wave is done
     __builtin_amdgcn_s_waitcnt(VMCNT_IMM(0));
     __syncthreads();
