@@ -130,27 +130,40 @@ __global__ __launch_bounds__(64 * AS_WAVES) void est_anchor_state(EstArgs a) {
           const bf16x8 kf = *(const bf16x8*)(kv + k_rd + tt * 32 * KPITCH + ks * 32);
           acc = mfma_bf16(kf, qf[ks], acc);
         }
-        // a tile whose 32 keys are visible to all 32 rows of the slice needs no mask
+        // a tile whose 32 keys are visible to all 32 rows of the slice needs no mask (a
+        // wave-uniform branch: most window tiles)
         const bool all_sink = ts + 31 < a.sink && ts + 31 <= ra;
         const bool all_win = ts >= ra + 31 - a.local + 1 && ts + 31 <= ra;
         float s[16];
         float tm = NEG_INF;
+        if (all_sink || all_win) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
-          const bool ok = (all_sink || all_win) ||
-                          (key <= row && (key < a.sink || key >= row - a.local + 1));
-          if (ok) mx = fmaxf(mx, acc[r]);
-          s[r] = ok ? acc[r] * sl2 : NEG_INF;
-          tm = fmaxf(tm, s[r]);
+          for (int r = 0; r < 16; ++r) {
+            mx = fmaxf(mx, acc[r]);
+            s[r] = acc[r] * sl2;
+            tm = fmaxf(tm, s[r]);
+          }
+        } else {
+          const int w_lo = row - a.local + 1;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = ts + half * 4 + 8 * (r >> 2) + (r & 3);
+            const bool ok = key <= row && (key < a.sink || key >= w_lo);
+            if (ok) mx = fmaxf(mx, acc[r]);
+            s[r] = ok ? acc[r] * sl2 : NEG_INF;
+            tm = fmaxf(tm, s[r]);
+          }
         }
         tm = half_pair_max(tm);
-        if (tm > m_run) {                              // exact running max (log2 domain)
-          const float alpha = m_run == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m_run - tm);
+        // The running max (log2 domain) moves only when a tile's scores exceed it by more than
+        // 8, so P stays <= 2^8 and O is rescaled rarely (the result is exact in the ratio).
+        if (__any(tm > m_run + 8.0f)) {
+          const float mnew = fmaxf(m_run, tm);
+          const float alpha = m_run == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
           l_run *= alpha;
 #pragma unroll
           for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
-          m_run = tm;
+          m_run = mnew;
         }
         const float msub = m_run == NEG_INF ? 0.f : m_run;
         bf16x8 pf[2];
