@@ -773,3 +773,45 @@ def test_prefill_arbitrary_lists(dev, granularity, bq):
     log(f"  arbitrary {granularity} bq={bq}: rows without keys {n_empty}, "
         f"max|dO|={err.max():.2e} mean={err.mean():.2e}")
     assert n_empty > 0 and err.max() < MAX_ABS and err.mean() < MEAN_ABS
+
+
+@pytest.mark.parametrize("bk,top_k,top_p", [(64, 8, 0.0), (64, 40, 0.0), (32, 12, 0.0), (64, 40, 0.6)])
+def test_decode_edge_lengths(dev, bk, top_k, top_p):
+    """Cache lengths at the edges: one token, the sink boundary, block boundaries, the window
+    boundary and a full cache, in one batch (selection, summaries and attention)."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    lens = [1, 31, 32, 63, 64, 65, 257, 300, 2048]
+    x = synth.make_decode(batch=len(lens), seq=2048, hq=8, hkv=2, head_dim=128, top_k=top_k)
+    x.cache_len[:] = np.array(lens, np.int32)
+    q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=bk)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=bk, top_k=top_k, sink=32, local=256,
+                                   top_p=top_p)
+    torch.cuda.synchronize()
+    kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, bk)
+    kb = kbar.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, L in enumerate(lens):
+        nb = -(-L // bk)
+        np.testing.assert_array_equal(kb[b, :nb], kbar_ref[b, :nb])
+    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=bk, top_k=top_k, sink=32,
+                               local=256, top_p=top_p)
+    s = sel.cpu().numpy()
+    if top_p > 0:
+        used, off, flips = check_topp_selection(s, ref)
+    else:
+        used, flips = {}, 0
+        for (b, g), r in ref.items():
+            k_ = min(top_k, -(-lens[b] // bk))
+            got = s[b, g, :k_]
+            assert (s[b, g, k_:] == -1).all() and np.all(np.diff(got) > 0)
+            diff = set(got.tolist()) ^ set(r["selected"].tolist())
+            assert diff <= set(r["ambiguous"].tolist()), ((b, g), sorted(diff))
+            flips += len(diff)
+            used[(b, g)] = got
+    O, LSE = oracle.decode_attention(x.q, x.k_cache, x.v_cache, x.cache_len, used, block_k=bk)
+    err = np.abs(o.float().cpu().numpy() - O)
+    assert err.max() < MAX_ABS and err.mean() < MEAN_ABS, (err.max(), err.mean())
+    assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
+    log(f"  decode edge lengths bk={bk} K={top_k} top_p={top_p}: flips={flips} max|dO|={err.max():.2e}")
