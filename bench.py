@@ -509,7 +509,7 @@ def main():
                                 args.command))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the workload "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the workload "
               "would shard by KV head with no exchange); run with --gpus 1", file=sys.stderr)
         raise SystemExit(2)
     import torch

@@ -7,7 +7,7 @@ relative-score test keeps a block when its estimated weight is at least tau time
 anchor's, i.e. anchor - score <= -ln tau: theta = -ln tau in the logit units of
 AnchorAttention Eq. (2).
 
-Readings (listed in the design doc): Err is computed per query head, summing |O - O~| over the
+Readings where the page is silent: Err is computed per query head, summing |O - O~| over the
 batch, the rows and the head dimensions and dividing by the number of rows (batch * seq);
 O is attention with every causal block kept; all heads are evaluated together every round
 and every head not yet below the bound halves its tau (the lists are unions over the query
