@@ -340,7 +340,8 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   constexpr int BINS = 2048;
   constexpr unsigned int FORCED = 0xFFFFFFFFu;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  extern __shared__ unsigned int skey[];             // [nKB]
+  extern __shared__ unsigned int skey[];             // [nKB] keys, then [nKB] scores
+  float* ssc = (float*)(skey + a.nKB);
   __shared__ unsigned int hist[BINS];
   __shared__ unsigned long long hmass[BINS];
   __shared__ unsigned int s_dig, s_need, s_cab;
@@ -353,11 +354,27 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   const int lb = min(max(a.cache_len[b], 0), a.L);
   const int nb = (lb + a.bk - 1) / a.bk;
   const float* sc = a.scores + ((int64_t)b * a.Hkv + g) * a.nKB;
+  // Thread t owns blocks t, t + 256, ... in every loop over the blocks below.  Its scores are
+  // loaded eight at a time, all in flight together: one load per iteration would wait out
+  // the memory latency once per 256 blocks.
   int nf_local = 0;
-  for (int j = tid; j < nb; j += 256) {
-    const bool forced = (j * a.bk < a.sink) || ((j + 1) * a.bk - 1 >= lb - a.local);
-    skey[j] = forced ? FORCED : float_order_key(sc[j]);
-    nf_local += forced;
+  for (int j0 = tid; j0 < nb; j0 += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = sc[min(j0 + 256 * e, nb - 1)];
+    // every value is taken here, so no load sinks into the conditional stores below
+#pragma unroll
+    for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(v[e]));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + 256 * e;
+      if (j < nb) {
+        const bool forced = (j * a.bk < a.sink) || ((j + 1) * a.bk - 1 >= lb - a.local);
+        skey[j] = forced ? FORCED : float_order_key(v[e]);
+        ssc[j] = v[e];
+        nf_local += forced;
+      }
+    }
   }
   const int kk = min(a.top_k, nb);
   unsigned int T = 0, mask = 0;                      // threshold on the resolved bits
@@ -369,14 +386,14 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   if (a.top_p > 0.f) {
     // max score, then the fixed-point weights and their sums (all, forced)
     float mloc = NEG_INF;
-    for (int j = tid; j < nb; j += 256) mloc = fmaxf(mloc, sc[j]);
+    for (int j = tid; j < nb; j += 256) mloc = fmaxf(mloc, ssc[j]);
     for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
     if (tid == 0) { s_z = 0; s_f = 0; s_nf = 0; }
     if ((tid & 63) == 0) s_max[tid >> 6] = mloc;
     __syncthreads();
     const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     auto wfix = [&](int j) -> unsigned long long {
-      return (unsigned long long)(expf(sc[j] - M) * 0x1p40f);
+      return (unsigned long long)(expf(ssc[j] - M) * 0x1p40f);
     };
     unsigned long long zl = 0, fl = 0;
     for (int j = tid; j < nb; j += 256) {
@@ -948,7 +965,7 @@ static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
       default: hipLaunchKernelGGL((dec_score_rows<D, 8>), sgrid, dim3(256), 0, s, a); break;
     }
   }
-  hipLaunchKernelGGL(dec_select_radix, dim3(a.Hkv, a.B), dim3(256), a.nKB * sizeof(unsigned int), s, a);
+  hipLaunchKernelGGL(dec_select_radix, dim3(a.Hkv, a.B), dim3(256), a.nKB * 2 * sizeof(unsigned int), s, a);
   const dim3 grid(a.n_splits, a.Hkv, a.B);
   if (a.bk == 64) {
     hipLaunchKernelGGL(dec_splitk_mfma<D>, grid, dim3(256), 0, s, a);
