@@ -43,7 +43,8 @@ from .estimate import (  # noqa: F401
 )
 from .attention import attention_rows, attention_all, dense_causal_reference_mask  # noqa: F401
 from .decode import (block_summary, decode_select, decode_attention, quantize_summary_q4,  # noqa: F401
-                     dequantize_summary_q4, pack_q4)
+                     dequantize_summary_q4, pack_q4, quantize_summary_fp4,
+                     dequantize_summary_fp4, pack_fp4)
 from .diagnostics import pruned_mass_fraction, sparsity_from_kept, sale_log_margin  # noqa: F401
 from .calibrate import full_lists, head_l1_error, calibrate_theta  # noqa: F401
 from .estimate_sale import estimate_rows_sale, estimate_all_sale, relative_scores  # noqa: F401

@@ -18,7 +18,9 @@ smaller at no accuracy cost): each summary row is cut into groups of 32 dims; a 
 a = max |x| gets the scale fp32(a / 7) rounded to bf16 and codes clamp(rint_even(fp32(x *
 fp32(7 / a))), -7, 7) (all zero for a = 0); the score then uses scale * code.  Storage
 (``pack_q4``) is a layout choice of this library, not the pages'.  4 code bits
-per dim plus one 16-bit scale per 32 dims is 4.5 bits per dim instead of 16 (3.56x).
+per dim plus one 16-bit scale per 32 dims is 4.5 bits per dim instead of 16 (3.56x).  The
+FP4 form (``quantize_summary_fp4``) is OCP MXFP4: E2M1 values with one power-of-two scale per
+32 dims, 4.25 bits per dim (3.76x).
 
 Readings: the summary is the mean of the block's cached keys (fp64 sum, fp64 division,
 rounded to fp32 and then to bf16, round to nearest even); the block score is the max over
@@ -41,6 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 from .estimate import _f64, softmax_scale
+from .estimate_sale import E2M1_GRID, dequantize_mxfp4, quantize_mxfp4
 
 AMBIGUITY_BAND = 1e-3
 # a budget is ambiguous when a cumulative share next to the decision lies this close to top_p
@@ -105,6 +108,32 @@ def pack_q4(codes: np.ndarray) -> np.ndarray:
         w |= u[..., 2 * j] << np.uint32(4 * j)
         w |= u[..., 2 * j + 1] << np.uint32(4 * (j + 4))
     return w.view(np.uint8).reshape(codes.shape[:-1] + (codes.shape[-1] // 2,))
+
+
+def quantize_summary_fp4(kbar: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """FP4 summaries (the page's other 4-bit format: FP4 microscale), read as OCP MXFP4: each
+    group of 32 dims shares the exponent e = floor(log2 max|x|) - 2 and each dim is an E2M1
+    value (the MXFP4 quantiser of the relative estimator).  kbar bf16 bits [..., D] ->
+    (values float64 [..., D] on the signed E2M1 grid, exponents int [..., D / 32]); the
+    summary is read as values * 2 ** e."""
+    return quantize_mxfp4(_f64(kbar).astype(np.float32))
+
+
+def dequantize_summary_fp4(vals: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    return dequantize_mxfp4(vals, exps)
+
+
+def pack_fp4(kbar: np.ndarray, vals: np.ndarray, exps: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Storage of FP4 summaries (a layout choice of this library): per dim the E2M1 nibble
+    (magnitude index into the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6 in bits 0-2, the sign bit of the
+    summary value -- negative zero included -- in bit 3), dim 2k in the low and 2k + 1 in the
+    high nibble of byte k; per 32 dims the E8M0 byte e + 127.
+    Returns (codes uint8 [..., D / 2], exps uint8 [..., D / 32])."""
+    mag = np.searchsorted(E2M1_GRID, np.abs(vals)).astype(np.uint8)   # exact grid values
+    sign = np.signbit(_f64(kbar).astype(np.float32)).astype(np.uint8)
+    nib = mag | (sign << 3)
+    codes = nib[..., 0::2] | (nib[..., 1::2] << 4)
+    return codes.astype(np.uint8), (np.asarray(exps) + 127).astype(np.uint8)
 
 
 def decode_forced(n_blocks: int, length: int, block_k: int, sink: int, local: int) -> np.ndarray:
