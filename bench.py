@@ -381,6 +381,8 @@ def bench_decode(args, dev):
     kbar = sa.build_block_summary(kc, cl, block_k=x.block_k)
     if args.summary == "q4":
         kbar = sa.quantize_block_summary(kbar, block_k=x.block_k)
+    elif args.summary == "fp4":
+        kbar = sa.quantize_block_summary_fp4(kbar, block_k=x.block_k)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     top_k = args.top_k or x.top_k
@@ -399,7 +401,8 @@ def bench_decode(args, dev):
     us = e0.elapsed_time(e1) * 1e3 / args.steps
     nkb = -(-L // x.block_k)
     sel_bytes = n_sel * x.block_k * D * 2 * 2
-    sum_bytes = B * Hkv * nkb * (D * 2 if args.summary == "bf16" else D // 2 + D // 32 * 2)
+    per_row = {"bf16": D * 2, "q4": D // 2 + D // 32 * 2, "fp4": D // 2 + D // 32}[args.summary]
+    sum_bytes = B * Hkv * nkb * per_row
     gbs = (sel_bytes + sum_bytes) / (us * 1e-6) / 1e9
     return {"metric": "sparse decode step time and achieved HBM GB/s",
             "value": round(gbs, 1), "unit": "GB/s (algorithmic)", "n_gpus": 1,
@@ -474,8 +477,8 @@ def main():
                     help="print per-kernel HBM bytes and GB/s for --kernels and exit")
     ap.add_argument("--kernels", default="est_quant_k,est_anchor_pool,est_score_block,est_compact")
     ap.add_argument("--kernel", default="attn_block")
-    ap.add_argument("--summary", choices=["bf16", "q4"], default="bf16",
-                    help="decode: block summaries in bf16 or 4-bit codes + bf16 scales")
+    ap.add_argument("--summary", choices=["bf16", "q4", "fp4"], default="bf16",
+                    help="decode: block summaries in bf16, 4-bit codes + bf16 scales (q4) or MXFP4 (fp4)")
     ap.add_argument("--estimator", choices=["pooled", "relative", "relative_mxfp4"],
                     default="pooled",
                     help="prefill: anchor vs pooled query, or the element-wise relative score "

@@ -28,7 +28,8 @@ from ._lib import (SA_BLOCK, SA_STRIPE, SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DEC
 
 __all__ = ["Lists", "AnchorState", "alloc_anchor_state", "estimate_mask", "sparse_prefill",
            "estimate_mask_anchor_state", "sparse_prefill_resume", "build_block_summary",
-           "quantize_block_summary", "sparse_decode", "calibrate_theta", "workspace_size",
+           "quantize_block_summary", "quantize_block_summary_fp4", "sparse_decode",
+           "calibrate_theta", "workspace_size",
            "SaError", "load_library"]
 
 
@@ -370,11 +371,29 @@ def quantize_block_summary(k_summary, *, block_k=64, seq_k=None, stream=None):
     return codes, scales
 
 
+def quantize_block_summary_fp4(k_summary, *, block_k=64, seq_k=None, stream=None):
+    """FP4 (MXFP4) summaries (sa_quantize_block_summary_fp4) of bf16 summaries
+    [B, nKB, Hkv, d]: returns (codes uint8 [B, nKB, Hkv, d/2], exps uint8 [B, nKB, Hkv, d/32])."""
+    lib = _lib.load()
+    _check_bf16("k_summary", k_summary, 4)
+    B, nkb, Hkv, D = k_summary.shape
+    s = _lib.SaShape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = B, Hkv, Hkv, D
+    s.seq_q, s.seq_k = 1, seq_k if seq_k is not None else nkb * block_k
+    codes = torch.empty((B, nkb, Hkv, D // 2), dtype=torch.uint8, device=k_summary.device)
+    exps = torch.empty((B, nkb, Hkv, D // 32), dtype=torch.uint8, device=k_summary.device)
+    _lib.check(lib.sa_quantize_block_summary_fp4(ctypes.byref(s), block_k, _ptr(k_summary),
+                                                 _ptr(codes), _ptr(exps), _stream(stream)),
+               "sa_quantize_block_summary_fp4")
+    return codes, exps
+
+
 def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_k=64, sink=32,
                   local=256, n_splits=0, softmax_scale=0.0, top_p=0.0, workspace=None, out=None,
                   return_selected=True, stream=None):
-    """Top-K block-sparse decode (sa_sparse_decode, or sa_sparse_decode_q4 when k_summary is
-    the (codes, scales) pair of quantize_block_summary).  q [B, Hq, d]; caches [B, L, Hkv, d].
+    """Top-K block-sparse decode (sa_sparse_decode; sa_sparse_decode_q4 when k_summary is the
+    (codes, scales) pair of quantize_block_summary, sa_sparse_decode_fp4 when it is the
+    (codes, exps) pair of quantize_block_summary_fp4).  q [B, Hq, d]; caches [B, L, Hkv, d].
     top_p in (0, 1] reads each (b, KV head)'s budget from the block-score distribution (at
     most top_k blocks); 0 selects top_k.
     Returns (o [B, Hq, d] bf16, lse [B, Hq] fp32, selected [B, Hkv, top_k] int32 or None;
@@ -397,7 +416,13 @@ def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_
     sel = None
     if return_selected:
         sel = torch.empty((B, k_cache.shape[2], top_k), dtype=torch.int32, device=q.device)
-    if isinstance(k_summary, (tuple, list)):
+    if isinstance(k_summary, (tuple, list)) and k_summary[1].dtype == torch.uint8:
+        codes, exps = k_summary
+        _lib.check(lib.sa_sparse_decode_fp4(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k_cache),
+                                            _ptr(v_cache), _ptr(codes), _ptr(exps), _ptr(cache_len),
+                                            _ptr(o), _ptr(lse), _ptr(sel), _ptr(workspace),
+                                            workspace.numel(), _stream(stream)), "sa_sparse_decode_fp4")
+    elif isinstance(k_summary, (tuple, list)):
         codes, scales = k_summary
         _lib.check(lib.sa_sparse_decode_q4(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k_cache),
                                            _ptr(v_cache), _ptr(codes), _ptr(scales), _ptr(cache_len),

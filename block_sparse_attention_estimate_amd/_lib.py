@@ -21,7 +21,8 @@ SA_MAX_Q_HEADS = 128
 EXPORTED = ("sa_workspace_size", "sa_estimate_mask", "sa_sparse_prefill",
             "sa_build_block_summary", "sa_sparse_decode", "sa_quantize_block_summary",
             "sa_sparse_decode_q4", "sa_calibrate_theta", "sa_status_string",
-            "sa_estimate_mask_anchor_state", "sa_sparse_prefill_resume")
+            "sa_estimate_mask_anchor_state", "sa_sparse_prefill_resume",
+            "sa_quantize_block_summary_fp4", "sa_sparse_decode_fp4")
 
 
 class SaShape(ctypes.Structure):
@@ -97,6 +98,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sa_sparse_decode_q4.restype = ctypes.c_int
     lib.sa_sparse_decode_q4.argtypes = [P(SaShape), P(SaDecodeParams), vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sa_quantize_block_summary_fp4.restype = ctypes.c_int
+    lib.sa_quantize_block_summary_fp4.argtypes = [P(SaShape), ctypes.c_int32, vp, vp, vp, vp]
+    lib.sa_sparse_decode_fp4.restype = ctypes.c_int
+    lib.sa_sparse_decode_fp4.argtypes = [P(SaShape), P(SaDecodeParams), vp, vp, vp, vp, vp, vp,
+                                         vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_calibrate_theta.restype = ctypes.c_int
     lib.sa_calibrate_theta.argtypes = [P(SaShape), P(SaSparseParams), vp, vp, vp, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_int32, P(ctypes.c_float),

@@ -14,6 +14,8 @@
 //   dec_score_rows     score[b, g, J] = max over the group's heads of c * q_h . kbar_J, one
 //                      coalesced summary row per 16-lane group, DPP reductions
 //   dec_score_q4_mfma  the same from 4-bit summaries on bf16 MFMA (heads as MFMA columns)
+//   dec_summary_fp4    FP4 (MXFP4) summaries: E2M1 codes and one E8M0 exponent per 32 dims
+//   dec_score_fp4_mfma the same from FP4 summaries (codes to bf16 by the fp4 convert)
 //   dec_select_radix   forced blocks + top (K - |F|) others by (score desc, block asc): radix
 //                      select of the K-th key (11 bits per pass, LDS histograms), ascending
 //                      output list; or a top-p budget of others by the same passes over
@@ -277,6 +279,118 @@ __global__ __launch_bounds__(256) void dec_score_q4_mfma(DecArgs a) {
       float v = 0.f;
 #pragma unroll
       for (int gi = 0; gi < NGR; ++gi) v += sg[gi] * (acc[gi][r] - qcor[r][gi]);
+      if (r < nh) mx = fmaxf(mx, v);
+    }
+    mx = half_pair_max(mx) * a.c;                      // heads 4..7 live in lane ^ 32
+    const int J = J0 + l32;
+    if (half == 0 && J < a.nKB) out[J] = J < nb ? mx : NEG_INF;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// FP4 block summaries (SpotAttention "Key findings": the INT4 / FP4 microscale selector key
+// cache), in the OCP Microscaling v1.0 MXFP4 format, per group of 32 dims of a bf16 summary
+// row: shared exponent e = floor(log2 max|x|) - 2 clamped to [-127, 127], stored as the E8M0
+// byte e + 127; codes E2M1 of |x| * 2^-e (an exact scaling) with the sign bit of x (negative
+// zero included) in bit 3; dim 2k in the low and dim 2k + 1 in the high nibble of byte k.
+// 4.25 bits per dim.  One thread per group.
+__global__ __launch_bounds__(256) void dec_summary_fp4(const uint16_t* ksum, uint8_t* codes,
+                                                       uint8_t* exps, int64_t n_groups) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= n_groups) return;
+  const uint16_t* x = ksum + gi * 32;
+  unsigned short bits[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u16x8 u = *(const u16x8*)(x + 8 * j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bits[8 * j + e] = u[e];
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(bf16_bits_to_float(bits[e])));
+  // floor(log2 amax) is the unbiased exponent field of a normal float; subnormals clamp to -127
+  int ex = -127;
+  if (amax > 0.f) ex = max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 129, -127);
+  unsigned int w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const unsigned int code = e2m1_code(ldexpf(fabsf(bf16_bits_to_float(bits[e])), -ex)) |
+                              ((unsigned int)(bits[e] >> 15) << 3);
+    w[e >> 3] |= code << (4 * (e & 7));
+  }
+  *(u32x4*)(codes + gi * 16) = (u32x4){w[0], w[1], w[2], w[3]};
+  exps[gi] = (uint8_t)(ex + 127);
+}
+
+// score[b, g, J] from FP4 summaries on bf16 MFMA, laid out as dec_score_q4_mfma (G heads as
+// the MFMA rows, 32 blocks as the columns, DEC_Q4_TILES tiles per wave).  The codes become
+// bf16 with v_cvt_scalef32_pk_bf16_fp4 at scale 1 (every E2M1 value is exact in bf16, two
+// dims per instruction, low nibble first); each 32-dim group accumulates on its own and is
+// scaled by its 2^e afterwards (exact), so the score is sum over groups of 2^e * q . code.
+template <int D>
+__global__ __launch_bounds__(256) void dec_score_fp4_mfma(DecArgs a) {
+  constexpr int KS = D / 16, NGR = D / 32, TILES = DEC_Q4_TILES;
+  const int g = blockIdx.x, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = tid >> 6;
+  const int Jw = (blockIdx.y * 4 + wave) * (32 * TILES);   // this wave's first block
+  if (Jw >= a.nKB) return;
+  const int nb = (min(max(a.cache_len[b], 0), a.L) + a.bk - 1) / a.bk;
+  const int64_t row0 = ((int64_t)b * a.nKB) * a.Hkv + g;   // row of block J: row0 + J * Hkv
+  // loads of one tile: the lane's code words (B operand: block J0 + l % 32, dims 16 ks +
+  // 8 half .. +8) and that block's group exponents
+  auto load = [&](int J0, unsigned int* w, unsigned int& ev) {
+    const int64_t rowi = row0 + (int64_t)min(J0 + l32, a.nKB - 1) * a.Hkv;
+    const uint8_t* crow = a.ksum_q4 + rowi * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) w[ks] = *(const unsigned int*)(crow + (2 * ks + half) * 4);
+    if (NGR == 4) ev = *(const unsigned int*)(a.ksum_exp + rowi * 4);
+    else ev = *(const unsigned short*)(a.ksum_exp + rowi * 2);
+  };
+  unsigned int wt[TILES][KS], et[TILES];
+#pragma unroll
+  for (int tt = 0; tt < TILES; ++tt) load(Jw + 32 * tt, wt[tt], et[tt]);
+  // Q (A operand): lane l holds head l % 32 of the group (zero beyond G), dims 16 ks + 8 half
+  bf16x8 qf[KS];
+  {
+    const int hc = min(l32, a.G - 1);
+    const uint16_t* qp = a.q + b * a.qs0 + (g * a.G + hc) * a.qs2 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = *(const bf16x8*)(qp + ks * 16);
+      if (l32 >= a.G) qf[ks] = (bf16x8){};
+    }
+  }
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const int nh = min(a.G - 4 * half, 4);            // valid heads among this lane's r = 0..3
+  float* out = a.scores + ((int64_t)b * a.Hkv + g) * a.nKB;
+#pragma unroll
+  for (int tt = 0; tt < TILES; ++tt) {
+    const int J0 = Jw + 32 * tt;
+    const unsigned int* w = wt[tt];
+    f32x16 acc[NGR];
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi) acc[gi] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x2 p[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], 1.0f, 0),
+                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], 1.0f, 1),
+                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], 1.0f, 2),
+                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], 1.0f, 3)};
+      bf16x8 kf;
+      __builtin_memcpy(&kf, p, 16);
+      acc[ks / 2] = mfma_bf16(qf[ks], kf, acc[ks / 2]);
+    }
+    int eg[NGR];
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi) eg[gi] = (int)((et[tt] >> (8 * gi)) & 0xFFu) - 127;
+    float mx = NEG_INF;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < NGR; ++gi) v += ldexpf(acc[gi][r], eg[gi]);
       if (r < nh) mx = fmaxf(mx, v);
     }
     mx = half_pair_max(mx) * a.c;                      // heads 4..7 live in lane ^ 32
@@ -954,7 +1068,10 @@ hipError_t launch_block_summary(const DecArgs& a, hipStream_t s) {
 template <int D>
 static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
   const dim3 sgrid(a.Hkv, (a.nKB + 127) / 128, a.B);
-  if (a.ksum_q4) {
+  if (a.ksum_q4 && a.ksum_exp) {
+    hipLaunchKernelGGL(dec_score_fp4_mfma<D>, dim3(a.Hkv, (a.nKB + 128 * DEC_Q4_TILES - 1) / (128 * DEC_Q4_TILES), a.B),
+                       dim3(256), 0, s, a);
+  } else if (a.ksum_q4) {
     hipLaunchKernelGGL(dec_score_q4_mfma<D>, dim3(a.Hkv, (a.nKB + 128 * DEC_Q4_TILES - 1) / (128 * DEC_Q4_TILES), a.B),
                        dim3(256), 0, s, a);
   } else {
@@ -986,6 +1103,14 @@ hipError_t launch_summary_q4(const uint16_t* ksum, uint8_t* codes, uint16_t* sca
   if (n_groups == 0) return hipSuccess;
   hipLaunchKernelGGL(dec_summary_q4, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0, s, ksum,
                      codes, scales, n_groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_summary_fp4(const uint16_t* ksum, uint8_t* codes, uint8_t* exps, int64_t n_groups,
+                              hipStream_t s) {
+  if (n_groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(dec_summary_fp4, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0, s, ksum,
+                     codes, exps, n_groups);
   return hipGetLastError();
 }
 

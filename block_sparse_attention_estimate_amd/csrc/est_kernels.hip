@@ -1135,19 +1135,6 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
 // E2M1 of |x| * 2^-e (exact scaling) rounded to nearest with ties to the even code, saturating
 // at 6, sign in bit 3; 32 codes in 16 bytes, dim j of the block in nibble j (low nibble first).
 // ---------------------------------------------------------------------------------------
-SA_DEV unsigned int e2m1_code(float y) {
-  // grid 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 go
-  // to the even code
-  if (y <= 0.25f) return 0u;
-  if (y < 0.75f) return 1u;
-  if (y <= 1.25f) return 2u;
-  if (y < 1.75f) return 3u;
-  if (y <= 2.5f) return 4u;
-  if (y < 3.5f) return 5u;
-  if (y <= 5.0f) return 6u;
-  return 7u;
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void est_quant_rows_fp4(EstArgs a, int which) {
   constexpr int NC = D / 32;                         // blocks per row

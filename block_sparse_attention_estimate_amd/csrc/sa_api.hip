@@ -388,10 +388,12 @@ sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k, const v
   return SA_OK;
 }
 
-// shared by the bf16- and the 4-bit-summary decode entries (exactly one summary form given)
+// shared by the bf16-, 4-bit- and FP4-summary decode entries (exactly one summary form given:
+// k_summary, or codes with scales, or codes with exps)
 static sa_status decode_impl(const sa_shape* shape, const sa_decode_params* params, const void* q,
                              const void* k_cache, const void* v_cache, const void* k_summary,
-                             const void* codes, const void* scales, const int32_t* cache_len,
+                             const void* codes, const void* scales, const void* exps,
+                             const int32_t* cache_len,
                              void* o, float* lse, int32_t* selected, void* ws, size_t ws_bytes,
                              hipStream_t stream) {
   sa_status st = check_decode(shape, params);
@@ -399,7 +401,8 @@ static sa_status decode_impl(const sa_shape* shape, const sa_decode_params* para
   if (!q || !k_cache || !v_cache || !cache_len || !o) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return SA_ERR_SHAPE;
-  if (k_summary ? !aligned16(k_summary) : (!aligned16(codes) || !aligned16(scales)))
+  if (k_summary ? !aligned16(k_summary)
+                : (!aligned16(codes) || !aligned16(exps ? exps : scales)))
     return SA_ERR_SHAPE;
   const DecLayout L = dec_layout(shape, params);
   if (!ws) return SA_ERR_WORKSPACE;
@@ -413,6 +416,7 @@ static sa_status decode_impl(const sa_shape* shape, const sa_decode_params* para
   a.ksum = (const uint16_t*)k_summary;
   a.ksum_q4 = (const uint8_t*)codes;
   a.ksum_scale = (const uint16_t*)scales;
+  a.ksum_exp = (const uint8_t*)exps;
   a.cache_len = cache_len;
   a.o = (uint16_t*)o;
   a.lse = lse;
@@ -435,8 +439,8 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params
                            const int32_t* cache_len, void* o, float* lse, int32_t* selected,
                            void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!k_summary) return SA_ERR_NULL;
-  return decode_impl(shape, params, q, k_cache, v_cache, k_summary, nullptr, nullptr, cache_len, o,
-                     lse, selected, ws, ws_bytes, stream);
+  return decode_impl(shape, params, q, k_cache, v_cache, k_summary, nullptr, nullptr, nullptr,
+                     cache_len, o, lse, selected, ws, ws_bytes, stream);
 }
 
 sa_status sa_quantize_block_summary(const sa_shape* shape, int32_t block_k, const void* k_summary,
@@ -461,7 +465,33 @@ sa_status sa_sparse_decode_q4(const sa_shape* shape, const sa_decode_params* par
                               hipStream_t stream) {
   if (!summary_codes || !summary_scales) return SA_ERR_NULL;
   return decode_impl(shape, params, q, k_cache, v_cache, nullptr, summary_codes, summary_scales,
-                     cache_len, o, lse, selected, ws, ws_bytes, stream);
+                     nullptr, cache_len, o, lse, selected, ws, ws_bytes, stream);
+}
+
+sa_status sa_quantize_block_summary_fp4(const sa_shape* shape, int32_t block_k,
+                                        const void* k_summary, void* codes, void* exps,
+                                        hipStream_t stream) {
+  sa_status st = check_shape_common(shape);
+  if (st != SA_OK) return st;
+  if (!k_summary || !codes || !exps) return SA_ERR_NULL;
+  if (block_k < 1) return SA_ERR_PARAM;
+  if (!aligned16(k_summary) || !aligned16(codes) || !aligned16(exps)) return SA_ERR_SHAPE;
+  const int64_t n_groups = (int64_t)shape->batch * ceil_div(shape->seq_k, block_k) *
+                           shape->n_kv_heads * (shape->head_dim / 32);
+  if (launch_summary_fp4((const uint16_t*)k_summary, (uint8_t*)codes, (uint8_t*)exps, n_groups,
+                         stream) != hipSuccess)
+    return SA_ERR_DEVICE;
+  return SA_OK;
+}
+
+sa_status sa_sparse_decode_fp4(const sa_shape* shape, const sa_decode_params* params, const void* q,
+                               const void* k_cache, const void* v_cache, const void* summary_codes,
+                               const void* summary_exps, const int32_t* cache_len, void* o,
+                               float* lse, int32_t* selected, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!summary_codes || !summary_exps) return SA_ERR_NULL;
+  return decode_impl(shape, params, q, k_cache, v_cache, nullptr, summary_codes, nullptr,
+                     summary_exps, cache_len, o, lse, selected, ws, ws_bytes, stream);
 }
 
 sa_status sa_calibrate_theta(const sa_shape* shape, const sa_sparse_params* params,

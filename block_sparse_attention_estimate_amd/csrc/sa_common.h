@@ -134,3 +134,17 @@ SA_DEV unsigned int float_order_key(float f) {
   unsigned int u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// E2M1 magnitude code (OCP Microscaling v1.0 FP4) of y >= 0: the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6
+// is codes 0..7, round to nearest with the midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 going to
+// the even code, saturating at 6.
+SA_DEV unsigned int e2m1_code(float y) {
+  if (y <= 0.25f) return 0u;
+  if (y < 0.75f) return 1u;
+  if (y <= 1.25f) return 2u;
+  if (y < 1.75f) return 3u;
+  if (y <= 2.5f) return 4u;
+  if (y < 3.5f) return 5u;
+  if (y <= 5.0f) return 6u;
+  return 7u;
+}

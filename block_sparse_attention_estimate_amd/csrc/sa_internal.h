@@ -70,6 +70,8 @@ struct DecArgs {
   const uint16_t* ksum;
   const uint8_t* ksum_q4;    // nullable: 4-bit summary codes [B, nKB, Hkv, D/2] (scoring uses these)
   const uint16_t* ksum_scale;  // bf16 scales [B, nKB, Hkv, D/32] of the 4-bit codes
+  const uint8_t* ksum_exp;     // nullable: E8M0 exponents [B, nKB, Hkv, D/32] when ksum_q4
+                               // holds FP4 (MXFP4) codes instead of the 4-bit integer ones
   const int32_t* cache_len;
   uint16_t* o;
   float* lse;
@@ -87,6 +89,8 @@ hipError_t launch_estimate(const EstArgs& a, int granularity, hipStream_t s);
 hipError_t launch_anchor_state(const EstArgs& a, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs& a, int D, int granularity, hipStream_t s);
 hipError_t launch_block_summary(const DecArgs& a, hipStream_t s);
+hipError_t launch_summary_fp4(const uint16_t* ksum, uint8_t* codes, uint8_t* exps, int64_t n_groups,
+                              hipStream_t s);
 hipError_t launch_summary_q4(const uint16_t* ksum, uint8_t* codes, uint16_t* scales, int64_t n_groups,
                              hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);

@@ -264,6 +264,30 @@ sa_status sa_sparse_decode_q4(const sa_shape* shape, const sa_decode_params* par
                               const int32_t* cache_len, void* o, float* lse, int32_t* selected,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* FP4 block summaries (SpotAttention, "Key findings": the selector's key cache quantised to
+ * INT4 or FP4 microscale is 3.5x smaller at no accuracy cost), in the OCP Microscaling v1.0
+ * MXFP4 format.  From bf16 summaries (contiguous [B, ceil(seq_k/block_k), Hkv, d], as
+ * written by sa_build_block_summary) each row is cut into groups of 32 dims; a group with
+ * a = max |x| gets the shared exponent e = floor(log2 a) - 2 clamped to [-127, 127] (-127
+ * when a = 0 or a is subnormal) and each x the E2M1 code of |x| * 2^-e (grid 0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6 as codes 0..7, nearest with ties to the even code, saturating at 6) with the
+ * sign bit of x in bit 3, so the summary is read as code value * 2^e.
+ * codes: device uint8 [B, nKB, Hkv, d/2], dim 2k in the low and dim 2k+1 in the high nibble
+ * of byte k of its row; exps: device uint8 [B, nKB, Hkv, d/32], the E8M0 byte e + 127.
+ * 4.25 bits per dim.  Errors as sa_quantize_block_summary.  Asynchronous on the stream. */
+sa_status sa_quantize_block_summary_fp4(const sa_shape* shape, int32_t block_k,
+                                        const void* k_summary, void* codes, void* exps,
+                                        hipStream_t stream);
+
+/* sa_sparse_decode scoring the blocks from FP4 summaries (E2M1 value * 2^e per dim, from
+ * sa_quantize_block_summary_fp4) instead of bf16 ones; everything else as sa_sparse_decode,
+ * with the same workspace size.  SA_ERR_NULL for a null codes or exps pointer. */
+sa_status sa_sparse_decode_fp4(const sa_shape* shape, const sa_decode_params* params,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               const void* summary_codes, const void* summary_exps,
+                               const int32_t* cache_len, void* o, float* lse, int32_t* selected,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Per-head threshold calibration (SALE, "Assumptions & free parameters": the per-head
  * threshold tau starts at 0.008 and is halved until the L1 output error
  * Err(tau) = ||O - O~||_1 / N meets a user-chosen bound; the relative-score test keeps a

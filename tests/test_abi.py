@@ -150,6 +150,12 @@ def test_validation_codes(lib):
     assert lib.sa_sparse_decode_q4(*args_q4, FAKE, dneed, None) == _lib.SA_ERR_NULL
     args_q4[6] = FAKE
     assert lib.sa_sparse_decode_q4(*args_q4, FAKE, dneed - 1, None) == _lib.SA_ERR_WORKSPACE
+    assert lib.sa_quantize_block_summary_fp4(ctypes.byref(ds), 0, FAKE, FAKE, FAKE, None) == _lib.SA_ERR_PARAM
+    assert lib.sa_quantize_block_summary_fp4(ctypes.byref(ds), 64, FAKE, FAKE, None, None) == _lib.SA_ERR_NULL
+    args_fp4 = [ctypes.byref(ds), ctypes.byref(dp), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None]
+    assert lib.sa_sparse_decode_fp4(*args_fp4, FAKE, dneed, None) == _lib.SA_ERR_NULL
+    args_fp4[6] = FAKE
+    assert lib.sa_sparse_decode_fp4(*args_fp4, FAKE, dneed - 1, None) == _lib.SA_ERR_WORKSPACE
     assert lib.sa_workspace_size(_lib.SA_OP_PREFILL, ctypes.byref(s), ctypes.byref(p)) == 0
 
 

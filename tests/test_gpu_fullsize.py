@@ -132,7 +132,7 @@ def test_stripe_64k_sampled(dev):
     _prefill_parity(dev, "stripe_64k", n_rows=24, n_attn=10)
 
 
-@pytest.mark.parametrize("summary", ["bf16", "q4", "bf16-topp"])
+@pytest.mark.parametrize("summary", ["bf16", "q4", "fp4", "bf16-topp"])
 def test_decode_b16_128k(dev, summary):
     """bf16-topp: top_p = 0.5 with a cap of 256 blocks, which the budgets of this workload
     (about 80 to 200 blocks) stay under."""
@@ -144,7 +144,11 @@ def test_decode_b16_128k(dev, summary):
     q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
     cl = torch.from_numpy(x.cache_len).to(dev)
     kbar = sa.build_block_summary(kc, cl, block_k=x.block_k)
-    summ = sa.quantize_block_summary(kbar, block_k=x.block_k) if summary == "q4" else kbar
+    summ = kbar
+    if summary == "q4":
+        summ = sa.quantize_block_summary(kbar, block_k=x.block_k)
+    elif summary == "fp4":
+        summ = sa.quantize_block_summary_fp4(kbar, block_k=x.block_k)
     top_p, top_k = (0.5, 256) if summary == "bf16-topp" else (0.0, x.top_k)
     o, lse, sel = sa.sparse_decode(q, kc, vc, summ, cl, block_k=x.block_k, top_k=top_k,
                                    sink=x.sink, local=x.local, top_p=top_p)
@@ -159,6 +163,12 @@ def test_decode_b16_128k(dev, summary):
         np.testing.assert_array_equal(summ[0].cpu().numpy(), oracle.pack_q4(c_ref))
         np.testing.assert_array_equal(summ[1].view(torch.int16).cpu().numpy().view(np.uint16), s_ref)
         score_src = oracle.dequantize_summary_q4(c_ref, s_ref)
+    elif summary == "fp4":
+        v_ref, e_ref = oracle.quantize_summary_fp4(kbar_ref)
+        c_ref, eb_ref = oracle.pack_fp4(kbar_ref, v_ref, e_ref)
+        np.testing.assert_array_equal(summ[0].cpu().numpy(), c_ref)
+        np.testing.assert_array_equal(summ[1].cpu().numpy(), eb_ref)
+        score_src = oracle.dequantize_summary_fp4(v_ref, e_ref)
     ref = oracle.decode_select(x.q, score_src, x.cache_len, block_k=x.block_k, top_k=top_k,
                                sink=x.sink, local=x.local, top_p=top_p)
     s = sel.cpu().numpy()
