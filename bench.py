@@ -173,7 +173,7 @@ def to_dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def cpu_baseline_prefill(x, dense_flops, n_est_rows=512, n_attn_rows=512, seed=1):
+def cpu_baseline_prefill(x, dense_flops, n_est_rows=1024, n_attn_rows=1024, seed=1):
     """The oracle (numpy fp64) on a bounded random sample of the same workload: estimate
     rows (b, g, i) and attention query blocks (b, h, i) drawn uniformly, timed separately and
     scaled by total rows / sampled rows to a whole-layer time."""
