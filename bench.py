@@ -386,7 +386,8 @@ def bench_decode(args, dev):
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     top_k = args.top_k or x.top_k
-    kw = dict(block_k=x.block_k, top_k=top_k, sink=x.sink, local=x.local, top_p=args.top_p)
+    kw = dict(block_k=x.block_k, top_k=top_k, sink=x.sink, local=x.local, top_p=args.top_p,
+              n_splits=args.n_splits)
     o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
     n_sel = int((sel >= 0).sum().item())                 # blocks selected over all (b, g)
     for _ in range(args.warmup):
@@ -491,6 +492,8 @@ def main():
                     help="prefill: one theta for every head instead of the workload's")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="decode: per-(b, KV head) budget from the block-score distribution")
+    ap.add_argument("--n-splits", type=int, default=0,
+                    help="decode: splits per (b, KV head) (0: the library's choice)")
     ap.add_argument("--top-k", type=int, default=0,
                     help="decode: block cap (default: the workload's K)")
     ap.add_argument("--calibrate", action="store_true",
