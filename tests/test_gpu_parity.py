@@ -278,7 +278,8 @@ def test_decode_fp4_reduced(dev, batch, seq, hq, hkv, d, top_k):
                           (2, 3000, 8, 2, 128, 12, 64, 0.9, "bf16"),    # the cap of K binds
                           (2, 3000, 8, 2, 128, 94, 32, 0.7, "bf16"),
                           (2, 5000, 8, 2, 128, 79, 64, 0.02, "bf16"),   # forced share suffices
-                          (3, 5000, 8, 2, 128, 79, 64, 0.8, "q4")])
+                          (3, 5000, 8, 2, 128, 79, 64, 0.8, "q4"),
+                          (2, 3000, 4, 1, 64, 47, 64, 0.8, "fp4")])
 def test_decode_topp_reduced(dev, batch, seq, hq, hkv, d, top_k, bk, top_p, summary):
     """Top-p budget: per (b, g) the forced blocks plus the oracle's budget of content blocks
     (one off only where the oracle's cumulative share lies within its band of top_p), in the
@@ -292,13 +293,19 @@ def test_decode_topp_reduced(dev, batch, seq, hq, hkv, d, top_k, bk, top_p, summ
     q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
     cl = torch.from_numpy(x.cache_len).to(dev)
     kbar = sa.build_block_summary(kc, cl, block_k=bk)
-    summ = kbar if summary == "bf16" else sa.quantize_block_summary(kbar, block_k=bk)
+    summ = kbar
+    if summary == "q4":
+        summ = sa.quantize_block_summary(kbar, block_k=bk)
+    elif summary == "fp4":
+        summ = sa.quantize_block_summary_fp4(kbar, block_k=bk)
     o, lse, sel = sa.sparse_decode(q, kc, vc, summ, cl, block_k=bk, top_k=top_k, sink=32,
                                    local=256, top_p=top_p)
     torch.cuda.synchronize()
     kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, bk)
     if summary == "q4":
         kbar_ref = oracle.dequantize_summary_q4(*oracle.quantize_summary_q4(kbar_ref))
+    elif summary == "fp4":
+        kbar_ref = oracle.dequantize_summary_fp4(*oracle.quantize_summary_fp4(kbar_ref))
     ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=bk, top_k=top_k, sink=32,
                                local=256, top_p=top_p)
     used, off, flips = check_topp_selection(sel.cpu().numpy(), ref)
@@ -817,8 +824,10 @@ def test_prefill_arbitrary_lists(dev, granularity, bq):
     assert n_empty > 0 and err.max() < MAX_ABS and err.mean() < MEAN_ABS
 
 
-@pytest.mark.parametrize("bk,top_k,top_p", [(64, 8, 0.0), (64, 40, 0.0), (32, 12, 0.0), (64, 40, 0.6)])
-def test_decode_edge_lengths(dev, bk, top_k, top_p):
+@pytest.mark.parametrize("bk,top_k,top_p,summary", [(64, 8, 0.0, "bf16"), (64, 40, 0.0, "bf16"),
+                                                     (32, 12, 0.0, "bf16"), (64, 40, 0.6, "bf16"),
+                                                     (64, 8, 0.0, "q4"), (64, 8, 0.0, "fp4")])
+def test_decode_edge_lengths(dev, bk, top_k, top_p, summary):
     """Cache lengths at the edges: one token, the sink boundary, block boundaries, the window
     boundary and a full cache, in one batch (selection, summaries and attention)."""
     import torch
@@ -829,7 +838,12 @@ def test_decode_edge_lengths(dev, bk, top_k, top_p):
     q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
     cl = torch.from_numpy(x.cache_len).to(dev)
     kbar = sa.build_block_summary(kc, cl, block_k=bk)
-    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=bk, top_k=top_k, sink=32, local=256,
+    summ = kbar
+    if summary == "q4":
+        summ = sa.quantize_block_summary(kbar, block_k=bk)
+    elif summary == "fp4":
+        summ = sa.quantize_block_summary_fp4(kbar, block_k=bk)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, summ, cl, block_k=bk, top_k=top_k, sink=32, local=256,
                                    top_p=top_p)
     torch.cuda.synchronize()
     kbar_ref = oracle.block_summary(x.k_cache, x.cache_len, bk)
@@ -837,7 +851,12 @@ def test_decode_edge_lengths(dev, bk, top_k, top_p):
     for b, L in enumerate(lens):
         nb = -(-L // bk)
         np.testing.assert_array_equal(kb[b, :nb], kbar_ref[b, :nb])
-    ref = oracle.decode_select(x.q, kbar_ref, x.cache_len, block_k=bk, top_k=top_k, sink=32,
+    score_src = kbar_ref
+    if summary == "q4":
+        score_src = oracle.dequantize_summary_q4(*oracle.quantize_summary_q4(kbar_ref))
+    elif summary == "fp4":
+        score_src = oracle.dequantize_summary_fp4(*oracle.quantize_summary_fp4(kbar_ref))
+    ref = oracle.decode_select(x.q, score_src, x.cache_len, block_k=bk, top_k=top_k, sink=32,
                                local=256, top_p=top_p)
     s = sel.cpu().numpy()
     if top_p > 0:
