@@ -61,13 +61,27 @@ def _check_bf16(name, t, ndim):
         raise ValueError(f"{name} must be {ndim}-D with a contiguous last dimension")
 
 
-def _prefill_shape(q, k, v=None, o=None) -> _lib.SaShape:
+def _head_map(s: _lib.SaShape, kv_head_of_q) -> None:
+    """Attach the GQA head map (query head -> KV head) to the shape; None keeps the default
+    h // (Hq // Hkv).  The ctypes array lives as long as the shape."""
+    if kv_head_of_q is None:
+        return
+    m = [int(x) for x in (kv_head_of_q.tolist() if hasattr(kv_head_of_q, "tolist") else kv_head_of_q)]
+    if len(m) != s.n_q_heads:
+        raise ValueError("kv_head_of_q needs one entry per query head")
+    arr = (ctypes.c_int32 * len(m))(*m)
+    s.kv_head_of_q = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    s._keep_map = arr
+
+
+def _prefill_shape(q, k, v=None, o=None, kv_head_of_q=None) -> _lib.SaShape:
     _check_bf16("q", q, 4)
     _check_bf16("k", k, 4)
     B, N, Hq, D = q.shape
     s = _lib.SaShape()
     s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = B, Hq, k.shape[2], D
     s.seq_q, s.seq_k = N, k.shape[1]
+    _head_map(s, kv_head_of_q)
     s.q_stride[:] = q.stride()[:3]
     s.k_stride[:] = k.stride()[:3]
     vv = v if v is not None else k
@@ -158,10 +172,10 @@ def alloc_anchor_state(q) -> AnchorState:
 
 def workspace_size(op, *, q=None, k=None, block_q=128, block_k=64, sink=32, local=256,
                    granularity="block", theta=None, estimator="pooled", shape=None,
-                   decode_params=None) -> int:
+                   decode_params=None, kv_head_of_q=None) -> int:
     lib = _lib.load()
     if op in (SA_OP_ESTIMATE, SA_OP_CALIBRATE, SA_OP_ESTIMATE_STATE):
-        s = _prefill_shape(q, k)
+        s = _prefill_shape(q, k, kv_head_of_q=kv_head_of_q)
         p, keep = _sparse_params(block_q, block_k, sink, local, granularity,
                                  theta if theta is not None else 0.0, 0.0, q.shape[2], estimator)
         return int(lib.sa_workspace_size(op, ctypes.byref(s), ctypes.byref(p)))
@@ -191,14 +205,14 @@ def alloc_lists(q, k, *, block_q, block_k=64, granularity="block", stride=None,
 def estimate_mask(q, k, theta, *, block_q=128, block_k=64, sink=32, local=256,
                   granularity="block", softmax_scale=0.0, stride=None, margins=False,
                   estimator="pooled", step=1, workspace=None, out: Lists | None = None,
-                  stream=None) -> Lists:
+                  kv_head_of_q=None, stream=None) -> Lists:
     """Estimation pass (sa_estimate_mask).  q [B, N, Hq, d], k [B, N, Hkv, d] bf16 CUDA
     tensors; theta scalar or [Hq] in logit units; estimator "pooled" (anchor vs pooled
     query), "relative" (element-wise int8 estimate against the row's sink-local log-sum-exp)
     or "relative_mxfp4" (the same with MXFP4 operands on the block-scaled fp4 MFMA);
     step > 1 identifies query blocks in groups of `step` (AnchorAttention's step)."""
     lib = _lib.load()
-    s = _prefill_shape(q, k)
+    s = _prefill_shape(q, k, kv_head_of_q=kv_head_of_q)
     p, keep = _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale,
                              q.shape[2], estimator, step)
     lists = out if out is not None else alloc_lists(q, k, block_q=block_q, block_k=block_k,
@@ -216,13 +230,13 @@ def estimate_mask(q, k, theta, *, block_q=128, block_k=64, sink=32, local=256,
 
 
 def sparse_prefill(q, k, v, lists: Lists, *, block_q=128, block_k=64, sink=32, local=256,
-                   softmax_scale=0.0, out=None, lse=True, stream=None):
+                   softmax_scale=0.0, out=None, lse=True, kv_head_of_q=None, stream=None):
     """Block/stripe-sparse attention over given lists (sa_sparse_prefill).
     Returns (o [B, N, Hq, d] bf16, lse [B, Hq, N] fp32 or None)."""
     lib = _lib.load()
     _check_bf16("v", v, 4)
     o = out if out is not None else torch.empty_like(q)
-    s = _prefill_shape(q, k, v, o)
+    s = _prefill_shape(q, k, v, o, kv_head_of_q=kv_head_of_q)
     p, keep = _sparse_params(block_q, block_k, sink, local, lists.granularity, None,
                              softmax_scale, q.shape[2])
     lse_t = None
@@ -240,13 +254,13 @@ def sparse_prefill(q, k, v, lists: Lists, *, block_q=128, block_k=64, sink=32, l
 def estimate_mask_anchor_state(q, k, v, theta, *, block_q=128, block_k=64, sink=32, local=256,
                                softmax_scale=0.0, margins=False, step=1, workspace=None,
                                out: Lists | None = None, state: AnchorState | None = None,
-                               stream=None):
+                               kv_head_of_q=None, stream=None):
     """Estimation pass with the anchor state (sa_estimate_mask_anchor_state; pooled
     estimator, block lists).  Returns (lists, state): the lists equal estimate_mask's, and
     the state holds the attention over each row's anchor region for sparse_prefill_resume."""
     lib = _lib.load()
     _check_bf16("v", v, 4)
-    s = _prefill_shape(q, k, v)
+    s = _prefill_shape(q, k, v, kv_head_of_q=kv_head_of_q)
     p, keep = _sparse_params(block_q, block_k, sink, local, "block", theta, softmax_scale,
                              q.shape[2], "pooled", step)
     lists = out if out is not None else alloc_lists(q, k, block_q=block_q, block_k=block_k,
@@ -267,14 +281,15 @@ def estimate_mask_anchor_state(q, k, v, theta, *, block_q=128, block_k=64, sink=
 
 
 def sparse_prefill_resume(q, k, v, lists: Lists, state: AnchorState, *, block_q=128, block_k=64,
-                          sink=32, local=256, softmax_scale=0.0, out=None, lse=True, stream=None):
+                          sink=32, local=256, softmax_scale=0.0, out=None, lse=True,
+                          kv_head_of_q=None, stream=None):
     """Block-sparse attention that starts from the anchor state and skips each row's anchor
     region (sa_sparse_prefill_resume).  Returns (o [B, N, Hq, d] bf16, lse [B, Hq, N] fp32 or
     None)."""
     lib = _lib.load()
     _check_bf16("v", v, 4)
     o = out if out is not None else torch.empty_like(q)
-    s = _prefill_shape(q, k, v, o)
+    s = _prefill_shape(q, k, v, o, kv_head_of_q=kv_head_of_q)
     p, keep = _sparse_params(block_q, block_k, sink, local, lists.granularity, None,
                              softmax_scale, q.shape[2])
     lse_t = None
@@ -294,7 +309,7 @@ def sparse_prefill_resume(q, k, v, lists: Lists, state: AnchorState, *, block_q=
 
 def calibrate_theta(q, k, v, *, tau0=0.008, err_bound=0.4, max_halvings=16, block_q=128,
                     block_k=64, sink=32, local=256, softmax_scale=0.0, estimator="pooled",
-                    workspace=None, stream=None):
+                    workspace=None, kv_head_of_q=None, stream=None):
     """Per-head theta calibration (sa_calibrate_theta; block granularity).  Returns
     (theta [Hq] float32, err [Hq] float32, halvings [Hq] int32) as numpy arrays: theta_h =
     -ln(tau0) + halvings_h * ln 2, err_h = sum |O - O~| over the head's rows and dims / rows.
@@ -302,7 +317,7 @@ def calibrate_theta(q, k, v, *, tau0=0.008, err_bound=0.4, max_halvings=16, bloc
     import numpy as np
     lib = _lib.load()
     _check_bf16("v", v, 4)
-    s = _prefill_shape(q, k, v, q)
+    s = _prefill_shape(q, k, v, q, kv_head_of_q=kv_head_of_q)
     p, keep = _sparse_params(block_q, block_k, sink, local, "block", 0.0, softmax_scale,
                              q.shape[2], estimator)
     need = int(lib.sa_workspace_size(SA_OP_CALIBRATE, ctypes.byref(s), ctypes.byref(p)))
@@ -321,13 +336,14 @@ def calibrate_theta(q, k, v, *, tau0=0.008, err_bound=0.4, max_halvings=16, bloc
             np.array(halv, dtype=np.int32))
 
 
-def _decode_shape(q, k_cache, v_cache, o=None) -> _lib.SaShape:
+def _decode_shape(q, k_cache, v_cache, o=None, kv_head_of_q=None) -> _lib.SaShape:
     _check_bf16("q", q, 3)
     _check_bf16("k_cache", k_cache, 4)
     B, Hq, D = q.shape
     s = _lib.SaShape()
     s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = B, Hq, k_cache.shape[2], D
     s.seq_q, s.seq_k = 1, k_cache.shape[1]
+    _head_map(s, kv_head_of_q)
     s.q_stride[:] = (q.stride(0), 0, q.stride(1))
     s.k_stride[:] = k_cache.stride()[:3]
     vv = v_cache if v_cache is not None else k_cache
@@ -390,7 +406,7 @@ def quantize_block_summary_fp4(k_summary, *, block_k=64, seq_k=None, stream=None
 
 def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_k=64, sink=32,
                   local=256, n_splits=0, softmax_scale=0.0, top_p=0.0, workspace=None, out=None,
-                  return_selected=True, stream=None):
+                  return_selected=True, kv_head_of_q=None, stream=None):
     """Top-K block-sparse decode (sa_sparse_decode; sa_sparse_decode_q4 when k_summary is the
     (codes, scales) pair of quantize_block_summary, sa_sparse_decode_fp4 when it is the
     (codes, exps) pair of quantize_block_summary_fp4).  q [B, Hq, d]; caches [B, L, Hkv, d].
@@ -401,7 +417,7 @@ def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_
     lib = _lib.load()
     _check_bf16("v_cache", v_cache, 4)
     o = out if out is not None else torch.empty_like(q)
-    s = _decode_shape(q, k_cache, v_cache, o)
+    s = _decode_shape(q, k_cache, v_cache, o, kv_head_of_q=kv_head_of_q)
     p = _lib.SaDecodeParams()
     p.block_k, p.top_k_blocks, p.sink_tokens, p.local_tokens = block_k, top_k, sink, local
     p.n_splits, p.softmax_scale = n_splits, float(softmax_scale or 0.0)

@@ -29,6 +29,7 @@ class SaShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("seq_q", ctypes.c_int32), ("seq_k", ctypes.c_int32),
+                ("kv_head_of_q", ctypes.POINTER(ctypes.c_int32)),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
                 ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
 

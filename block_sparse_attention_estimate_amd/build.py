@@ -42,5 +42,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(OBJ, "libsa_hostsan.so")
+# host-side sanitizers for the C ABI's validation code: each -fsanitize= goes to the host
+# pass only (-Xarch_host); the device code is compiled as in the product build
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that the sanitized library needs preloaded."""
+    clang = os.path.join(os.path.dirname(HIPCC), "..", "llvm", "bin", "clang")
+    r = _run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"])
+    return r.stdout.strip()
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libsa with the host code of the C ABI (sa_api.hip: argument validation, workspace
+    carve-out, launches) built with AddressSanitizer and UndefinedBehaviorSanitizer; the kernel
+    objects are those of the product build (build() first).  For CPU tests of the validation
+    paths only: loading it needs the ASan runtime preloaded (asan_runtime())."""
+    os.makedirs(OBJ, exist_ok=True)
+    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "sa_api.hip"]
+    for o in objs:
+        if not os.path.exists(o):
+            raise RuntimeError("build() the product library first: " + o)
+    api_o = os.path.join(OBJ, "sa_api_hostsan.o")
+    _run([HIPCC, *FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, "sa_api.hip"), "-o", api_o])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-fsanitize=address",
+          "-fsanitize=undefined", "-shared-libsan", "-o", SAN_LIB, api_o, *objs])
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)

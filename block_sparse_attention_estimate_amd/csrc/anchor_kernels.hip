@@ -84,12 +84,13 @@ __global__ __launch_bounds__(64 * AS_WAVES) void est_anchor_state(EstArgs a) {
     const int hg = nt / ntph, tr = nt % ntph;
     const int ra = r0 + tr * 32;
     const bool active = nt < G * ntph && ra < r1;   // uniform per wave
-    const int h = g * G + hg;
+    const int h = g * G + hg;          // packed head (index of the anchors handed to the estimate)
+    const int hq = a.qh[h];            // its query head (index of Q and of the state)
     const int row = ra + l32;
     bf16x8 qf[KS];
     if (active) {
       const int rowc = min(row, a.N - 1);
-      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + h * a.qs2 + half * 8;
+      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + hq * a.qs2 + half * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
     }
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(64 * AS_WAVES) void est_anchor_state(EstArgs a) {
     if (row < r1) {
       // every row's region holds its diagonal key, so lt >= 1 and m_run is finite
       const float inv = 1.0f / lt;
-      uint16_t* op = a.st_o + (((int64_t)b * a.N + row) * a.Hq + h) * D + half * 4;
+      uint16_t* op = a.st_o + (((int64_t)b * a.N + row) * a.Hq + hq) * D + half * 4;
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
@@ -212,9 +213,8 @@ __global__ __launch_bounds__(64 * AS_WAVES) void est_anchor_state(EstArgs a) {
           *(u32x2*)(op + dm * 32 + 8 * q4) = (u32x2){w0, w1};
         }
       if (half == 0) {
-        const int64_t sr = ((int64_t)b * a.Hq + h) * a.N + row;
-        a.st_lse[sr] = (m_run + __log2f(lt)) * 0.69314718055994531f;
-        a.xa[sr] = __fmul_rn(mx, a.c);
+        a.st_lse[((int64_t)b * a.Hq + hq) * a.N + row] = (m_run + __log2f(lt)) * 0.69314718055994531f;
+        a.xa[((int64_t)b * a.Hq + h) * a.N + row] = __fmul_rn(mx, a.c);
       }
     }
   }

@@ -40,8 +40,11 @@
 //    k0..k0+3 of dim d0 + i -- exactly the 4 keys the P^T register layout pairs with that lane.
 // ---------------------------------------------------------------------------------------
 
-template <int D, int HPW, bool RESUME, bool STRIPE>
+// MODE: 0 = lists of 64-key blocks; 1 = lists of key columns (stripes); 2 = lists of 32-key
+// blocks (two listed blocks per 64-key tile, gathered like columns)
+template <int D, int HPW, bool RESUME, int MODE>
 __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
+  constexpr bool STRIPE = MODE == 1, BK32 = MODE == 2, GATHER = MODE != 0;
   // The host pass only needs this kernel's signature (for its launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NWV = 2 * HPW;             // waves: 2 slices of 32 rows per head
@@ -91,7 +94,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   const int r0 = iq * a.bq + tsub * 64;
   if (iq < 0 || r0 >= a.N) return;
   const int r_last = min(r0 + 63, a.N - 1);
-  const int h = g * a.G + hp * HPW + (wave >> 1);
+  // query head of this wave (packed head g * G + j of the workgroup's KV head)
+  const int h = a.qh[g * a.G + hp * HPW + (wave >> 1)];
   const int rw = r0 + (wave & 1) * 32;
   const int row = rw + l32;
 
@@ -116,6 +120,16 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
     ntile = (n + 63) / 64;
     n_main = ntile;
     while (n_main > 0 && (list[min(n_main * 64, n) - 1] > r0 || n_main * 64 > n)) --n_main;
+  } else if (BK32) {
+    // 32-key block lists: two listed blocks per tile; blocks from `r_last + 1` on hold no key
+    // of this work item; the tiles from n_main on need a mask (a block past the first row's
+    // diagonal or the end, or the empty second half of the last tile)
+    while (n > 0 && list[n - 1] * 32 >= r_last + 1) --n;
+    ntile = (n + 1) / 2;
+    n_main = ntile;
+    while (n_main > 0 && (2 * n_main > n || list[2 * n_main - 1] * 32 + 31 >= r0 + 1 ||
+                          list[2 * n_main - 1] * 32 + 31 >= a.N))
+      --n_main;
   } else {
     // Tiles past `cut` hold no key this work item needs: causally masked for every row, or (when
     // resuming) causally masked or inside every row's local window, which the anchor state holds.
@@ -152,24 +166,35 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   const int64_t tstride = dma_v ? a.vs1 : a.ks1;       // elements between key rows
   const uint16_t* gbase = dma_v ? a.v + b * a.vs0 + g * a.vs2 : a.k + b * a.ks0 + g * a.ks2;
   const int region = dma_v ? KREG : 0;
-  int s_off[SLOTS];                                    // element offset in a full tile
-  int s_row[STRIPE ? SLOTS : 1];                       // (gathered tiles) row of this lane's bytes
+  const int nkb = (a.N + 63) >> 6;                     // key blocks of the sequence
+  // Block lists: byte offset of this lane's 16 bytes within a tile (row r of the window's
+  // bytes, column cb; pads get a harmless copy of the row start), added to the tile's
+  // wave-uniform base address, so the loads take a scalar base and one 32-bit offset.
+  // Column lists: the row of this lane's bytes and their element offset within the row.
+  uint32_t s_voff[SLOTS];
+  int s_off[GATHER ? SLOTS : 1];
+  int s_row[GATHER ? SLOTS : 1];
 #pragma unroll
   for (int k = 0; k < SLOTS; ++k) {
     const int o = min(wbase + k, nwin - 1) * 1024 + lane * 16;
     const int r = o / pitch_b, cb = o % pitch_b;
-    if (STRIPE) {
+    const int cbytes = cb < ROWB ? cb : 0;
+    if (GATHER) {
       s_row[k] = r;
-      s_off[k] = (cb < ROWB ? cb / 16 : 0) * 8;       // column offset within the row
-    } else {
-      s_off[k] = r * (int)tstride + (cb < ROWB ? cb / 16 : 0) * 8;   // pads get a harmless copy
+      s_off[k] = cbytes / 2;
     }
+    s_voff[k] = (uint32_t)((int64_t)r * tstride * 2 + cbytes);
   }
-  // What the DMA of tile t needs, read one step ahead of the issue: the key block id (block
-  // lists; a scalar load), or this lane's column id per slot (column lists; vector loads, rows
+  // LDS window of slot k in the stage at stb (windows past NWIN go to `spare`)
+  auto dst = [&](unsigned char* stb, int k) -> unsigned char* {
+    return wbase + k < nwin ? stb + region + (wbase + k) * 1024 : spare;
+  };
+  // What the DMA of tile t needs, read ahead of the issue: the key block id (block lists; a
+  // scalar load, clamped to the sequence's blocks so a bad entry cannot address memory
+  // outside K and V), or this lane's column id per slot (column lists; vector loads, rows
   // past the list's end repeat its last entry).
   struct Src {
-    int v[STRIPE ? SLOTS : 1];
+    int v[STRIPE ? SLOTS : (BK32 ? 2 : 1)];
   };
   auto fetch = [&](int t) -> Src {
     Src sv;
@@ -177,49 +202,58 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
       const int tt = min(t, ntile - 1);
 #pragma unroll
       for (int k = 0; k < SLOTS; ++k) sv.v[k] = list_g[min(tt * 64 + s_row[k], n - 1)];
+    } else if constexpr (BK32) {
+      // the tile's two 32-key blocks (the second -1 when the list ends in the first); ids
+      // clamped to the sequence's blocks
+      const int tt = min(t, ntile - 1);
+      const int nb32 = (a.N + 31) >> 5;
+      sv.v[0] = min(max(list[2 * tt], 0), nb32 - 1);
+      sv.v[1] = 2 * tt + 1 < n ? min(max(list[2 * tt + 1], 0), nb32 - 1) : -1;
     } else {
-      sv.v[0] = list[min(t, ntile - 1)];
+      sv.v[0] = min(max(list[min(t, ntile - 1)], 0), nkb - 1);
     }
     return sv;
   };
-  // Issue the DMA of tile t (clamped to the list) into the stage at stb.  Every wave issues exactly
-  // SLOTS loads per call, so the vmcnt waits below are compile-time constants.
+  // Issue the DMA of a tile into the stage at stb.  Every wave issues exactly SLOTS loads per
+  // call, so the vmcnt waits below are compile-time constants.
   auto issue = [&](unsigned char* stb, const Src& sv) {
-    if constexpr (STRIPE) {
+    if constexpr (GATHER) {
 #pragma unroll
       for (int k = 0; k < SLOTS; ++k) {
-        const int tok = min(max(sv.v[k], 0), a.N - 1);
+        int tok;
+        if constexpr (STRIPE) {
+          tok = sv.v[k];
+        } else {
+          // row r of the tile: row r % 32 of the tile's first or second block (an empty
+          // second half reads the first block's rows: a harmless copy, masked)
+          const int blk = s_row[k] < 32 || sv.v[1] < 0 ? sv.v[0] : sv.v[1];
+          tok = blk * 32 + (s_row[k] & 31);
+        }
+        tok = min(max(tok, 0), a.N - 1);
         const uint16_t* src = gbase + (int64_t)tok * tstride + s_off[k];
-        if (wbase + k < nwin)
-          __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, stb + region + (wbase + k) * 1024), 16, 0, 0);
-        else
-          __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, spare), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, dst(stb, k)), 16, 0, 0);
       }
       return;
     }
-    const int jb = sv.v[0];
-    const int t0 = jb * 64;
-    if (t0 + 63 < a.N) {
-      const uint16_t* tb = gbase + (int64_t)t0 * tstride;
+    // block lists: one buffer resource per tile (base = the tile's first row, in scalar
+    // registers), the lane's 32-bit offset within the tile, the range = the tile's rows
+    const int t0 = sv.v[0] * 64;
+    const int last = min(63, a.N - 1 - t0);             // last row of the tile in the sequence
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(gbase + (int64_t)t0 * tstride), 0, (int)((int64_t)last * tstride * 2 + ROWB),
+        0x00020000);
+    if (last == 63) {
 #pragma unroll
-      for (int k = 0; k < SLOTS; ++k) {
-        if (wbase + k < nwin)
-          __builtin_amdgcn_global_load_lds(tb + s_off[k], LDS_PTR(void, stb + region + (wbase + k) * 1024), 16, 0, 0);
-        else
-          __builtin_amdgcn_global_load_lds(tb + s_off[k], LDS_PTR(void, spare), 16, 0, 0);
-      }
+      for (int k = 0; k < SLOTS; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, dst(stb, k)), 16, (int)s_voff[k], 0, 0, 0);
     } else {
       // ragged last block: rows past the end read the last row
 #pragma unroll
       for (int k = 0; k < SLOTS; ++k) {
         const int o = min(wbase + k, nwin - 1) * 1024 + lane * 16;
-        const int r = o / pitch_b;
-        const int tok = min(t0 + r, a.N - 1);
-        const uint16_t* src = gbase + (int64_t)tok * tstride + (s_off[k] - r * (int)tstride);
-        if (wbase + k < nwin)
-          __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, stb + region + (wbase + k) * 1024), 16, 0, 0);
-        else
-          __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, spare), 16, 0, 0);
+        const int r = dma_v ? o / VPITCH : o / KPITCH;
+        const int back = (int)((int64_t)max(r - last, 0) * tstride * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, dst(stb, k)), 16, (int)s_voff[k] - back, 0, 0, 0);
       }
     }
   };
@@ -235,6 +269,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   float m_run = -1e30f, l_run = 0.f;
   const float sl2 = a.scale_log2;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
   if (RESUME) {
     // Start from the anchor state: with its log-sum-exp as the reference point the state is
@@ -256,21 +291,128 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   }
 
   // ---- the phases of a tile ----
-  // S^T = K Q^T from the stage at sb
+  // K fragment i of S^T = K Q^T (key half i & 1, k-step i >> 1) from the stage at sb
+  auto kread = [&](const unsigned char* sb, int i) -> bf16x8 {
+    return *(const bf16x8*)(sb + k_rd + (i & 1) * 32 * KPITCH + (i >> 1) * 32);
+  };
+  // V^T fragment i of key half mt (16-key group 2 mt + i / DM, d tile i % DM), read with two
+  // transposing LDS reads
+  auto vread = [&](const unsigned char* sb, int mt, int i) -> bf16x8 {
+    const int s4 = 2 * mt + i / DM, dm = i % DM;
+    const unsigned char* vp = sb + v_rd + 16 * s4 * VPITCH + dm * 64;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp + 8 * VPITCH));
+    const v4i16 both[2] = {lo, hi};
+    bf16x8 vf;
+    __builtin_memcpy(&vf, both, 16);
+    return vf;
+  };
+  // P^T is kept as packed bf16 pairs: pw[8 mt + 4 s2 + k] holds entries 8 s2 + 2k and
+  // 8 s2 + 2k + 1 of key half mt of the lane's S^T column; B operand of 16-key group s4
+  auto pfrag = [&](const uint32_t* pw, int s4) -> bf16x8 {
+    const u32x4 w4 = {pw[4 * s4], pw[4 * s4 + 1], pw[4 * s4 + 2], pw[4 * s4 + 3]};
+    bf16x8 f;
+    __builtin_memcpy(&f, &w4, 16);
+    return f;
+  };
+  // P entry e of key half mt: exp2(S scale - m); at odd e the pair is rounded to bf16, stored
+  // and added to the lane's partial row sum (the sum of the values P V uses)
+  auto exp_elem = [&](const f32x16* sacc, int mt, int e, float mneg, float* xs, uint32_t* pw,
+                      float& ls) {
+    xs[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][e], sl2, mneg));
+    if (e & 1) {
+      const f32x2 x2 = {xs[e - 1], xs[e]};
+      const bf16x2 pr = __builtin_convertvector(x2, bf16x2);
+      pw[8 * mt + e / 2] = __builtin_bit_cast(uint32_t, pr);
+      ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
+    }
+  };
+  // P^T of key half mt in one go; returns this lane's sum of the rounded values
+  auto expo = [&](const f32x16* sacc, int mt, uint32_t* pw) -> float {
+    const float mneg = -m_run;
+    float xs[16], ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) exp_elem(sacc, mt, e, mneg, xs, pw, ls);
+    return ls;
+  };
+  // S^T = K Q^T from the stage at sb (no other work: the first tile)
   auto qk = [&](const unsigned char* sb, f32x16* sacc) {
     sacc[0] = (f32x16){};
     sacc[1] = (f32x16){};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 kf = *(const bf16x8*)(sb + k_rd + mt * 32 * KPITCH + ks * 32);
-        sacc[mt] = mfma_bf16(kf, qf[ks], sacc[mt]);
-      }
+    for (int i = 0; i < 2 * KS; ++i) sacc[i & 1] = mfma_bf16(kread(sb, i), qf[i >> 1], sacc[i & 1]);
   };
+  // The phases of a step are written in issue order and fenced (sched_barrier), so that every
+  // LDS read is issued several MFMAs ahead of its use and the softmax VALU work is spread
+  // between the MFMAs of the same wave.
+  // S(t+1) = K(t+1) Q^T from the stage at sb, with P(t)'s first key half: four K fragments in
+  // flight, then per MFMA the next fragment's read and the exponentials of the next MFMA's share.
+  auto qk_exp = [&](const unsigned char* sb, f32x16* nxt, const f32x16* cur, uint32_t* pw) -> float {
+    constexpr int NF = 2 * KS, AH = 4, EPM = 16 / NF;
+    const float mneg = -m_run;
+    float xs[16], ls = 0.f;
+    bf16x8 kf[AH];
+#pragma unroll
+    for (int i = 0; i < AH; ++i) kf[i] = kread(sb, i);
+#pragma unroll
+    for (int j = 0; j < EPM; ++j) exp_elem(cur, 0, j, mneg, xs, pw, ls);
+    nxt[0] = (f32x16){};
+    nxt[1] = (f32x16){};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      nxt[i & 1] = mfma_bf16(kf[i % AH], qf[i >> 1], nxt[i & 1]);
+      if (i + AH < NF) kf[i % AH] = kread(sb, i + AH);
+      if (i + 1 < NF) {
+#pragma unroll
+        for (int j = 0; j < EPM; ++j) exp_elem(cur, 0, (i + 1) * EPM + j, mneg, xs, pw, ls);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return ls;
+  };
+  // O^T += V^T P^T over key half mt from the stage at sb: three V fragments in flight, then per
+  // MFMA the next fragment's reads and (with_exp) the exponentials of P(t)'s second half.
+  auto pv_exp = [&](const unsigned char* sb, int mt, uint32_t* pw, const f32x16* cur,
+                    bool with_exp, auto&& extra) -> float {
+    constexpr int NF = 2 * DM, AH = 3, EPM = 16 / NF;
+    const float mneg = -m_run;
+    float xs[16], ls = 0.f;
+    bf16x8 vf[AH];
+#pragma unroll
+    for (int i = 0; i < AH; ++i) vf[i] = vread(sb, mt, i);
+    if (with_exp) {
+#pragma unroll
+      for (int j = 0; j < EPM; ++j) exp_elem(cur, 1, j, mneg, xs, pw, ls);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      oacc[i % DM] = mfma_bf16(vf[i % AH], pfrag(pw, 2 * mt + i / DM), oacc[i % DM]);
+      if (i + AH < NF) vf[i % AH] = vread(sb, mt, i + AH);
+      if (with_exp && i + 1 < NF) {
+#pragma unroll
+        for (int j = 0; j < EPM; ++j) exp_elem(cur, 1, (i + 1) * EPM + j, mneg, xs, pw, ls);
+      }
+      extra(i, NF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return ls;
+  };
+  auto no_extra = [](int, int) {};
   // entries of tile t past the diagonal or the end of the sequence (resuming: also those in
   // the row's anchor region, which the state already holds; the window includes the diagonal)
-  auto mask = [&](int t, f32x16* sacc) {
+  // token of entry (mt, r) of a block-list tile with source ids js (-1: no token)
+  auto tile_tok = [&](const Src& js, int mt, int r) -> int {
+    const int key = mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+    if constexpr (BK32) {
+      const int blk = mt == 0 ? js.v[0] : js.v[1];
+      return blk < 0 ? -1 : blk * 32 + (key & 31);
+    } else {
+      return js.v[0] * 64 + key;
+    }
+  };
+  auto mask = [&](int t, const Src& js, f32x16* sacc) {
     if constexpr (STRIPE) {
       // the tile's 64 column ids, lane i holding entry 64 t + i (past the list's end: none)
       const int e = t * 64 + lane;
@@ -284,43 +426,23 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
         }
       return;
     }
-    const int Jb = list[t];
+    (void)t;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int tok = Jb * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
+        const int tok = tile_tok(js, mt, r);
         const bool drop = RESUME ? (tok < a.sink || tok >= row - a.local + 1 || tok >= a.N)
-                                 : (tok > row || tok >= a.N);
+                                 : (tok < 0 || tok > row || tok >= a.N);
         if (drop) sacc[mt][r] = NEG_INF;
       }
-  };
-  // P^T of key half mt = exp2(S^T scale - m) in bf16 (pf[2 mt], pf[2 mt + 1]); returns this
-  // lane's sum of the rounded values
-  auto expo = [&](const f32x16* sacc, int mt, bf16x8* pf) -> float {
-    const float mneg = -m_run;
-    float ls = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      f32x8 tt;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * s2 + e], sl2, mneg));
-      const bf16x8 pb = __builtin_convertvector(tt, bf16x8);
-      pf[mt * 2 + s2] = pb;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 pr = {pb[e], pb[e + 1]};
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
-      }
-    }
-    return ls;
   };
   // The running max m stays fixed while every P value of a key half is at most 2^16 (checked
   // on the lane's partial row sum, which bounds each value).  A half that breaks the bound
   // (scores more than 16 above m in the log2 domain, or the first tile, while m is still
   // -1e30) moves m to the half's row max, rescales O and l -- which may already hold the other
   // half's P V at the old m -- and recomputes its P.  No per-tile row max is taken.
-  auto settle = [&](const f32x16* sacc, int mt, bf16x8* pf, float ts) {
+  auto settle = [&](const f32x16* sacc, int mt, uint32_t* pw, float ts) {
     if (__any(!(ts <= 65536.0f))) {
       float v = NEG_INF;
 #pragma unroll
@@ -331,64 +453,51 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
       l_run *= alpha;
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
-      ts = expo(sacc, mt, pf);
+      ts = expo(sacc, mt, pw);
     }
     l_run += ts;
   };
-  // O^T += V^T P^T over the 16-key groups of key half mt, with transposing V reads from the
-  // stage at sb
-  auto pv = [&](const unsigned char* sb, int mt, const bf16x8* pf) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm) {
-        const int s4 = 2 * mt + s2;
-        const unsigned char* vp = sb + v_rd + 16 * s4 * VPITCH + dm * 64;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vp + 8 * VPITCH));
-        const v4i16 both[2] = {lo, hi};
-        bf16x8 vf;
-        __builtin_memcpy(&vf, both, 16);
-        oacc[dm] = mfma_bf16(vf, pf[s4], oacc[dm]);
-      }
-  };
 
-  // Software pipeline over the list.  On entry to step t, S(t) is in `cur` (masked) and tiles
-  // t+1 and t+2 are in LDS.  Step t computes P(t)'s first key half while the MFMAs of S(t+1)
-  // run, P(t)'s second half while P V of the first half runs, and P V of the second half,
-  // then issues the DMA of tile t+3 into the stage of tile t-1 and waits for tile t+2, so at
-  // every barrier only the newest tile is in flight.
+  // Software pipeline over the list.  On entry to step t, S(t) is in `cur` (masked), tiles t
+  // and t+1 are in LDS, tile t+2 is in flight and the stage of tile t-1 is free.  Step t issues
+  // the DMA of tile t+3 into that stage, computes P(t)'s first key half while the MFMAs of
+  // S(t+1) run, P(t)'s second half while P V of the first half runs, and P V of the second
+  // half, then waits for tile t+2: each tile has about two steps to arrive.  The list entries
+  // a step needs were read one step earlier (the scalar loads return under the barrier).
   if (ntile > 0) {
-    issue(st0, fetch(0));
-    issue(st1, fetch(1));
-    issue(st2, fetch(2));
+    const Src j0 = fetch(0), j1 = fetch(1), j2 = fetch(2);
+    issue(st0, j0);
+    issue(st1, j1);
+    issue(st2, j2);
+    Src jc = fetch(3);                 // DMA source of tile t+3
+    Src ja = j1, jb2 = j2;             // sources of tiles t+1 and t+2 (their masks)
     DMA_BARRIER(SLOTS);
     f32x16 sa[2], sbb[2];
     qk(st0, sa);
-    if (n_main == 0 || (RESUME && list[0] * 64 < a.sink)) mask(0, sa);
+    if (n_main == 0 || (RESUME && j0.v[0] * 64 < a.sink)) mask(0, j0, sa);
     auto step = [&](unsigned char* sc, unsigned char* sn, unsigned char* sd, int t,
                     f32x16* cur, f32x16* nxt, bool may_mask) {
-      const Src jd = fetch(t + 3);
-      bf16x8 pf[4];
-      const float t0s = expo(cur, 0, pf);
-      qk(sn, nxt);
-      settle(cur, 0, pf, t0s);
-      const float t1s = expo(cur, 1, pf);
-      pv(sc, 0, pf);
-      settle(cur, 1, pf, t1s);
-      pv(sc, 1, pf);
-      if (may_mask && t + 1 >= n_main) mask(t + 1, nxt);
-      issue(sd, jd);
+      issue(sd, jc);
+      const Src jd = fetch(t + 4);
+      uint32_t pw[16];
+      const float t0s = qk_exp(sn, nxt, cur, pw);
+      settle(cur, 0, pw, t0s);
+      const float t1s = pv_exp(sc, 0, pw, cur, true, no_extra);
+      settle(cur, 1, pw, t1s);
+      pv_exp(sc, 1, pw, cur, false, no_extra);
+      if (may_mask && t + 1 >= n_main) mask(t + 1, ja, nxt);
+      ja = jb2;
+      jb2 = jc;
+      jc = jd;
       DMA_BARRIER(SLOTS);
     };
     auto last = [&](unsigned char* sc, f32x16* cur) {
-      bf16x8 pf[4];
-      const float t0s = expo(cur, 0, pf);
-      settle(cur, 0, pf, t0s);
-      const float t1s = expo(cur, 1, pf);
-      pv(sc, 0, pf);
-      settle(cur, 1, pf, t1s);
-      pv(sc, 1, pf);
+      uint32_t pw[16];
+      const float t0s = expo(cur, 0, pw);
+      settle(cur, 0, pw, t0s);
+      const float t1s = pv_exp(sc, 0, pw, cur, true, no_extra);
+      settle(cur, 1, pw, t1s);
+      pv_exp(sc, 1, pw, cur, false, no_extra);
     };
     int t = 0;
     for (; t + 4 < n_main; t += 4) {          // the next tile of every step needs no mask
@@ -453,11 +562,13 @@ static hipError_t launch_block(const AttnArgs& a0, hipStream_t s) {
   a.total = a.B * a.Hkv * a.n_hp * a.nQB * a.tpb;
   if (a.total == 0) return hipSuccess;
   if (a.st_o)
-    hipLaunchKernelGGL((attn_block<D, HPW, true, false>), dim3(a.total), dim3(128 * HPW), 0, s, a);
+    hipLaunchKernelGGL((attn_block<D, HPW, true, 0>), dim3(a.total), dim3(128 * HPW), 0, s, a);
   else if (a.stripe)
-    hipLaunchKernelGGL((attn_block<D, HPW, false, true>), dim3(a.total), dim3(128 * HPW), 0, s, a);
+    hipLaunchKernelGGL((attn_block<D, HPW, false, 1>), dim3(a.total), dim3(128 * HPW), 0, s, a);
+  else if (a.bk32)
+    hipLaunchKernelGGL((attn_block<D, HPW, false, 2>), dim3(a.total), dim3(128 * HPW), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_block<D, HPW, false, false>), dim3(a.total), dim3(128 * HPW), 0, s, a);
+    hipLaunchKernelGGL((attn_block<D, HPW, false, 0>), dim3(a.total), dim3(128 * HPW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -468,8 +579,8 @@ static hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   return launch_block<D, 1>(a, s);
 }
 
-// Block and column lists both run attn_block; a.stripe (set from the granularity) selects the
-// instance that gathers listed rows.
+// Block and column lists both run attn_block; a.stripe (set from the granularity) and a.bk32
+// (32-key block lists) select the instances that gather listed rows.
 hipError_t launch_prefill(const AttnArgs& a, int D, int granularity, hipStream_t s) {
   (void)granularity;
   return D == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);

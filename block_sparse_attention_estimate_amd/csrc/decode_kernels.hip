@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void dec_score_rows(DecArgs a) {
   float qv[G][DPL];
 #pragma unroll
   for (int hg = 0; hg < G; ++hg) {
-    const uint16_t* qp = a.q + b * a.qs0 + (g * G + hg) * a.qs2 + sub * DPL;
+    const uint16_t* qp = a.q + b * a.qs0 + a.qh[g * G + hg] * a.qs2 + sub * DPL;
     if (DPL == 8) {
       const u16x8 u = *(const u16x8*)qp;
 #pragma unroll
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void dec_score_q4_mfma(DecArgs a) {
   float qs_l[NGR];                       // 136 * sum of head l % 32's dims in group gi
   {
     const int hc = min(l32, a.G - 1);
-    const uint16_t* qp = a.q + b * a.qs0 + (g * a.G + hc) * a.qs2 + half * 8;
+    const uint16_t* qp = a.q + b * a.qs0 + a.qh[g * a.G + hc] * a.qs2 + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = *(const bf16x8*)(qp + ks * 16);
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void dec_score_fp4_mfma(DecArgs a) {
   bf16x8 qf[KS];
   {
     const int hc = min(l32, a.G - 1);
-    const uint16_t* qp = a.q + b * a.qs0 + (g * a.G + hc) * a.qs2 + half * 8;
+    const uint16_t* qp = a.q + b * a.qs0 + a.qh[g * a.G + hc] * a.qs2 + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = *(const bf16x8*)(qp + ks * 16);
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(256) void dec_splitk(DecArgs a) {
   float qv[G][DPL];
 #pragma unroll
   for (int hg = 0; hg < G; ++hg) {
-    const uint16_t* qp = a.q + b * a.qs0 + (g * G + hg) * a.qs2 + sub * DPL;
+    const uint16_t* qp = a.q + b * a.qs0 + a.qh[g * G + hg] * a.qs2 + sub * DPL;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) qv[hg][e] = bf16_bits_to_float(qp[e]) * sl2;
   }
@@ -853,7 +853,7 @@ __global__ __launch_bounds__(256, 1) void dec_splitk_mfma(DecArgs a) {
   bf16x8 qf[KS];
   {
     const int hc = min(l32, a.G - 1);
-    const uint16_t* qp = a.q + b * a.qs0 + (g * a.G + hc) * a.qs2 + half * 8;
+    const uint16_t* qp = a.q + b * a.qs0 + a.qh[g * a.G + hc] * a.qs2 + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = *(const bf16x8*)(qp + ks * 16);
@@ -1051,9 +1051,10 @@ __global__ __launch_bounds__(D) void dec_combine(DecArgs a) {
       }
   }
   const float o = lt > 0.f ? at / lt : 0.f;
-  ((uint16_t*)a.o)[b * a.os0 + h * a.os2 + d] = float_to_bf16_bits(o);
+  const int hq = a.qh[h];                         // partials are kept per packed head
+  ((uint16_t*)a.o)[b * a.os0 + hq * a.os2 + d] = float_to_bf16_bits(o);
   if (a.lse && d == 0)
-    a.lse[(int64_t)b * a.Hq + h] = lt > 0.f ? (mx + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
+    a.lse[(int64_t)b * a.Hq + hq] = lt > 0.f ? (mx + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
 }
 
 // ---------------------------------------------------------------------------------------

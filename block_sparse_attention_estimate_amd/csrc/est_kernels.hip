@@ -31,7 +31,9 @@
 #define NEG_INF (-__builtin_huge_valf())
 
 // ---------------------------------------------------------------------------------------
-// int8 key tiles: a = max |K| over the tile, scale = a / 127, code = rint(K * (127 / a)).
+// int8 key blocks: a = max |K| over the block's keys (block_k = 64, or each 32-key half of the
+// 64-key tile when block_k = 32), scale = a / 127, code = rint(K * (127 / a)).
+// One workgroup per 64-key tile.
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void est_quant_k(EstArgs a) {
@@ -39,8 +41,10 @@ __global__ __launch_bounds__(256) void est_quant_k(EstArgs a) {
   constexpr int PER = 64 * CH / 256;     // chunks per thread (tile of 64 keys)
   const int J = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  // chunk c of this thread holds key J*64 + tid / CH + c * (256 / CH): the first half of the
+  // chunks lies in keys 0..31 of the tile, the second half in keys 32..63
   u16x8 v[PER];
-  float amax = 0.f;
+  float amax[2] = {0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
     const int ch = tid + c * 256;
@@ -52,35 +56,56 @@ __global__ __launch_bounds__(256) void est_quant_k(EstArgs a) {
       v[c] = (u16x8)(0);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf16_bits_to_float(v[c][e])));
+    for (int e = 0; e < 8; ++e)
+      amax[c / (PER / 2)] = fmaxf(amax[c / (PER / 2)], fabsf(bf16_bits_to_float(v[c][e])));
   }
-  __shared__ float red[4];
-  amax = wave_max(amax);
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __shared__ float red[2][4];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const float m = wave_max(amax[hf]);
+    if ((tid & 63) == 0) red[hf][tid >> 6] = m;
+  }
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float inv = 0.f, scale = 1.f;
-  if (amax > 0.f) {
-    inv = __fdiv_rn(127.0f, amax);
-    scale = __fdiv_rn(amax, 127.0f);
+  const bool split = a.bk == 32;
+  float inv[2], scale[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const float m0 = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    const float m1 = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const float am = split ? (hf == 0 ? m0 : m1) : fmaxf(m0, m1);
+    inv[hf] = 0.f;
+    scale[hf] = 1.f;
+    if (am > 0.f) {
+      inv[hf] = __fdiv_rn(127.0f, am);
+      scale[hf] = __fdiv_rn(am, 127.0f);
+    }
   }
-  int8_t* dst = a.kq + ((int64_t)(b * a.Hkv + g) * a.nKB * 64) * D;
+  int8_t* dst = a.kq + ((int64_t)(b * a.Hkv + g) * a.nKT * 64) * D;
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
     const int ch = tid + c * 256;
     const int key = J * 64 + ch / CH;
     const int dc = (ch % CH) * 8;
+    const float iv = inv[c / (PER / 2)];
     unsigned int w[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float r = rintf(__fmul_rn(bf16_bits_to_float(v[c][e]), inv));
+      float r = rintf(__fmul_rn(bf16_bits_to_float(v[c][e]), iv));
       r = fminf(fmaxf(r, -127.f), 127.f);
       const int qi = (int)r;
       w[e >> 2] |= ((unsigned int)(qi & 0xFF)) << (8 * (e & 3));
     }
     *(u32x2*)(dst + (int64_t)key * D + dc) = (u32x2){w[0], w[1]};
   }
-  if (tid == 0) a.sk[(b * a.Hkv + g) * a.nKB + J] = scale;
+  if (tid == 0) {
+    float* sk = a.sk + (int64_t)(b * a.Hkv + g) * a.nKB;
+    if (split) {
+      sk[2 * J] = scale[0];
+      if (2 * J + 1 < a.nKB) sk[2 * J + 1] = scale[1];
+    } else {
+      sk[J] = scale[0];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -158,7 +183,7 @@ __global__ __launch_bounds__(64 * EST_AP_WAVES) void est_anchor_pool(EstArgs a) 
     auto load_q = [&](int nt, bf16x8* qf) {
       const int hg = nt / ntph, tr = nt % ntph;
       const int rowc = min(r0 + tr * 32 + l32, a.N - 1);
-      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + (g * G + hg) * a.qs2 + half * 8;
+      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + a.qh[g * G + hg] * a.qs2 + half * 8;
   #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
     };
@@ -218,7 +243,7 @@ __global__ __launch_bounds__(64 * EST_AP_WAVES) void est_anchor_pool(EstArgs a) 
     for (int c = tid % 64; c < ncg; c += 64) {
       const int rg = tid / 64;                      // row group = wave
       const int hg = c / (D / 8), d8 = (c % (D / 8)) * 8;
-      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r0 * a.qs1 + (g * G + hg) * a.qs2 + d8;
+      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r0 * a.qs1 + a.qh[g * G + hg] * a.qs2 + d8;
       double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
       int r = rg;
       for (; r + 7 * NW < nrows; r += 8 * NW) {     // eight rows of this group in flight
@@ -304,7 +329,7 @@ __global__ __launch_bounds__(256) void est_anchor_pool_gl(EstArgs a) {
       const int row = ra + l32;
       const int rowc = min(row, a.N - 1);
       bf16x8 qf[KS];
-      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + h * a.qs2 + half * 8;
+      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + a.qh[h] * a.qs2 + half * 8;
   #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
       float mx = NEG_INF;
@@ -365,7 +390,7 @@ __global__ __launch_bounds__(256) void est_anchor_pool_gl(EstArgs a) {
   for (int p = tid; p < G * D / 2; p += 256) {
     const int hg = p / (D / 2), d2 = (p % (D / 2)) * 2;
     const int h = g * G + hg;
-    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r0 * a.qs1 + h * a.qs2 + d2;
+    const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r0 * a.qs1 + a.qh[h] * a.qs2 + d2;
     double s0[4] = {0.0, 0.0, 0.0, 0.0}, s1[4] = {0.0, 0.0, 0.0, 0.0};
     int r = 0;
     for (; r + 8 <= nrows; r += 8) {
@@ -419,8 +444,10 @@ __global__ __launch_bounds__(256) void est_anchor_pool_gl(EstArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // Block scores.  D^T[key][row] = K_q . qbar_q^T on 32x32x32 int8 MFMA (exact int32); a lane
-// owns one (query block, head) row and 16 keys of each 32-key tile, so the block max is
-// in-lane plus one half swap.  Workgroup = 4 waves x 64 rows (256 rows), 32 key blocks.
+// owns one (query block, head) row and 16 keys of each 32-key half of a 64-key tile, so a
+// block's max is in-lane plus one half swap.  Workgroup = 4 waves x 64 rows (256 rows), 32
+// key tiles of 64 keys (32 key blocks of 64, or 64 key blocks of 32: block_k = 32 takes each
+// half of a tile as its own block, with its own key scale).
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, int n_jc) {
@@ -439,9 +466,10 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
   const int rows_total = a.nQB * G;
   const int R_last = min(rt * 256 + 255, rows_total - 1);
   const int e_last = min(a.N, (R_last / G + 1) * a.bq) - 1;
-  const int J0 = jc * 32;
+  const int J0 = jc * 32;                             // first 64-key tile of the chunk
   if (J0 * 64 > e_last) return;
   const int J_end = min(J0 + 32, e_last / 64 + 1);
+  const bool bk32 = a.bk == 32;                      // key blocks of 32: two per tile
 
   int rowR[NT], e_i[NT], jmax[NT];
   float thr[NT], sqv[NT];
@@ -454,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
     const int Rc = min(R, rows_total - 1);
     const int iq = Rc / G, hg = Rc % G;
     e_i[nt] = min(a.N, (iq + 1) * a.bq) - 1;
-    jmax[nt] = R < rows_total ? e_i[nt] / 64 : -1;
+    jmax[nt] = R < rows_total ? e_i[nt] / a.bk : -1;     // last causal key block
     thr[nt] = a.abar[row_base + Rc] - a.theta[g * G + hg];
     sqv[nt] = a.sq[row_base + Rc];
     const int8_t* qp = a.qq + (row_base + Rc) * D + half * 16;
@@ -472,7 +500,7 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
   __shared__ __attribute__((aligned(1024))) unsigned char ks2[WIN * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char ks3[WIN * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
-  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D;
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKT * 64) * D;
   int s_off[SL];                                      // byte offset in a tile of this lane's 16 bytes
 #pragma unroll
   for (int k = 0; k < SL; ++k) {
@@ -489,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
     }
   };
   const int k_rd = l32 * KP + half * 16;
-  unsigned int bits[NT] = {0u, 0u};
+  unsigned long long bits[NT] = {0ull, 0ull};   // bit (block - first block of the chunk)
 
   // one key tile: D^T on int8 MFMA, block max, margin, max over the group, keep bit
   auto tile = [&](const unsigned char* st, int J) {
@@ -506,38 +534,50 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_i8(kf, qf[nt][ks], acc[mt][nt]);
       }
-    const float skv = load_uniform(a.sk + (int64_t)bg * a.nKB + J);
+    // key-block scales of the tile's blocks (block_k = 32: one per half)
+    const float* skb = a.sk + (int64_t)bg * a.nKB;
+    const float skv0 = load_uniform(skb + (bk32 ? 2 * J : J));
+    const float skv1 = bk32 ? load_uniform(skb + min(2 * J + 1, a.nKB - 1)) : skv0;
     const bool need_mask = (J * 64 + 63 > e_min) || (J * 64 + 63 >= a.N);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      int m = INT32_MIN;
+      // max of the int32 dots over the block's causal keys: the whole tile (block_k = 64) or
+      // each half (block_k = 32)
+      int m[2] = {INT32_MIN, INT32_MIN};
       if (!need_mask) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) m = max(m, acc[mt][nt][r]);
+          for (int r = 0; r < 16; ++r) m[mt] = max(m[mt], acc[mt][nt][r]);
       } else {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
-            if (key <= e_i[nt] && key < a.N) m = max(m, acc[mt][nt][r]);
+            if (key <= e_i[nt] && key < a.N) m[mt] = max(m[mt], acc[mt][nt][r]);
           }
       }
-      m = max(m, swap_halves_i(m));
-      const bool cand = J <= jmax[nt];
-      float margin = NEG_INF;
-      if (cand && m != INT32_MIN) {
-        const float mult = __fmul_rn(__fmul_rn(sqv[nt], skv), a.c);
-        const float s_hat = __fmul_rn((float)m, mult);
-        margin = s_hat - thr[nt];
-      }
-      for (int o = 1; o < G; o <<= 1) margin = fmaxf(margin, __shfl_xor(margin, o));
-      if (margin >= 0.f) bits[nt] |= 1u << (J - J0);
-      if (a.margins && cand && half == 0 && (rowR[nt] % G) == 0) {
-        const int iq = rowR[nt] / G;
-        a.margins[((int64_t)bg * a.nQB + iq) * a.nKB + J] = margin;
+      if (!bk32) m[0] = max(m[0], m[1]);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        if (hb == 1 && !bk32) break;
+        const int Jb = bk32 ? 2 * J + hb : J;            // key block
+        int mm = max(m[hb], swap_halves_i(m[hb]));
+        const bool cand = Jb <= jmax[nt];
+        float margin = NEG_INF;
+        if (cand && mm != INT32_MIN) {
+          const float skv = hb == 0 ? skv0 : skv1;
+          const float mult = __fmul_rn(__fmul_rn(sqv[nt], skv), a.c);
+          const float s_hat = __fmul_rn((float)mm, mult);
+          margin = s_hat - thr[nt];
+        }
+        for (int o = 1; o < G; o <<= 1) margin = fmaxf(margin, __shfl_xor(margin, o));
+        if (margin >= 0.f) bits[nt] |= 1ull << (bk32 ? 2 * (J - J0) + hb : J - J0);
+        if (a.margins && cand && half == 0 && (rowR[nt] % G) == 0) {
+          const int iq = rowR[nt] / G;
+          a.margins[((int64_t)bg * a.nQB + iq) * a.nKB + Jb] = margin;
+        }
       }
     }
   };
@@ -571,7 +611,13 @@ __global__ __launch_bounds__(256, 2) void est_score_block(EstArgs a, int n_rt, i
   for (int nt = 0; nt < NT; ++nt) {
     if (half == 0 && rowR[nt] < rows_total && (rowR[nt] % G) == 0) {
       const int iq = rowR[nt] / G;
-      a.bits[((int64_t)bg * a.nQB + iq) * a.W + jc] = bits[nt];
+      uint32_t* wrow = a.bits + ((int64_t)bg * a.nQB + iq) * a.W;
+      if (bk32) {
+        wrow[2 * jc] = (unsigned int)bits[nt];
+        if (2 * jc + 1 < a.W) wrow[2 * jc + 1] = (unsigned int)(bits[nt] >> 32);
+      } else {
+        wrow[jc] = (unsigned int)bits[nt];
+      }
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -674,7 +720,7 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
   __shared__ __attribute__((aligned(1024))) unsigned char kst[NST * WIN * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
   auto stage = [&](int j) { return kst + (j % NST) * (WIN * 1024); };
-  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D;
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKT * 64) * D;
   int s_off[SL];                                      // byte offset in a tile of this lane's 16 bytes
 #pragma unroll
   for (int k = 0; k < SL; ++k) {
@@ -826,7 +872,7 @@ __global__ __launch_bounds__(256) void est_quant_q_rows(EstArgs a) {
   const int h = (int)(Rc % a.Hq);
   const int r = (int)((Rc / a.Hq) % a.N);
   const int b = (int)(Rc / ((int64_t)a.Hq * a.N));
-  const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r * a.qs1 + h * a.qs2 + sub * EPL;
+  const uint16_t* qp = a.q + b * a.qs0 + (int64_t)r * a.qs1 + a.qh[h] * a.qs2 + sub * EPL;
   float v[EPL];
   if (EPL == 8) {
     const u16x8 u = *(const u16x8*)qp;
@@ -890,12 +936,13 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int r0 = I * a.bq;
   const int e = min(a.N, r0 + a.bq) - 1;
-  const int ncand = e / 64 + 1;
+  const bool bk32 = a.bk == 32;                      // key blocks of 32: two per 64-key tile
+  const int ncand = e / a.bk + 1;                    // causal key blocks
   for (int j = tid; j < ncand; j += 256) mkey[j] = 0u;
   __syncthreads();
   const int SUBS = a.bq / 64;
   const int U = a.G * SUBS;
-  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKB * 64) * D + half * 16;
+  const int8_t* kbase = a.kq + ((int64_t)bg * a.nKT * 64) * D + half * 16;
   const float* skb = a.sk + (int64_t)bg * a.nKB;
   const int sink_last = a.sink > 0 ? (min(a.sink, a.N) - 1) / 64 : -1;
 
@@ -919,7 +966,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char kst[4 * WIN * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
   auto stage = [&](int j) { return kst + (j & 3) * (WIN * 1024); };
-  const int8_t* ktile0 = a.kq + ((int64_t)bg * a.nKB * 64) * D;
+  const int8_t* ktile0 = a.kq + ((int64_t)bg * a.nKT * 64) * D;
   int s_off[SL];
 #pragma unroll
   for (int k = 0; k < SL; ++k) {
@@ -936,7 +983,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
     }
   };
   const int k_rd = l32 * KP + half * 16;
-  const int Jn = ncand;                                // causal key tiles of the block
+  const int Jn = e / 64 + 1;                           // causal 64-key tiles of the block
 
   for (int u0 = 0; u0 < U; u0 += 8) {
     const int ua = u0 + 2 * wave;
@@ -993,7 +1040,8 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
       if (J > sink_last && J < wlo) J = wlo;           // skip the tiles between the areas
       i32x4 kf[2][KS];
       load_k(J, kf);
-      const float skv = load_uniform(skb + J);
+      const float skv0 = load_uniform(skb + (bk32 ? 2 * J : J));
+      const float skv1 = bk32 ? load_uniform(skb + min(2 * J + 1, a.nKB - 1)) : skv0;
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
         if (uu == 1 && !two) break;
@@ -1003,7 +1051,8 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int row = rowv[uu][nt];
-          const float mult = __fmul_rn(__fmul_rn(sqv[uu][nt], skv), a.c);
+          const float mult0 = __fmul_rn(__fmul_rn(sqv[uu][nt], skv0), a.c);
+          const float mult1 = __fmul_rn(__fmul_rn(sqv[uu][nt], skv1), a.c);
           // online log-sum-exp over the lane's keys of the row's area
           float m_ = mr[uu][nt], s_ = sr_[uu][nt];
 #pragma unroll
@@ -1013,7 +1062,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
               const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
               const bool in = key <= row && key < a.N && (key < a.sink || key >= row - a.local + 1);
               if (in) {
-                const float v = __fmul_rn((float)acc[mt][nt][r], mult);
+                const float v = __fmul_rn((float)acc[mt][nt][r], mt == 0 ? mult0 : mult1);
                 const float mn = fmaxf(m_, v);
                 s_ = s_ * __expf(m_ - mn) + __expf(v - mn);
                 m_ = mn;
@@ -1039,8 +1088,9 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
 
     // 2. every causal key tile: best (S~ - LSE + theta) over the wave's rows and units
     auto tile = [&](const unsigned char* st, int J) {
-      const float skv = load_uniform(skb + J);
-      float best = NEG_INF;
+      const float skv0 = load_uniform(skb + (bk32 ? 2 * J : J));
+      const float skv1 = bk32 ? load_uniform(skb + min(2 * J + 1, a.nKB - 1)) : skv0;
+      float best[2] = {NEG_INF, NEG_INF};                // per key block of the tile
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
         if (uu == 1 && !two) break;
@@ -1062,31 +1112,40 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int row = rowv[uu][nt];
-          int m = INT32_MIN;
+          int m[2] = {INT32_MIN, INT32_MIN};
           if (!need_mask) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) m = max(m, acc[mt][nt][r]);
+              for (int r = 0; r < 16; ++r) m[mt] = max(m[mt], acc[mt][nt][r]);
           } else {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
-                if (key <= row && key < a.N) m = max(m, acc[mt][nt][r]);
+                if (key <= row && key < a.N) m[mt] = max(m[mt], acc[mt][nt][r]);
               }
           }
-          m = max(m, swap_halves_i(m));
-          if (m != INT32_MIN && row < a.N) {
-            const float mult = __fmul_rn(__fmul_rn(sqv[uu][nt], skv), a.c);
-            const float rel = __fmul_rn((float)m, mult) - lse[uu][nt];
-            best = fmaxf(best, rel + thv[uu]);
+          if (!bk32) m[0] = max(m[0], m[1]);
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            if (hb == 1 && !bk32) break;
+            const int mm = max(m[hb], swap_halves_i(m[hb]));
+            if (mm != INT32_MIN && row < a.N) {
+              const float mult = __fmul_rn(__fmul_rn(sqv[uu][nt], hb == 0 ? skv0 : skv1), a.c);
+              const float rel = __fmul_rn((float)mm, mult) - lse[uu][nt];
+              best[hb] = fmaxf(best[hb], rel + thv[uu]);
+            }
           }
         }
       }
-      best = wave_max(best);
-      if (lane == 0 && best > NEG_INF) lds_max_u32(&mkey[J], float_order_key(best));
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        if (hb == 1 && !bk32) break;
+        const float bw = wave_max(best[hb]);
+        if (lane == 0 && bw > NEG_INF) lds_max_u32(&mkey[bk32 ? 2 * J + hb : J], float_order_key(bw));
+      }
     };
     // Tile j is in stage j % 4; tiles j+1 and j+2 are loaded or in flight.  Step j computes
     // tile j (waves with units), issues tile j+3 (clamped to the last tile, so every wave
@@ -1138,7 +1197,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel(EstArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void est_quant_rows_fp4(EstArgs a, int which) {
   constexpr int NC = D / 32;                         // blocks per row
-  const int64_t rows = which == 0 ? (int64_t)a.B * a.N * a.Hq : (int64_t)a.B * a.Hkv * a.nKB * 64;
+  const int64_t rows = which == 0 ? (int64_t)a.B * a.N * a.Hq : (int64_t)a.B * a.Hkv * a.nKT * 64;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= rows * NC) return;
   const int c = (int)(t % NC);
@@ -1150,13 +1209,13 @@ __global__ __launch_bounds__(256) void est_quant_rows_fp4(EstArgs a, int which) 
     const int h = (int)(row % a.Hq);
     const int r = (int)((row / a.Hq) % a.N);
     const int b = (int)(row / ((int64_t)a.Hq * a.N));
-    src = a.q + b * a.qs0 + (int64_t)r * a.qs1 + h * a.qs2 + c * 32;
+    src = a.q + b * a.qs0 + (int64_t)r * a.qs1 + a.qh[h] * a.qs2 + c * 32;
     const int64_t orow = ((int64_t)b * a.Hq + h) * a.N + r;
     codes = (uint8_t*)a.qr + orow * (D / 2) + c * 16;
     scales = (uint8_t*)a.sr + orow * NC + c;
   } else {                                           // row = (b, g, token of the padded tiles)
-    const int r = (int)(row % ((int64_t)a.nKB * 64));
-    const int bg = (int)(row / ((int64_t)a.nKB * 64));
+    const int r = (int)(row % ((int64_t)a.nKT * 64));
+    const int bg = (int)(row / ((int64_t)a.nKT * 64));
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     if (r < a.N) src = a.k + b * a.ks0 + (int64_t)r * a.ks1 + g * a.ks2 + c * 32;
     codes = a.k4 + row * (D / 2) + c * 16;
@@ -1212,13 +1271,14 @@ __global__ __launch_bounds__(256, 2) void est_score_rel_fp4(EstArgs a) {
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int r0 = I * a.bq;
   const int e = min(a.N, r0 + a.bq) - 1;
-  const int ncand = e / 64 + 1;
+  const bool bk32 = a.bk == 32;                      // key blocks of 32: two per 64-key tile
+  const int ncand = e / a.bk + 1;                    // causal key blocks
   for (int j = tid; j < ncand; j += 256) mkey[j] = 0u;
   __syncthreads();
   const int SUBS = a.bq / 64;
   const int U = a.G * SUBS;
-  const uint8_t* kc0 = a.k4 + ((int64_t)bg * a.nKB * 64) * CB;
-  const uint8_t* ksc0 = a.k4s + ((int64_t)bg * a.nKB * 64) * SB;
+  const uint8_t* kc0 = a.k4 + ((int64_t)bg * a.nKT * 64) * CB;
+  const uint8_t* ksc0 = a.k4s + ((int64_t)bg * a.nKT * 64) * SB;
   const int sink_last = a.sink > 0 ? (min(a.sink, a.N) - 1) / 64 : -1;
 
   // key tiles in LDS: 64 code rows (pitch CB + 16: the 16 rows one quarter-wave reads land on
@@ -1257,7 +1317,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel_fp4(EstArgs a) {
                                        LDS_PTR(void, wdw < WIN ? st + wdw * 1024 : kspare), 16, 0, 0);
     }
   };
-  const int Jn = ncand;
+  const int Jn = e / 64 + 1;                         // causal 64-key tiles
 
   for (int u0 = 0; u0 < U; u0 += 8) {
     const int ua = u0 + 2 * wave;
@@ -1362,7 +1422,7 @@ __global__ __launch_bounds__(256, 2) void est_score_rel_fp4(EstArgs a) {
 
     // 2. every causal key tile: best (S~ - LSE + theta) over the wave's rows and units
     auto tile = [&](const unsigned char* st, int J) {
-      float best = NEG_INF;
+      float best[2] = {NEG_INF, NEG_INF};                // per key block of the tile
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
         if (uu == 1 && !two) break;
@@ -1373,27 +1433,37 @@ __global__ __launch_bounds__(256, 2) void est_score_rel_fp4(EstArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int row = rowv[uu][nt];
-          float m = NEG_INF;
+          float m[2] = {NEG_INF, NEG_INF};
           if (!need_mask) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[mt][nt][r]);
+              for (int r = 0; r < 16; ++r) m[mt] = fmaxf(m[mt], acc[mt][nt][r]);
           } else {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int key = J * 64 + mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3);
-                if (key <= row && key < a.N) m = fmaxf(m, acc[mt][nt][r]);
+                if (key <= row && key < a.N) m[mt] = fmaxf(m[mt], acc[mt][nt][r]);
               }
           }
-          m = fmaxf(m, swap_halves(m));
-          if (m > NEG_INF && row < a.N) best = fmaxf(best, __fmul_rn(m, a.c) - lse[uu][nt] + thv[uu]);
+          if (!bk32) m[0] = fmaxf(m[0], m[1]);
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            if (hb == 1 && !bk32) break;
+            const float mm = fmaxf(m[hb], swap_halves(m[hb]));
+            if (mm > NEG_INF && row < a.N)
+              best[hb] = fmaxf(best[hb], __fmul_rn(mm, a.c) - lse[uu][nt] + thv[uu]);
+          }
         }
       }
-      best = wave_max(best);
-      if (lane == 0 && best > NEG_INF) lds_max_u32(&mkey[J], float_order_key(best));
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        if (hb == 1 && !bk32) break;
+        const float bw = wave_max(best[hb]);
+        if (lane == 0 && bw > NEG_INF) lds_max_u32(&mkey[bk32 ? 2 * J + hb : J], float_order_key(bw));
+      }
     };
     issue(ks0, 0);
     issue(ks1, min(1, Jn - 1));
@@ -1528,7 +1598,7 @@ template <int D>
 static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream_t s) {
   if (a.estimator == SA_EST_RELATIVE_MXFP4) {
     const int64_t qchunks = (int64_t)a.B * a.N * a.Hq * (D / 32);
-    const int64_t kchunks = (int64_t)a.B * a.Hkv * a.nKB * 64 * (D / 32);
+    const int64_t kchunks = (int64_t)a.B * a.Hkv * a.nKT * 64 * (D / 32);
     hipLaunchKernelGGL(est_quant_rows_fp4<D>, dim3((unsigned int)((qchunks + 255) / 256)), dim3(256), 0, s, a, 0);
     hipLaunchKernelGGL(est_quant_rows_fp4<D>, dim3((unsigned int)((kchunks + 255) / 256)), dim3(256), 0, s, a, 1);
     hipLaunchKernelGGL(est_score_rel_fp4<D>, dim3(a.B * a.Hkv * a.nQB), dim3(256),
@@ -1537,7 +1607,7 @@ static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream
     hipLaunchKernelGGL(est_compact, dim3(a.B * a.Hkv * a.nQB), dim3(256), 0, s, a, a.bk);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(est_quant_k<D>, dim3(a.nKB, a.Hkv, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(est_quant_k<D>, dim3(a.nKT, a.Hkv, a.B), dim3(256), 0, s, a);
   if (a.estimator == SA_EST_RELATIVE) {
     const int64_t rows = (int64_t)a.B * a.N * a.Hq;
     hipLaunchKernelGGL(est_quant_q_rows<D>, dim3((unsigned int)((rows + 15) / 16)), dim3(256), 0, s, a);
@@ -1556,7 +1626,7 @@ static hipError_t launch_estimate_d(const EstArgs& a, int granularity, hipStream
     hipLaunchKernelGGL(est_anchor_pool_gl<D>, dim3(a.nQB, a.Hkv, a.B), dim3(256), 0, s, a);
   const int rows_total = a.nQB * a.G;
   const int n_rt = (rows_total + 255) / 256;
-  const int n_jc = (a.nKB + 31) / 32;
+  const int n_jc = (a.nKT + 31) / 32;                // chunks of 32 key tiles of 64
   const int grid = a.B * a.Hkv * n_rt * n_jc;
   if (granularity == SA_STRIPE) {
     const int n_rt_s = (rows_total + 127) / 128;

@@ -20,6 +20,25 @@ float resolve_scale(float s, int d) {
   return (float)(1.0 / sqrt((double)d));
 }
 
+// The packing order of the query heads: qh[g * G + j] = the j-th query head (ascending) whose
+// KV head is g.  Without a map, query head h uses KV head h / G, so qh is the identity.
+sa_status make_head_map(const sa_shape* s, uint8_t* qh) {
+  const int Hq = s->n_q_heads, Hkv = s->n_kv_heads, G = Hq / Hkv;
+  if (!s->kv_head_of_q) {
+    for (int h = 0; h < Hq; ++h) qh[h] = (uint8_t)h;
+    return SA_OK;
+  }
+  for (int h = 0; h < Hq; ++h)
+    if (s->kv_head_of_q[h] < 0 || s->kv_head_of_q[h] >= Hkv) return SA_ERR_PARAM;
+  int fill[SA_MAX_Q_HEADS] = {0};
+  for (int h = 0; h < Hq; ++h) {
+    const int g = s->kv_head_of_q[h];
+    if (fill[g] >= G) return SA_ERR_UNSUPPORTED;   // unequal group sizes cannot be packed
+    qh[g * G + fill[g]++] = (uint8_t)h;
+  }
+  return SA_OK;
+}
+
 sa_status check_shape_common(const sa_shape* s) {
   if (!s) return SA_ERR_NULL;
   if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->seq_q < 1 || s->seq_k < 1)
@@ -29,7 +48,8 @@ sa_status check_shape_common(const sa_shape* s) {
   if (s->head_dim != 64 && s->head_dim != 128) return SA_ERR_UNSUPPORTED;
   if (s->n_q_heads > SA_MAX_Q_HEADS) return SA_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return SA_ERR_UNSUPPORTED;
-  return SA_OK;
+  uint8_t qh[SA_MAX_Q_HEADS];
+  return make_head_map(s, qh);
 }
 
 bool strides_ok(const int64_t st[3]) {
@@ -50,6 +70,8 @@ sa_status check_prefill_shape(const sa_shape* s) {
   if (s->q_stride[2] < s->head_dim || s->k_stride[2] < s->head_dim ||
       s->v_stride[2] < s->head_dim || s->o_stride[2] < s->head_dim)
     return SA_ERR_SHAPE;
+  // the attention addresses a K/V tile's rows with 32-bit byte offsets from the tile's start
+  if (s->k_stride[1] >= (1 << 24) || s->v_stride[1] >= (1 << 24)) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
 
@@ -64,7 +86,8 @@ sa_status check_sparse_params(const sa_shape* s, const sa_sparse_params* p, bool
   if (p->step < 0) return SA_ERR_PARAM;
   if (p->sink_tokens < 0 || p->local_tokens < 1) return SA_ERR_PARAM;
   if (p->block_q != 64 && p->block_q != 128) return SA_ERR_UNSUPPORTED;
-  if (p->block_k != 64) return SA_ERR_UNSUPPORTED;
+  // key blocks of 64, or of 32 (two per 64-key tile) for block lists
+  if (p->block_k != 64 && !(p->block_k == 32 && p->granularity == SA_BLOCK)) return SA_ERR_UNSUPPORTED;
   if (isnan(p->softmax_scale) || isinf(p->softmax_scale)) return SA_ERR_PARAM;
   if (need_theta)
     for (int h = 0; h < s->n_q_heads; ++h)
@@ -82,11 +105,12 @@ EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p, bool with_sta
   EstLayout L{};
   const int N = s->seq_q, D = s->head_dim, B = s->batch, Hkv = s->n_kv_heads, Hq = s->n_q_heads;
   const int nQB = ceil_div(N, p->block_q), nKB = ceil_div(N, p->block_k);
+  const int nKT = ceil_div(N, 64);             // 64-key tiles (the unit keys are staged in)
   // stripe bit rows cover the padded key range (whole 64-key tiles)
-  const int ncand = p->granularity == SA_STRIPE ? nKB * 64 : nKB;
+  const int ncand = p->granularity == SA_STRIPE ? nKT * 64 : nKB;
   L.W = ceil_div(ncand, 32);
   size_t off = 0;
-  L.kq = off;   off = align_up(off + (size_t)B * Hkv * nKB * 64 * D);
+  L.kq = off;   off = align_up(off + (size_t)B * Hkv * nKT * 64 * D);
   L.sk = off;   off = align_up(off + (size_t)B * Hkv * nKB * sizeof(float));
   L.qq = off;   off = align_up(off + (size_t)B * Hq * nQB * D);
   L.sq = off;   off = align_up(off + (size_t)B * Hq * nQB * sizeof(float));
@@ -98,7 +122,7 @@ EstLayout est_layout(const sa_shape* s, const sa_sparse_params* p, bool with_sta
   const bool fp4 = p->estimator == SA_EST_RELATIVE_MXFP4;
   L.qr = off;   off = align_up(off + rows * (fp4 ? D / 2 : D));
   L.sr = off;   off = align_up(off + rows * (fp4 ? D / 32 : sizeof(float)));
-  const size_t krows = fp4 ? (size_t)B * Hkv * nKB * 64 : 0;
+  const size_t krows = fp4 ? (size_t)B * Hkv * nKT * 64 : 0;
   L.k4 = off;   off = align_up(off + krows * D / 2);
   L.k4s = off;  off = align_up(off + krows * D / 32);
   L.xa = off;   off = align_up(off + (with_state ? (size_t)B * Hq * N * sizeof(float) : 0));
@@ -195,7 +219,8 @@ size_t sa_workspace_size(int op, const sa_shape* shape, const void* params) {
   if (op == SA_OP_ESTIMATE || op == SA_OP_ESTIMATE_STATE) {
     const sa_sparse_params* p = (const sa_sparse_params*)params;
     if (check_prefill_shape(shape) != SA_OK || check_sparse_params(shape, p, true) != SA_OK) return 0;
-    if (op == SA_OP_ESTIMATE_STATE && (p->estimator != SA_EST_POOLED || p->granularity != SA_BLOCK))
+    if (op == SA_OP_ESTIMATE_STATE &&
+        (p->estimator != SA_EST_POOLED || p->granularity != SA_BLOCK || p->block_k != 64))
       return 0;
     return est_layout(shape, p, op == SA_OP_ESTIMATE_STATE).total;
   }
@@ -229,7 +254,9 @@ static sa_status estimate_impl(const sa_shape* shape, const sa_sparse_params* pa
   if (!aligned16(q) || !aligned16(k)) return SA_ERR_SHAPE;
   const bool with_state = state != nullptr;
   if (with_state) {
-    if (params->estimator != SA_EST_POOLED || params->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
+    if (params->estimator != SA_EST_POOLED || params->granularity != SA_BLOCK ||
+        params->block_k != 64)
+      return SA_ERR_UNSUPPORTED;
     if (!v || !state->o || !state->lse) return SA_ERR_NULL;
     if (!aligned16(v) || !aligned16(state->o) || ((uintptr_t)state->lse & 3u) != 0) return SA_ERR_SHAPE;
   }
@@ -251,7 +278,7 @@ static sa_status estimate_impl(const sa_shape* shape, const sa_sparse_params* pa
   a.G = a.Hq / a.Hkv; a.D = shape->head_dim; a.N = N;
   a.bq = params->block_q; a.bk = params->block_k;
   a.sink = params->sink_tokens; a.local = params->local_tokens;
-  a.nQB = nQB; a.nKB = nKB;
+  a.nQB = nQB; a.nKB = nKB; a.nKT = ceil_div(N, 64);
   a.c = resolve_scale(params->softmax_scale, a.D);
   char* base = (char*)ws;
   a.kq = (int8_t*)(base + L.kq);
@@ -271,7 +298,8 @@ static sa_status estimate_impl(const sa_shape* shape, const sa_sparse_params* pa
   a.idx = out->idx;
   a.stride = out->stride;
   a.margins = out->margins;
-  for (int h = 0; h < a.Hq; ++h) a.theta[h] = params->theta[h];
+  make_head_map(shape, a.qh);
+  for (int j = 0; j < a.Hq; ++j) a.theta[j] = params->theta[a.qh[j]];
   if (with_state) {
     a.v = (const uint16_t*)v;
     a.vs0 = shape->v_stride[0]; a.vs1 = shape->v_stride[1]; a.vs2 = shape->v_stride[2];
@@ -296,7 +324,7 @@ static sa_status prefill_impl(const sa_shape* shape, const sa_sparse_params* par
   if (!q || !k || !v || !o || !lists || !lists->counts || !lists->idx) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SA_ERR_SHAPE;
   if (state) {
-    if (params->granularity != SA_BLOCK) return SA_ERR_UNSUPPORTED;
+    if (params->granularity != SA_BLOCK || params->block_k != 64) return SA_ERR_UNSUPPORTED;
     if (!state->o || !state->lse) return SA_ERR_NULL;
     if (!aligned16(state->o) || ((uintptr_t)state->lse & 3u) != 0) return SA_ERR_SHAPE;
   }
@@ -319,6 +347,8 @@ static sa_status prefill_impl(const sa_shape* shape, const sa_sparse_params* par
   a.tpb = params->block_q / 64;
   a.scale_log2 = resolve_scale(params->softmax_scale, shape->head_dim) * 1.4426950408889634f;
   a.stripe = params->granularity == SA_STRIPE;
+  a.bk32 = params->block_k == 32;
+  make_head_map(shape, a.qh);
   if (state) {
     a.st_o = (const uint16_t*)state->o;
     a.st_lse = state->lse;
@@ -369,6 +399,7 @@ static void fill_dec_args(DecArgs& a, const sa_shape* s, int block_k) {
   a.B = s->batch; a.Hq = s->n_q_heads; a.Hkv = s->n_kv_heads; a.G = a.Hq / a.Hkv;
   a.D = s->head_dim; a.L = s->seq_k; a.bk = block_k;
   a.nKB = ceil_div(s->seq_k, block_k);
+  make_head_map(s, a.qh);
 }
 
 sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k, const void* k_cache,

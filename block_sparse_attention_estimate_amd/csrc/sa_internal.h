@@ -12,18 +12,19 @@ struct EstArgs {
   const uint16_t* k;
   int64_t qs0, qs1, qs2, ks0, ks1, ks2;
   int B, Hq, Hkv, G, D, N, bq, bk, sink, local, nQB, nKB;
+  int nKT;                 // 64-key tiles of the sequence (the unit keys are staged in)
   float c;                 // softmax scale, fp32
   // workspace carve-out
-  int8_t* kq;              // [B, Hkv, nKB * bk, D] int8 keys
-  float* sk;               // [B, Hkv, nKB] key-tile scales
+  int8_t* kq;              // [B, Hkv, nKT * 64, D] int8 keys
+  float* sk;               // [B, Hkv, nKB] key-block scales (one per block_k keys)
   int8_t* qq;              // [B, Hkv, nQB, G, D] int8 pooled queries
   float* sq;               // [B, Hkv, nQB, G] pooled-query scales
   float* abar;             // [B, Hkv, nQB, G] block-averaged anchors
   uint32_t* bits;          // [B, Hkv, nQB, W] keep bits
   int8_t* qr;              // relative estimator: int8 query rows [B, Hq, N, D]
   float* sr;               // and their scales [B, Hq, N]
-  uint8_t* k4;             // MXFP4 estimator: K codes [B, Hkv, nKB * 64, D / 2]
-  uint8_t* k4s;            // and E8M0 scales [B, Hkv, nKB * 64, D / 32]
+  uint8_t* k4;             // MXFP4 estimator: K codes [B, Hkv, nKT * 64, D / 2]
+  uint8_t* k4s;            // and E8M0 scales [B, Hkv, nKT * 64, D / 32]
   int estimator;           // SA_EST_POOLED, SA_EST_RELATIVE or SA_EST_RELATIVE_MXFP4
   int step;                // query blocks per identification group (<= 1: none)
   int W;                   // words per bit row
@@ -39,7 +40,10 @@ struct EstArgs {
   int32_t* idx;
   int32_t stride;
   float* margins;
-  float theta[SA_MAX_Q_HEADS];
+  float theta[SA_MAX_Q_HEADS];  // per packed head: theta of query head qh[g * G + j]
+  // query head of packed head g * G + j (the j-th query head of KV head g): the index of Q, O,
+  // LSE and the anchor state in their head dimension
+  uint8_t qh[SA_MAX_Q_HEADS];
 };
 
 struct AttnArgs {
@@ -61,6 +65,8 @@ struct AttnArgs {
   const float* st_lse;     // [B, Hq, N] natural log
   int sink, local;
   int stripe;              // 1: the lists name key columns (gathered rows), 0: key blocks
+  int bk32;                // 1: block lists of 32-key blocks (two per 64-key tile)
+  uint8_t qh[SA_MAX_Q_HEADS];  // query head of packed head g * G + j
 };
 
 struct DecArgs {
@@ -83,6 +89,7 @@ struct DecArgs {
   int B, Hq, Hkv, G, D, L, bk, nKB, top_k, sink, local, n_splits;
   float c;
   float top_p;             // 0: fixed K; (0, 1]: top-p budget capped at K
+  uint8_t qh[SA_MAX_Q_HEADS];  // query head of packed head g * G + j
 };
 
 hipError_t launch_estimate(const EstArgs& a, int granularity, hipStream_t s);

@@ -25,13 +25,16 @@
  *    `sa_decode_params` and `sa_lists` themselves are HOST structs read during the call.
  *  - Layout: Q, K, V, O are bf16 with head_dim contiguous; the (batch, token, head)
  *    strides are given in ELEMENTS and must be multiples of 8 (16-byte rows); base
- *    pointers must be 16-byte aligned.  Query head h uses KV head h / (Hq / Hkv).
+ *    pointers must be 16-byte aligned.  Query head h uses KV head kv_head_of_q[h] (sa_shape),
+ *    by default h / (Hq / Hkv).
  *  - Execution: asynchronous on `stream`.  All validation happens on the host before any
  *    launch; on an error nothing is launched and no output is touched.
  *  - Errors: returned as `sa_status`; no exception or abort crosses the ABI.  A HIP launch
  *    failure is reported as SA_ERR_DEVICE.
- *  - Supported (v1): head_dim in {64, 128}; block_q in {64, 128}; block_k == 64;
- *    n_q_heads <= 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8}.
+ *  - Supported (v1): head_dim in {64, 128}; block_q in {64, 128}; block_k in {32, 64} for
+ *    block lists (SALE's configuration is block_q 64, block_k 32) and 64 for stripes and the
+ *    anchor-state pair; n_q_heads <= 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8}; the token
+ *    strides of K and V (k_stride[1], v_stride[1]) below 2^24 elements.
  *  - Sizes: batch, head counts, seq_q and seq_k are at least 1; an empty problem is
  *    SA_ERR_SHAPE (there is nothing to launch: callers skip the call).  seq_q < 2^30; at most
  *    8192 key blocks for decode.
@@ -64,12 +67,22 @@ enum { SA_OP_ESTIMATE = 0, SA_OP_PREFILL = 1, SA_OP_DECODE = 2, SA_OP_CALIBRATE 
 
 #define SA_MAX_Q_HEADS 128
 
-/* Problem statement: batch, heads, head_dim, query/key lengths and element strides of
- * the (batch, token, head) dimensions of each tensor.  For decode, seq_q is 1 and seq_k is
- * the cache capacity (tokens per sequence in the cache buffers); q/o strides use the token
- * stride slot unused. */
+/* Problem statement: batch, heads, head_dim, query/key lengths, the GQA head map and
+ * element strides of the (batch, token, head) dimensions of each tensor.  For decode, seq_q is
+ * 1 and seq_k is the cache capacity (tokens per sequence in the cache buffers); q/o strides
+ * use the token stride slot unused.
+ *
+ * kv_head_of_q (HOST int32 [n_q_heads], nullable; read during the call): the KV head each
+ * query head attends with (grouped-query attention; KVpop, referee minor comment 4: the query
+ * heads sharing a KV head are aggregated with max, so a list row is per KV head).  NULL means
+ * h / (n_q_heads / n_kv_heads).  Every value must lie in [0, n_kv_heads) (else SA_ERR_PARAM)
+ * and every KV head must have exactly n_q_heads / n_kv_heads query heads (the kernels pack a
+ * group's heads onto one K/V tile; otherwise SA_ERR_UNSUPPORTED).  The heads of a group may sit
+ * anywhere in the head dimension of Q and O; per-query-head inputs and outputs (theta, O, LSE,
+ * the anchor state, calibration results) stay indexed by the query head itself. */
 typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim, seq_q, seq_k;
+  const int32_t* kv_head_of_q;
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
 } sa_shape;
 
@@ -114,7 +127,11 @@ enum { SA_EST_POOLED = 0, SA_EST_RELATIVE = 1, SA_EST_RELATIVE_MXFP4 = 2 };
 
 /* Per-row kept lists (the index set I of Eq. (3)), one row per (batch, KV head, query
  * block), rows ordered (b, g, i).  Row r holds counts[r] ascending key-block ids (block
- * granularity) or key-column ids (stripe granularity) in idx[r*stride ...].  Forced sink and
+ * granularity, blocks of block_k keys) or key-column ids (stripe granularity) in
+ * idx[r*stride ...].  Lists given to sa_sparse_prefill may come from the caller: entries must
+ * be ascending and lie in [0, ceil(seq_k / block_k)) (columns: [0, seq_k)); entries outside
+ * that range are clamped into it on the device (memory stays in bounds; the result for such a
+ * list is unspecified).  Forced sink and
  * local entries are included.  counts always receives the true count; entries past
  * `stride` are dropped (stripe lists only -- block lists require stride >= ceil(seq_k /
  * block_k)), so a caller detects stripe overflow as counts[r] > stride after the call.

@@ -84,8 +84,21 @@ def test_validation_codes(lib):
     assert _est(lib, s, p, q=FAKE + 8, ws_bytes=need) == _lib.SA_ERR_SHAPE   # misaligned
     pn, keep2 = _params(float("nan"))
     assert _est(lib, s, pn, ws_bytes=need) == _lib.SA_ERR_PARAM
-    pu, keep3 = _params(4.0, bk=32)
+    pu, keep3 = _params(4.0, bk=16)
     assert _est(lib, s, pu, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
+    # 32-key blocks: block lists only (stripes stage 64-key tiles), not with the anchor state
+    p32, keep32 = _params(4.0, bk=32)
+    need32 = lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(p32))
+    assert need32 > 0
+    assert _est(lib, s, p32, stride=8, ws_bytes=need32 - 1) == _lib.SA_ERR_WORKSPACE
+    assert _est(lib, s, p32, stride=7, ws_bytes=need32) == _lib.SA_ERR_CAPACITY   # 8 key blocks
+    p32s, keep32s = _params(4.0, bk=32, gran=_lib.SA_STRIPE)
+    assert _est(lib, s, p32s, ws_bytes=need32) == _lib.SA_ERR_UNSUPPORTED
+    assert lib.sa_workspace_size(_lib.SA_OP_ESTIMATE_STATE, ctypes.byref(s), ctypes.byref(p32)) == 0
+    # token strides of K and V are limited to 2^24 elements (32-bit tile offsets)
+    big = _shape()
+    big.k_stride[1] = 1 << 24
+    assert _est(lib, big, p, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
     pq, keep4 = _params(4.0, bq=96)
     assert _est(lib, s, pq, ws_bytes=need) == _lib.SA_ERR_UNSUPPORTED
     pe, keep6 = _params(4.0)
@@ -219,3 +232,44 @@ def test_anchor_state_validation(lib):
     st.o = FAKE
     ls.stride = 3
     assert resume() == _lib.SA_ERR_CAPACITY
+    p32, keep4 = _params(4.0, bk=32)
+    ls.stride = 8
+    assert resume(pp=p32) == _lib.SA_ERR_UNSUPPORTED
+    assert est(pp=p32) == _lib.SA_ERR_UNSUPPORTED
+
+
+def _with_map(s, m):
+    arr = (ctypes.c_int32 * len(m))(*m)
+    s.kv_head_of_q = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return arr
+
+
+def test_head_map_validation(lib):
+    """The GQA head map: values in [0, n_kv_heads) (else SA_ERR_PARAM), equal group sizes
+    (else SA_ERR_UNSUPPORTED); a valid permuted map passes every shape check."""
+    p, keep = _params(4.0, Hq=4)
+    s = _shape(Hq=4, Hkv=2)
+    need = lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(p))
+    m_ok = _with_map(s, [1, 0, 0, 1])
+    assert lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(p)) == need
+    # the map passes: the call fails only on the (short) workspace
+    assert _est(lib, s, p, ws_bytes=need - 1) == _lib.SA_ERR_WORKSPACE
+    for bad, code in (([0, 1, 2, 1], _lib.SA_ERR_PARAM), ([0, -1, 1, 1], _lib.SA_ERR_PARAM),
+                      ([0, 0, 0, 1], _lib.SA_ERR_UNSUPPORTED), ([1, 1, 1, 1], _lib.SA_ERR_UNSUPPORTED)):
+        m_bad = _with_map(s, bad)
+        assert _est(lib, s, p, ws_bytes=need) == code, bad
+        assert lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(p)) == 0
+        ls = _lib.SaLists()
+        ls.counts, ls.idx, ls.stride, ls.margins = FAKE, FAKE, 4, None
+        assert lib.sa_sparse_prefill(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE,
+                                     ctypes.byref(ls), FAKE, None, None) == code, bad
+        ds = _shape(B=2, Hq=4, Hkv=2, N=1000)
+        ds.seq_q = 1
+        keep_d = _with_map(ds, bad)
+        dp = _lib.SaDecodeParams()
+        dp.block_k, dp.top_k_blocks, dp.sink_tokens, dp.local_tokens = 64, 8, 32, 256
+        assert lib.sa_workspace_size(_lib.SA_OP_DECODE, ctypes.byref(ds), ctypes.byref(dp)) == 0
+        assert lib.sa_sparse_decode(ctypes.byref(ds), ctypes.byref(dp), FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, None, None, FAKE, 1 << 30, None) == code, bad
+        assert lib.sa_build_block_summary(ctypes.byref(ds), 64, FAKE, FAKE, FAKE, None) == code
+    del m_ok, m_bad, keep_d

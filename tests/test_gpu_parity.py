@@ -753,8 +753,10 @@ def test_decode_determinism(dev, top_p):
                            b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_)
 
 
-@pytest.mark.parametrize("granularity,bq", [("block", 128), ("block", 64), ("stripe", 128)])
-def test_prefill_arbitrary_lists(dev, granularity, bq):
+@pytest.mark.parametrize("granularity,bq,bk", [("block", 128, 64), ("block", 64, 64),
+                                               ("stripe", 128, 64), ("block", 64, 32),
+                                               ("block", 128, 32)])
+def test_prefill_arbitrary_lists(dev, granularity, bq, bk):
     """Lists a caller builds itself (not from the estimate): random ascending subsets that
     include entries past the diagonal (ignored: only j <= r counts), empty lists, and lists
     whose entries all lie in a row's future.  Rows that see no key get O = 0 and LSE = -inf;
@@ -765,7 +767,7 @@ def test_prefill_arbitrary_lists(dev, granularity, bq):
     x = synth.make_prefill(name, seq=1500, hq=8, hkv=2)
     B, N, Hq, D = x.q.shape
     Hkv, G = 2, 4
-    nqb, nkb = -(-N // bq), -(-N // 64)
+    nqb, nkb = -(-N // bq), -(-N // bk)
     rng = np.random.default_rng(21)
     ref_lists = {}
     for g in range(Hkv):
@@ -776,7 +778,7 @@ def test_prefill_arbitrary_lists(dev, granularity, bq):
                 kept = np.zeros(0, np.int64)                       # empty
             elif kind == 1:                                        # only the far future
                 r1 = min(N, (i + 1) * bq)
-                lo = r1 // 64 + 1 if granularity == "block" else r1 + 5
+                lo = r1 // bk + 1 if granularity == "block" else r1 + 5
                 kept = np.arange(lo, ncand) if lo < ncand else np.zeros(0, np.int64)
             else:                                                  # random, incl. future
                 kept = np.nonzero(rng.random(ncand) < rng.uniform(0.02, 0.6))[0]
@@ -790,20 +792,20 @@ def test_prefill_arbitrary_lists(dev, granularity, bq):
     lists = sa.Lists(torch.from_numpy(counts).to(dev), torch.from_numpy(idx).to(dev), stride,
                      granularity)
     q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
-    o, lse = sa.sparse_prefill(q, k, v, lists, block_q=bq, block_k=64, sink=32, local=256)
+    o, lse = sa.sparse_prefill(q, k, v, lists, block_q=bq, block_k=bk, sink=32, local=256)
     torch.cuda.synchronize()
     og = o.float().cpu().numpy()
     lg = lse.cpu().numpy()
     def toks_of(b, h, i):
         kept = ref_lists[(b, h // G, i)]
-        t = kept if granularity == "stripe" else (kept[:, None] * 64 + np.arange(64)).ravel()
+        t = kept if granularity == "stripe" else (kept[:, None] * bk + np.arange(bk)).ravel()
         return t[t < N]
     rows = [(0, h, i) for h in range(Hq) for i in range(nqb)]
     # the oracle's plain definition needs some listed token in range; blocks without one are
     # checked as rows without keys below
     with_toks = [(b, h, i) for (b, h, i) in rows if toks_of(b, h, i).size > 0]
     with np.errstate(invalid="ignore", divide="ignore"):
-        res = oracle.attention_rows(x.q, x.k, x.v, ref_lists, block_q=bq, block_k=64,
+        res = oracle.attention_rows(x.q, x.k, x.v, ref_lists, block_q=bq, block_k=bk,
                                     granularity=granularity, rows=with_toks)
     n_empty = 0
     errs = []
@@ -819,7 +821,7 @@ def test_prefill_arbitrary_lists(dev, granularity, bq):
                 errs.append(np.abs(og[b, r, h] - oref[t]))
                 assert abs(lg[b, h, r] - lref[t]) < 1e-2, (b, h, r)
     err = np.concatenate(errs)
-    log(f"  arbitrary {granularity} bq={bq}: rows without keys {n_empty}, "
+    log(f"  arbitrary {granularity} bq={bq} bk={bk}: rows without keys {n_empty}, "
         f"max|dO|={err.max():.2e} mean={err.mean():.2e}")
     assert n_empty > 0 and err.max() < MAX_ABS and err.mean() < MEAN_ABS
 
