@@ -168,21 +168,121 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+FLUSH_BYTES = 512 << 20       # written between timed repetitions (larger than the 256 MB MALL)
+
+
+class SclkSampler:
+    """Samples the GPU shader clock (the active level of the sysfs pp_dpm_sclk table) from a
+    thread while the timed repetitions run.  Reports the distinct levels seen (MHz) or None
+    when the table is not readable."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thr = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for pth in self.paths:
+            try:
+                for line in open(pth):
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().split("mhz")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thr.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.paths:
+            self._thr.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = np.asarray(self.samples, dtype=np.float64)
+        return {"median_mhz": float(np.median(v)), "min_mhz": float(v.min()),
+                "max_mhz": float(v.max()), "samples": int(v.size),
+                "source": "sysfs pp_dpm_sclk active level, sampled every 5 ms during the timed reps"}
+
+
+def pct(v):
+    """median, p10, p90 of a list of times"""
+    a = np.asarray(v, dtype=np.float64)
+    return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
+
+
+def useful_pairs_block(counts, idx, stride, N, block_q, block_k):
+    """Causal (row, key) pairs inside the kept tiles: sum over kept (b, g, i, J) of the pairs
+    (r, j) with r in query block i, j in key block J, j <= r and j < N."""
+    c = counts.reshape(-1).astype(np.int64)
+    ix = idx.reshape(c.size, stride).astype(np.int64)
+    nqb = counts.shape[-1]
+    iq = np.tile(np.arange(nqb, dtype=np.int64), c.size // nqb)
+    valid = np.arange(stride)[None, :] < c[:, None]
+    r0 = (iq * block_q)[:, None]
+    r1 = np.minimum(N, (iq + 1) * block_q)[:, None]
+    k0 = ix * block_k
+    k1 = np.minimum(N, k0 + block_k)
+
+    def tri(x):   # 1 + 2 + ... + x
+        return x * (x + 1) // 2
+    # rows in [max(r0, k0), min(r1, k1)) see r - k0 + 1 keys of the tile; rows from
+    # max(r0, k1) on see all k1 - k0
+    lo, hi = np.maximum(r0, k0), np.minimum(r1, k1)
+    pairs = np.where(hi > lo, tri(hi - k0) - tri(lo - k0), 0)
+    pairs = pairs + np.maximum(r1 - np.maximum(r0, k1), 0) * (k1 - k0)
+    return int((pairs * valid).sum())
+
+
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    return model, affinity
+
+
 def to_dev(bits, dev):
     import torch
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def cpu_baseline_prefill(x, dense_flops, n_est_rows=1024, n_attn_rows=1024, seed=1):
-    """The oracle (numpy fp64) on a bounded random sample of the same workload: estimate
-    rows (b, g, i) and attention query blocks (b, h, i) drawn uniformly, timed separately and
-    scaled by total rows / sampled rows to a whole-layer time."""
+def cpu_baseline_prefill(x, dense_flops, n_est_rows=None, n_attn_rows=512, seed=1):
+    """The oracle (numpy fp64) on the same workload: the estimate over every row (b, g, i)
+    (n_est_rows=None) or a random sample of them, timed, and the attention over a random
+    sample of query blocks (b, h, i) under the oracle's own lists, timed and scaled by total
+    rows / sampled rows to the layer (extrapolated)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+        blas = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        blas = None
+    model, affinity = cpu_info()
     B, N, Hq, D = x.q.shape
     Hkv = x.k.shape[2]
     G = Hq // Hkv
@@ -190,29 +290,41 @@ def cpu_baseline_prefill(x, dense_flops, n_est_rows=1024, n_attn_rows=1024, seed
     rng = np.random.default_rng(seed)
     kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local,
               granularity=x.granularity)
-    # estimate sample, grouped by KV head so each group's key tiles are quantised once
-    gs = rng.integers(0, Hkv, n_est_rows)
-    is_ = rng.integers(0, nqb, n_est_rows)
-    rows = sorted((0, int(g), int(i)) for g, i in zip(gs, is_))
+    all_rows = [(b, g, i) for b in range(B) for g in range(Hkv) for i in range(nqb)]
+    if n_est_rows is None or n_est_rows >= len(all_rows):
+        rows = all_rows
+    else:
+        pick = rng.choice(len(all_rows), size=n_est_rows, replace=False)
+        rows = sorted(all_rows[j] for j in pick)        # grouped by KV head: tiles quantised once
     t0 = time.perf_counter()
     ref = oracle.estimate_rows(x.q, x.k, x.theta, rows=rows, keep_margins=False, **kw)
     t_est = time.perf_counter() - t0
-    # attention sample: lists from the oracle's own estimate of those rows
+    # attention sample: random (b, g, i) rows of the estimate, a random head of the group each
     arows = []
-    for (b, g, i) in rows[:n_attn_rows]:
+    for j in rng.choice(len(rows), size=min(n_attn_rows, len(rows)), replace=False):
+        b, g, i = rows[j]
         arows.append((b, g * G + int(rng.integers(0, G)), i))
+    # grouped by (b, KV head): the oracle converts one group's keys and values at a time
+    arows.sort(key=lambda r: (r[0], r[1] // G, r[1], r[2]))
     lists = {key: r["kept"] for key, r in ref.items()}
     t0 = time.perf_counter()
     oracle.attention_rows(x.q, x.k, x.v, lists, rows=arows, block_q=x.block_q,
                           block_k=x.block_k, granularity=x.granularity)
     t_att = time.perf_counter() - t0
-    full = t_est * (B * Hkv * nqb) / len(rows) + t_att * (B * Hq * nqb) / len(arows)
+    est_layer = t_est * (B * Hkv * nqb) / len(rows)
+    att_layer = t_att * (B * Hq * nqb) / len(arows)
+    full = est_layer + att_layer
+    est_kind = "measured over every row" if len(rows) == len(all_rows) else \
+        f"extrapolated from {len(rows)} random rows"
     return {"value": dense_flops / full / 1e12, "unit": "TFLOP/s (dense-equivalent)",
-            "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} random estimate rows (b,g,i) in {t_est:.1f}s and "
-                      f"{len(arows)} random attention query blocks (b,h,i) in {t_att:.1f}s, "
-                      f"scaled by rows to the whole layer ({full:.0f}s)",
-            "est_s": t_est, "attn_s": t_att, "extrapolated_layer_s": full}
+            "cores": blas, "kind": "oracle",
+            "sample": f"estimate: {len(rows)} of {len(all_rows)} rows (b,g,i) in {t_est:.1f}s "
+                      f"({est_kind}); attention: {len(arows)} random query blocks (b,h,i) in "
+                      f"{t_att:.1f}s, extrapolated by rows to the layer ({att_layer:.0f}s); "
+                      f"layer {full:.0f}s",
+            "cpu_model": model, "affinity_cores": affinity, "blas_threads": blas,
+            "estimate_s": round(est_layer, 2), "estimate_measured": len(rows) == len(all_rows),
+            "attention_s_extrapolated": round(att_layer, 1)}
 
 
 def bench_prefill(args, dev):
@@ -244,41 +356,51 @@ def bench_prefill(args, dev):
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    # two copies of the inputs, used alternately, and a 512 MB write between repetitions, so
+    # that no repetition finds its inputs in the caches (the MALL holds 256 MB)
+    copies = [(q, k, v), tuple(t.clone() for t in (q, k, v))]
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        qq, kk, vv = copies[i % 2]
         if ev is not None:
             ev[0].record(stream)
         if reuse:
-            sa.estimate_mask_anchor_state(q, k, v, x.theta, step=args.step, workspace=ws,
+            sa.estimate_mask_anchor_state(qq, kk, vv, x.theta, step=args.step, workspace=ws,
                                           out=lists, state=state, **kw)
         else:
-            sa.estimate_mask(q, k, x.theta, granularity=x.granularity, estimator=est,
+            sa.estimate_mask(qq, kk, x.theta, granularity=x.granularity, estimator=est,
                              step=args.step, workspace=ws, out=lists, **kw)
         if ev is not None:
             ev[1].record(stream)
         if reuse:
-            sa.sparse_prefill_resume(q, k, v, lists, state, out=o, lse=False, **kw)
+            sa.sparse_prefill_resume(qq, kk, vv, lists, state, out=o, lse=False, **kw)
         else:
-            sa.sparse_prefill(q, k, v, lists, out=o, lse=False, **kw)
+            sa.sparse_prefill(qq, kk, vv, lists, out=o, lse=False, **kw)
         if ev is not None:
             ev[2].record(stream)
 
     log("warmup")
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
+        flush.fill_(float(i))
     torch.cuda.synchronize()
     if x.granularity == "stripe" and lists.overflowed():
         raise SystemExit("stripe list capacity exceeded; raise --stripe-capacity")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, evs[i])
+            flush.fill_(float(i))               # outside the timed events
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     est_ms = [e[0].elapsed_time(e[1]) for e in evs]
     att_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    ms_step = wall * 1e3 / args.steps
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    ms_step, p10_step, p90_step = pct(step_ms)
     counts = lists.counts.cpu().numpy().astype(np.int64)
     nqb = counts.shape[2]
     ends = np.minimum(N, (np.arange(nqb) + 1) * x.block_q) - 1
@@ -316,10 +438,21 @@ def bench_prefill(args, dev):
         units_desc = (f"{kept_units} visited (head, 64x{x.block_k} tile) x "
                       f"{flops_per_unit / 1e6:.3f} MFLOP (the anchor state covers the rest)")
     dense_flops = 2.0 * N * N * D * Hq * B
-    att_avg = float(np.mean(att_ms))
-    est_avg = float(np.mean(est_ms))
+    att_avg, att_p10, att_p90 = pct(att_ms)
+    est_avg, est_p10, est_p90 = pct(est_ms)
     achieved = kept_flops / (att_avg * 1e-3) / 1e12
     per_group = (counts.sum(axis=(0, 2)) / (cands.sum() * B)).round(4).tolist()
+    useful = None
+    if x.granularity == "block" and not reuse:
+        # causal (row, key) pairs inside the kept tiles, 4 d flops each per query head
+        pairs = useful_pairs_block(counts, lists.idx.cpu().numpy(), lists.stride, N, x.block_q,
+                                   x.block_k)
+        useful = 4.0 * D * pairs * G
+    theta_g = [round(float(t), 3) for t in x.theta.reshape(Hkv, G)[:, 0]] \
+        if np.all(x.theta.reshape(Hkv, G) == x.theta.reshape(Hkv, G)[:, :1]) else \
+        [round(float(t), 3) for t in x.theta]
+    theta_desc = (f"theta per KV head {theta_g}" if len(theta_g) == Hkv else
+                  f"theta per query head {theta_g}")
     # the attention kernel the library launches for these lists
     kernel = "attn_block"
     out = {
@@ -332,17 +465,27 @@ def bench_prefill(args, dev):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload}: batch {B}, {Hq}/{Hkv} heads, d {D}, "
                                f"seq {N}, block {x.block_q}x{x.block_k}, sink {x.sink}, "
-                               f"local {x.local}, {x.granularity}, {est} estimator, theta per "
-                               f"query head {sorted(set(np.round(x.theta, 3).tolist()))}" +
+                               f"local {x.local}, {x.granularity}, {est} estimator, " + theta_desc +
                                (f", step {args.step}" if args.step > 1 else "") +
                                (", anchor-state reuse" if reuse else ""),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_step, 3),
+        "timing": {"reps": args.steps, "statistic": "median of per-repetition HIP event times "
+                                                    "on the library's stream",
+                   "step_ms_median_p10_p90": [round(ms_step, 3), round(p10_step, 3), round(p90_step, 3)],
+                   "estimate_ms_median_p10_p90": [round(est_avg, 3), round(est_p10, 3), round(est_p90, 3)],
+                   "attention_ms_median_p10_p90": [round(att_avg, 3), round(att_p10, 3), round(att_p90, 3)],
+                   "step_ms_mean": round(float(np.mean(step_ms)), 3),
+                   "wall_ms_per_rep_incl_flush": round(wall * 1e3 / args.steps, 3),
+                   "input_copies": 2, "flush_bytes_between_reps": FLUSH_BYTES,
+                   "sclk": sclk.summary()},
         "estimate_ms": round(est_avg, 3), "attention_ms": round(att_avg, 3),
         "estimate_over_attention": round(est_avg / att_avg, 4),
         "kept_density": round(density, 5), "kept_density_per_kv_head": per_group,
         "kept_tile_tflops": round(achieved, 2),
         "kept_tile_frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "useful_pair_tflops": None if useful is None else round(useful / (att_avg * 1e-3) / 1e12, 2),
+        "useful_pair_flops": useful,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if reuse else
@@ -368,6 +511,15 @@ def bench_prefill(args, dev):
     return out
 
 
+def _decode_params(x, kw):
+    from block_sparse_attention_estimate_amd import _lib
+    p = _lib.SaDecodeParams()
+    p.block_k, p.top_k_blocks, p.sink_tokens, p.local_tokens = (kw["block_k"], kw["top_k"],
+                                                                 kw["sink"], kw["local"])
+    p.n_splits, p.softmax_scale, p.top_p = kw["n_splits"], 0.0, float(kw["top_p"] or 0.0)
+    return p
+
+
 def bench_decode(args, dev):
     import torch
     import block_sparse_attention_estimate_amd as sa
@@ -390,16 +542,32 @@ def bench_decode(args, dev):
               n_splits=args.n_splits)
     o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
     n_sel = int((sel >= 0).sum().item())                 # blocks selected over all (b, g)
-    for _ in range(args.warmup):
-        sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
+    # two copies of the caches and summaries, used alternately, and a 512 MB write between
+    # repetitions: the selected K/V (256 MiB) and the summaries would otherwise sit in the MALL
+    kc2, vc2 = kc.clone(), vc.clone()
+    kbar2 = tuple(t.clone() for t in kbar) if isinstance(kbar, tuple) else kbar.clone()
+    copies = [(q, kc, vc, kbar), (q.clone(), kc2, vc2, kbar2)]
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    ws = torch.empty(sa.workspace_size(sa.SA_OP_DECODE, shape=sa._decode_shape(q, kc, vc, o),
+                                       decode_params=_decode_params(x, kw)),
+                     dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        qq, kk, vv, kb = copies[i % 2]
+        sa.sparse_decode(qq, kk, vv, kb, cl, out=o, workspace=ws, return_selected=False, **kw)
+        flush.fill_(float(i))
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        sa.sparse_decode(q, kc, vc, kbar, cl, out=o, **kw)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    with SclkSampler() as sclk:
+        for i in range(args.steps):
+            qq, kk, vv, kb = copies[i % 2]
+            evs[i][0].record(stream)
+            sa.sparse_decode(qq, kk, vv, kb, cl, out=o, workspace=ws, return_selected=False, **kw)
+            evs[i][1].record(stream)
+            flush.fill_(float(i))
+        torch.cuda.synchronize()
+    rep_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+    us, us_p10, us_p90 = pct(rep_us)
     nkb = -(-L // x.block_k)
     sel_bytes = n_sel * x.block_k * D * 2 * 2
     per_row = {"bf16": D * 2, "q4": D // 2 + D // 32 * 2, "fp4": D // 2 + D // 32}[args.summary]
@@ -417,6 +585,12 @@ def bench_decode(args, dev):
                                    f"{args.summary} block summaries",
                        "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
             "us_per_step": round(us, 2),
+            "timing": {"reps": args.steps, "statistic": "median of per-repetition HIP event times "
+                                                        "on the library's stream",
+                       "us_median_p10_p90": [round(us, 2), round(us_p10, 2), round(us_p90, 2)],
+                       "us_mean": round(float(np.mean(rep_us)), 2),
+                       "input_copies": 2, "flush_bytes_between_reps": FLUSH_BYTES,
+                       "sclk": sclk.summary()},
             "mean_blocks_selected": round(n_sel / (B * Hkv), 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -461,7 +635,7 @@ def bench_calibrate(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_128k",
                     choices=list(PREFILL) + ["decode_b16_128k"])

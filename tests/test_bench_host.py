@@ -96,3 +96,28 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_useful_pairs_block_brute_force():
+    """bench.useful_pairs_block counts the causal (row, key) pairs inside kept tiles: checked
+    against a loop over rows and keys on random lists, ragged ends and 32-key blocks."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for N, bq, bk in [(1000, 128, 64), (777, 64, 32), (4096, 128, 64), (130, 64, 64), (1, 64, 64)]:
+        nqb, nkb = -(-N // bq), -(-N // bk)
+        counts = np.zeros((2, 2, nqb), np.int32)
+        idx = np.zeros((2, 2, nqb, nkb), np.int32)
+        want = 0
+        for b in range(2):
+            for g in range(2):
+                for i in range(nqb):
+                    r0, r1 = i * bq, min(N, (i + 1) * bq)
+                    cand = np.arange((r1 - 1) // bk + 1)
+                    kept = np.sort(rng.choice(cand, size=rng.integers(0, len(cand) + 1), replace=False))
+                    counts[b, g, i] = len(kept)
+                    idx[b, g, i, :len(kept)] = kept
+                    for J in kept:
+                        for r in range(r0, r1):
+                            for j in range(J * bk, min(N, J * bk + bk)):
+                                want += j <= r
+        assert bench.useful_pairs_block(counts, idx, nkb, N, bq, bk) == want

@@ -1,8 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
 
-The oracle recomputes sampled rows one by one (every row at 32K); attention parity is
-checked on sampled query blocks whose GPU list equals the oracle's list (the oracle's list
-is the attention input; rows whose lists differ only by ambiguous entries are counted)."""
+The oracle recomputes the lists row by row: every row at 32K, 128K and the 64K stripe
+workload, sampled rows for the element-wise estimators; attention parity is checked on
+sampled query blocks whose GPU list equals the oracle's list (the oracle's list is the
+attention input; rows whose lists differ only by ambiguous entries are counted)."""
 import numpy as np
 import pytest
 
@@ -22,18 +23,26 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled", reuse=False):
+_RUN = {}
+
+
+def _gpu_run(dev, name, estimator, reuse, theta, seed):
+    """The GPU estimate + attention of one workload, kept for the tests that follow (the
+    every-row tests check one KV head each against the same run)."""
     import torch
     import block_sparse_attention_estimate_amd as sa
+    key = (name, estimator, reuse, theta, seed)
+    if key in _RUN:
+        return _RUN[key]
+    _RUN.clear()
     log(f"generating {name}")
     x = synth.make_prefill(name, seed=seed)
-    B, N, Hq, D = x.q.shape
-    Hkv = x.k.shape[2]
-    G = Hq // Hkv
-    nqb = -(-N // x.block_q)
+    if theta is not None:
+        x.theta = np.full(x.q.shape[2], theta, np.float32)
     q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
     kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
     stride = 8192 if x.granularity == "stripe" else None
+    st = None
     if reuse:
         lists, st = sa.estimate_mask_anchor_state(q, k, v, x.theta, **kw)
         o, lse = sa.sparse_prefill_resume(q, k, v, lists, st, **kw)
@@ -43,18 +52,36 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled
         o, lse = sa.sparse_prefill(q, k, v, lists, **kw)
     torch.cuda.synchronize()
     assert not lists.overflowed()
-    rng = np.random.default_rng(seed + 7)
+    run = dict(x=x, lists=lists, o=o.float().cpu(), lse=lse.cpu().numpy(),
+               st=None if st is None else (st.o.float().cpu().numpy(), st.lse.cpu().numpy()))
+    del q, k, v, o, lse, st
+    _RUN[key] = run
+    return run
+
+
+def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled", reuse=False,
+                    theta=None, groups=None):
+    """Lists of `n_rows` sampled rows (None: every row of the KV heads in `groups`, default
+    all) against the oracle, and the attention of `n_attn` query blocks among them."""
+    run = _gpu_run(dev, name, estimator, reuse, theta, seed)
+    x, lists = run["x"], run["lists"]
+    B, N, Hq, D = x.q.shape
+    Hkv = x.k.shape[2]
+    G = Hq // Hkv
+    nqb = -(-N // x.block_q)
+    groups = list(range(Hkv)) if groups is None else list(groups)
+    rng = np.random.default_rng(seed + 7 + 101 * groups[0])
     if n_rows is None:
-        rows = [(0, g, i) for g in range(Hkv) for i in range(nqb)]
+        rows = [(0, g, i) for g in groups for i in range(nqb)]
     else:
         gi = set()
-        for g in range(Hkv):                     # first, last and random query blocks
+        for g in groups:                         # first, last and random query blocks
             gi.add((g, 0))
             gi.add((g, nqb - 1))
         while len(gi) < n_rows:
-            gi.add((int(rng.integers(0, Hkv)), int(rng.integers(0, nqb))))
+            gi.add((int(rng.choice(groups)), int(rng.integers(0, nqb))))
         rows = sorted((0, g, i) for g, i in gi)
-    log(f"oracle estimate of {len(rows)} rows ({estimator})")
+    log(f"oracle estimate of {len(rows)} rows ({estimator}, KV heads {groups})")
     if estimator == "pooled":
         ref = oracle.estimate_rows(x.q, x.k, x.theta, rows=rows, keep_margins=False,
                                    block_q=x.block_q, block_k=x.block_k, sink=x.sink,
@@ -62,7 +89,8 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled
     else:
         ref = oracle.estimate_rows_sale(x.q, x.k, x.theta, rows=rows, keep_margins=False,
                                         block_q=x.block_q, block_k=x.block_k, sink=x.sink,
-                                        local=x.local)
+                                        local=x.local,
+                                        lowbit="mxfp4" if estimator == "relative_mxfp4" else "int8")
     nrows, entries, flips = compare_lists(lists, ref)
     log(f"  lists ok: rows={nrows} entries={entries} ambiguous flips={flips}")
     counts = lists.counts.cpu().numpy()
@@ -74,13 +102,13 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled
     last = [key for key in same if key[2] == nqb - 1]
     if last and last[0] not in pick:
         pick[-1] = last[0]
+    pick.sort()                                  # grouped by KV head for the oracle
     arows = [(b, g * G + int(rng.integers(0, G)), i) for (b, g, i) in pick]
     log(f"oracle attention of {len(arows)} query blocks")
     res = oracle.attention_rows(x.q, x.k, x.v, {key: ref[key]["kept"] for key in pick},
                                 rows=arows, block_q=x.block_q, block_k=x.block_k,
                                 granularity=x.granularity)
-    og = o.float().cpu()
-    lg = lse.cpu().numpy()
+    og, lg = run["o"], run["lse"]
     errs, lerrs = [], []
     for (b, h, i), (oref, lref) in res.items():
         r0 = i * x.block_q
@@ -95,8 +123,7 @@ def _prefill_parity(dev, name, n_rows=None, n_attn=12, seed=0, estimator="pooled
     if reuse:
         sref = oracle.anchor_state_rows(x.q, x.k, x.v, block_q=x.block_q, sink=x.sink,
                                         local=x.local, rows=arows)
-        so = st.o.float().cpu().numpy()
-        sl = st.lse.cpu().numpy()
+        so, sl = run["st"]
         e1, e2 = [], []
         for (b, h, i), (oa, la) in sref.items():
             r0 = i * x.block_q
@@ -118,8 +145,25 @@ def test_llama8b_32k_relative_sampled(dev):
     _prefill_parity(dev, "llama8b_32k", n_rows=32, n_attn=10, estimator="relative")
 
 
-def test_llama8b_128k_sampled(dev):
-    _prefill_parity(dev, "llama8b_128k", n_rows=40, n_attn=12)
+@pytest.mark.parametrize("g", range(8))
+def test_llama8b_128k_every_row(dev, g):
+    """The headline workload, one KV head per case (one GPU run for all eight): every (b, g, i)
+    list of the 128K layer against the oracle, and the attention of 25 query blocks per KV
+    head, 200 in all (random, plus a last block)."""
+    _prefill_parity(dev, "llama8b_128k", n_rows=None, n_attn=25, groups=[g])
+
+
+def test_llama8b_128k_relative_sampled(dev):
+    """SALE's element-wise int8 estimator at 128K in bench.py's configuration for it
+    (--estimator relative --theta 4.83, i.e. tau = 0.008 on every head)."""
+    _prefill_parity(dev, "llama8b_128k", n_rows=16, n_attn=6, estimator="relative", theta=4.83)
+
+
+def test_llama8b_32k_relative_mxfp4_sampled(dev):
+    """The MXFP4 relative estimator at 32K in bench.py's configuration for it
+    (--estimator relative_mxfp4 --theta 4.83)."""
+    _prefill_parity(dev, "llama8b_32k", n_rows=32, n_attn=10, estimator="relative_mxfp4",
+                    theta=4.83)
 
 
 @pytest.mark.parametrize("name", ["llama8b_32k", "llama8b_128k"])
@@ -128,8 +172,11 @@ def test_anchor_reuse_sampled(dev, name):
     _prefill_parity(dev, name, n_rows=24, n_attn=10, reuse=True)
 
 
-def test_stripe_64k_sampled(dev):
-    _prefill_parity(dev, "stripe_64k", n_rows=24, n_attn=10)
+@pytest.mark.parametrize("gs", [(0, 1, 2, 3), (4, 5, 6, 7)])
+def test_stripe_64k_every_row(dev, gs):
+    """Every column list of the 64K stripe workload against the oracle (four KV heads per
+    case, one GPU run for both), and the attention of 8 query blocks per case."""
+    _prefill_parity(dev, "stripe_64k", n_rows=None, n_attn=8, groups=gs)
 
 
 @pytest.mark.parametrize("summary", ["bf16", "q4", "fp4", "bf16-topp"])
