@@ -29,7 +29,7 @@ from ._lib import (SA_BLOCK, SA_STRIPE, SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DEC
 __all__ = ["Lists", "AnchorState", "alloc_anchor_state", "estimate_mask", "sparse_prefill",
            "estimate_mask_anchor_state", "sparse_prefill_resume", "build_block_summary",
            "quantize_block_summary", "quantize_block_summary_fp4", "sparse_decode",
-           "calibrate_theta", "workspace_size",
+           "sparse_decode_noalloc", "calibrate_theta", "workspace_size",
            "SaError", "load_library"]
 
 
@@ -450,3 +450,24 @@ def sparse_decode(q, k_cache, v_cache, k_summary, cache_len, *, block_k=64, top_
                                         _ptr(lse), _ptr(sel), _ptr(workspace), workspace.numel(),
                                         _stream(stream)), "sa_sparse_decode")
     return o, lse, sel
+
+
+def sparse_decode_noalloc(q, k_cache, v_cache, k_summary, cache_len, *, out, lse, selected=None,
+                          block_k=64, top_k=64, sink=32, local=256, n_splits=0, softmax_scale=0.0,
+                          top_p=0.0, kv_head_of_q=None, stream=None):
+    """sa_sparse_decode_noalloc: sparse_decode with bf16 summaries whose scratch is the
+    library's static per-GPU array (no workspace, nothing allocated by the call).  The caller
+    passes every output: out [B, Hq, d] bf16, lse [B, Hq] fp32, optional selected [B, Hkv,
+    top_k] int32.  Calls that overlap on one GPU race (they share the array)."""
+    lib = _lib.load()
+    _check_bf16("v_cache", v_cache, 4)
+    s = _decode_shape(q, k_cache, v_cache, out, kv_head_of_q=kv_head_of_q)
+    p = _lib.SaDecodeParams()
+    p.block_k, p.top_k_blocks, p.sink_tokens, p.local_tokens = block_k, top_k, sink, local
+    p.n_splits, p.softmax_scale = n_splits, float(softmax_scale or 0.0)
+    p.top_p = float(top_p or 0.0)
+    _lib.check(lib.sa_sparse_decode_noalloc(ctypes.byref(s), ctypes.byref(p), _ptr(q), _ptr(k_cache),
+                                            _ptr(v_cache), _ptr(k_summary), _ptr(cache_len),
+                                            _ptr(out), _ptr(lse), _ptr(selected), _stream(stream)),
+               "sa_sparse_decode_noalloc")
+    return out, lse, selected

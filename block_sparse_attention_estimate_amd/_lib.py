@@ -22,7 +22,8 @@ EXPORTED = ("sa_workspace_size", "sa_estimate_mask", "sa_sparse_prefill",
             "sa_build_block_summary", "sa_sparse_decode", "sa_quantize_block_summary",
             "sa_sparse_decode_q4", "sa_calibrate_theta", "sa_status_string",
             "sa_estimate_mask_anchor_state", "sa_sparse_prefill_resume",
-            "sa_quantize_block_summary_fp4", "sa_sparse_decode_fp4")
+            "sa_quantize_block_summary_fp4", "sa_sparse_decode_fp4", "sa_sparse_decode_noalloc")
+SA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class SaShape(ctypes.Structure):
@@ -94,6 +95,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sa_sparse_decode.restype = ctypes.c_int
     lib.sa_sparse_decode.argtypes = [P(SaShape), P(SaDecodeParams), vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, ctypes.c_size_t, vp]
+    lib.sa_sparse_decode_noalloc.restype = ctypes.c_int
+    lib.sa_sparse_decode_noalloc.argtypes = [P(SaShape), P(SaDecodeParams), vp, vp, vp, vp, vp, vp,
+                                             vp, vp, vp]
     lib.sa_quantize_block_summary.restype = ctypes.c_int
     lib.sa_quantize_block_summary.argtypes = [P(SaShape), ctypes.c_int32, vp, vp, vp, vp]
     lib.sa_sparse_decode_q4.restype = ctypes.c_int

@@ -3,7 +3,15 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sa_internal.h"
+
+// Scratch of sa_sparse_decode_noalloc: one array per GPU (each device holds its own copy of
+// the code object's data), held until the process ends.  Host code never uses the name of the
+// array as an address: it looks up each device's address once (hipGetSymbolAddress, with the
+// device current) and passes that pointer to the kernels.
+static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -463,6 +471,41 @@ static sa_status decode_impl(const sa_shape* shape, const sa_decode_params* para
   a.c = resolve_scale(params->softmax_scale, shape->head_dim);
   if (launch_decode(a, stream) != hipSuccess) return SA_ERR_DEVICE;
   return SA_OK;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's address of `scratch`, looked up on the first call with that device
+sa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return SA_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+}  // namespace
+
+sa_status sa_sparse_decode_noalloc(const sa_shape* shape, const sa_decode_params* params,
+                                   const void* q, const void* k_cache, const void* v_cache,
+                                   const void* k_summary, const int32_t* cache_len, void* o,
+                                   float* lse, int32_t* selected, hipStream_t stream) {
+  sa_status st = check_decode(shape, params);
+  if (st != SA_OK) return st;
+  if (!k_summary) return SA_ERR_NULL;
+  if (dec_layout(shape, params).total > SA_NOALLOC_SCRATCH_BYTES) return SA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != SA_OK) return st;
+  return decode_impl(shape, params, q, k_cache, v_cache, k_summary, nullptr, nullptr, nullptr,
+                     cache_len, o, lse, selected, ws, SA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params, const void* q,

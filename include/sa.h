@@ -259,6 +259,24 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params
                            void* o, float* lse, int32_t* selected,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* sa_sparse_decode without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The call's scratch (block scores, the selection, per-split partial outputs)
+ * lives in a static device array of SA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU
+ * it runs on until the process ends; its address is looked up once per device, on the first
+ * call with that device current, and no call allocates or frees memory.  Every call on a GPU
+ * uses that GPU's one array and may leave data in it: calls that overlap on one GPU (other
+ * streams, other host threads) race, so the caller serialises them.  Arguments, results and
+ * errors as sa_sparse_decode, plus SA_ERR_WORKSPACE when the call needs more scratch than
+ * SA_NOALLOC_SCRATCH_BYTES (sa_workspace_size(SA_OP_DECODE, ...) gives the need: about 1.6 MB
+ * at batch 16, 32/8 heads, a 128K-token cache, K = 64) and SA_ERR_DEVICE when the array's
+ * device address cannot be obtained. */
+#define SA_NOALLOC_SCRATCH_BYTES (16u << 20)
+sa_status sa_sparse_decode_noalloc(const sa_shape* shape, const sa_decode_params* params,
+                                   const void* q, const void* k_cache, const void* v_cache,
+                                   const void* k_summary, const int32_t* cache_len,
+                                   void* o, float* lse, int32_t* selected, hipStream_t stream);
+
 /* 4-bit block summaries (SpotAttention, "Key findings": quantising the selector's key cache
  * to INT4 / FP4 shrinks it 3.5x at no accuracy cost).  From bf16 summaries (as written by
  * sa_build_block_summary, contiguous [B, ceil(seq_k/block_k), Hkv, d]) each row is cut into

@@ -169,6 +169,22 @@ def test_validation_codes(lib):
     assert lib.sa_sparse_decode_fp4(*args_fp4, FAKE, dneed, None) == _lib.SA_ERR_NULL
     args_fp4[6] = FAKE
     assert lib.sa_sparse_decode_fp4(*args_fp4, FAKE, dneed - 1, None) == _lib.SA_ERR_WORKSPACE
+    # the no-allocation decode: validation as sa_sparse_decode, then the static scratch limit
+    nargs = [ctypes.byref(ds), ctypes.byref(dp), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None,
+             None]
+    assert lib.sa_sparse_decode_noalloc(*nargs) == _lib.SA_ERR_NULL          # no summary
+    big = _shape(B=64, Hq=32, Hkv=8, N=8192 * 64)
+    big.seq_q = 1
+    bp = _lib.SaDecodeParams()
+    bp.block_k, bp.top_k_blocks, bp.sink_tokens, bp.local_tokens = 64, 64, 32, 256
+    assert lib.sa_workspace_size(_lib.SA_OP_DECODE, ctypes.byref(big), ctypes.byref(bp)) > \
+        _lib.SA_NOALLOC_SCRATCH_BYTES
+    assert lib.sa_sparse_decode_noalloc(ctypes.byref(big), ctypes.byref(bp), FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, None, None, None) == _lib.SA_ERR_WORKSPACE
+    dp.top_k_blocks = 0
+    assert lib.sa_sparse_decode_noalloc(ctypes.byref(ds), ctypes.byref(dp), FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, None, None, None) == _lib.SA_ERR_PARAM
+    dp.top_k_blocks = 8
     assert lib.sa_workspace_size(_lib.SA_OP_PREFILL, ctypes.byref(s), ctypes.byref(p)) == 0
 
 
