@@ -110,16 +110,27 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   if (STRIPE) {
     // column lists: the entries this work item can see (<= r_last, ascending); tiles of 64
     // gathered columns; tiles from n_main on need a mask (a column past the first row's
-    // diagonal or the end, or entries past the list's end)
-    int lo = 0, hi = n;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (list[mid] <= r_last) lo = mid + 1; else hi = mid;
-    }
-    n = lo;
+    // diagonal or the end, or entries past the list's end).  The entries <= a limit are a
+    // prefix of the list, counted by a 64-way search: each round every lane reads one entry
+    // (vector loads, one round trip per round) and the wave's ballot narrows the range to one
+    // lane's stride.
+    auto count_le = [&](int limit) -> int {
+      int lo = 0, len = n;                       // the count lies in [lo, lo + len]
+      while (len > 0) {
+        const int step = (len + 63) >> 6;
+        const int idx = lo + min((lane + 1) * step, len) - 1;
+        const int c = __popcll(__ballot(list_g[idx] <= limit));
+        const int a0 = min(c * step, len);       // entries known to pass
+        const int a1 = min((c + 1) * step, len) - 1;  // the entry at a1 fails (when c < 64)
+        lo += a0;
+        len = c >= 64 ? 0 : a1 - a0;
+      }
+      return lo;
+    };
+    const int n0 = count_le(r0);                 // entries visible to every row of the item
+    n = count_le(r_last);
     ntile = (n + 63) / 64;
-    n_main = ntile;
-    while (n_main > 0 && (list[min(n_main * 64, n) - 1] > r0 || n_main * 64 > n)) --n_main;
+    n_main = n0 / 64;                            // full tiles of entries <= r0
   } else if (BK32) {
     // 32-key block lists: two listed blocks per tile; blocks from `r_last + 1` on hold no key
     // of this work item; the tiles from n_main on need a mask (a block past the first row's

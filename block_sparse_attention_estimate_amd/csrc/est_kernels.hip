@@ -25,6 +25,8 @@
 //
 // Floating-point steps that decide an integer (int8 codes, keep bits) use explicit
 // round-to-nearest operations (__fmul_rn, __fdiv_rn, rintf) in the order the oracle uses.
+#include <type_traits>
+
 #include "sa_common.h"
 #include "sa_internal.h"
 
@@ -163,6 +165,17 @@ __global__ __launch_bounds__(64 * EST_AP_WAVES) void est_anchor_pool(EstArgs a) 
     const int n_win_t = win_start <= hi_blk ? (hi_blk - win_start) / 32 + 1 : 0;
     const int n_rows = (n_sink_t + n_win_t) * 32;     // <= MAXROWS for local <= 352, bq <= 128
     auto tile_start = [&](int t) { return t < n_sink_t ? t * 32 : win_start + (t - n_sink_t) * 32; };
+    // Q fragments of this wave's n-tiles (32 rows of one head each), the next one loaded while
+    // the current one's MFMAs run; the first goes out before the keys are staged
+    auto load_q = [&](int nt, bf16x8* qf) {
+      const int hg = nt / ntph, tr = nt % ntph;
+      const int rowc = min(r0 + tr * 32 + l32, a.N - 1);
+      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + a.qh[g * G + hg] * a.qs2 + half * 8;
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
+    };
+    bf16x8 qn[KS];
+    if (wave < G * ntph) load_q(wave, qn);
     {
       const uint16_t* kb = a.k + b * a.ks0 + g * a.ks2;
       const int nwin = (n_rows * KPITCH + 1023) / 1024;
@@ -178,17 +191,6 @@ __global__ __launch_bounds__(64 * EST_AP_WAVES) void est_anchor_pool(EstArgs a) 
     }
     const int k_rd = l32 * KPITCH + half * 16;
 
-    // Q fragments of this wave's n-tiles (32 rows of one head each), the next one loaded while
-    // the current one's MFMAs run
-    auto load_q = [&](int nt, bf16x8* qf) {
-      const int hg = nt / ntph, tr = nt % ntph;
-      const int rowc = min(r0 + tr * 32 + l32, a.N - 1);
-      const uint16_t* qp = a.q + b * a.qs0 + (int64_t)rowc * a.qs1 + a.qh[g * G + hg] * a.qs2 + half * 8;
-  #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
-    };
-    bf16x8 qn[KS];
-    if (wave < G * ntph) load_q(wave, qn);
     for (int nt = wave; nt < G * ntph; nt += NW) {
       const int hg = nt / ntph, tr = nt % ntph;
       const int ra = r0 + tr * 32;
@@ -664,7 +666,7 @@ SA_DEV void read_key_fragments<2, 80>(unsigned int addr, i32x4 (&kf)[2][2]) {
 // Workgroup = 4 waves x 64 rows, 32 key tiles of 64 columns.
 // ---------------------------------------------------------------------------------------
 template <int D, int G, bool MARGINS>
-__global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, int n_jc) {
+__global__ __launch_bounds__(256, 4) void est_score_stripe(EstArgs a, int n_rt, int n_jc) {
   // The host pass only needs this kernel's signature (for its launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KS = D / 32;
@@ -708,15 +710,27 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
   int erw[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) erw[r] = erow(Rw + half * 4 + 8 * (r >> 2) + (r & 3));
+  // The keep test fp32(D * sq * sk * c) >= thr, rewritten per row as D * sk >= u with
+  // u = thr / (sq * c) (a zero threshold stays zero, so 0 >= 0 keeps when a scale is zero):
+  // per tile one product u * (1 / sk) per row, then per element one conversion and one
+  // compare.  The decision can differ from the fp32 product only where the margin is within a
+  // few ulps of zero (far inside the ambiguity band of the lists).
+  float uthr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) uthr[r] = thr[r] == 0.f ? 0.f : thr[r] / (sqv[r] * a.c);
+  // the first row of the wave sees the fewest keys: tiles up to its last key need no causal test
+  const int e_first = erow(Rw);
 
-  // K tiles go HBM -> LDS with direct loads into six stages shared by the four waves (rows
-  // padded to D + 16 bytes, so the 16 rows one quarter-wave reads land on distinct banks);
-  // a step is short here (8 MFMAs), so four tiles are kept in flight.  The stages are one
+  // K tiles go HBM -> LDS with direct loads into three stages shared by the four waves (rows
+  // padded to D + 16 bytes, so the 16 rows one quarter-wave reads land on distinct banks).
+  // A step is short here (8 MFMAs) and latency-bound, so the stages are few and four
+  // workgroups share a CU (16 waves) rather than keeping many tiles in flight per workgroup:
+  // at 64K this is 1.4x faster than six stages at two workgroups per CU.  The stages are one
   // array indexed at run time, so the loop body (and the kernel's code) exists once.
   constexpr int KP = D + 16;
   constexpr int WIN = (64 * KP + 1023) / 1024;       // 1 KB windows per tile
   constexpr int SL = (WIN + 3) / 4;                   // windows per wave
-  constexpr int NST = 6;
+  constexpr int NST = 3;
   __shared__ __attribute__((aligned(1024))) unsigned char kst[NST * WIN * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char kspare[1024];
   auto stage = [&](int j) { return kst + (j % NST) * (WIN * 1024); };
@@ -756,9 +770,19 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
       for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma_i8(qf[ks], kf[nt][ks], acc[nt]);
     const float skv = load_uniform(a.sk + (int64_t)bg * a.nKB + J);
     // keep <=> fp32(fp32(D) * m) - (abar - theta) >= 0 <=> fp32(fp32(D) * m) >= (abar - theta)
-    float mult[16];
+    float mult[16], tk[16];
+    if (MARGINS) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mult[r] = __fmul_rn(__fmul_rn(sqv[r], skv), a.c);
+      for (int r = 0; r < 16; ++r) mult[r] = __fmul_rn(__fmul_rn(sqv[r], skv), a.c);
+    } else {
+      // D >= u / sk (1 / sk clamped to a finite value: a zero tile has D = 0, kept iff u <= 0)
+      const float isk = fminf(1.0f / skv, 1e30f);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tk[r] = uthr[r] * isk;
+    }
+    // the keep bits and margins of the tile; CAUSAL: some key may lie past a row's last key
+    auto epilogue = [&](auto causal_tag) {
+    constexpr bool CAUSAL = decltype(causal_tag)::value;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int key = J * 64 + nt * 32 + l32;
@@ -770,8 +794,14 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int r = 4 * ag + bb;
-          const float y = __fmul_rn((float)acc[nt][r], mult[r]);
-          bal[bb] = __ballot(y >= thr[r] && key <= erw[r]);
+          if (MARGINS) {
+            const float y = __fmul_rn((float)acc[nt][r], mult[r]);
+            bal[bb] = __ballot(y >= thr[r] && key <= erw[r]);
+          } else if (!CAUSAL) {
+            bal[bb] = __ballot((float)acc[nt][r] >= tk[r]);
+          } else {
+            bal[bb] = __ballot((float)acc[nt][r] >= tk[r] && key <= erw[r]);
+          }
         }
         const int Rg = Rw + 8 * ag;                      // first row of this 8-row group
         if (lane == 0) {
@@ -826,11 +856,17 @@ __global__ __launch_bounds__(256, 2) void est_score_stripe(EstArgs a, int n_rt, 
         }
       }
     }
+    };
+    // one branch per tile: tiles wholly before the wave's first row's last key skip the test
+    if (MARGINS || J * 64 + 63 > e_first)
+      epilogue(std::integral_constant<bool, true>{});
+    else
+      epilogue(std::integral_constant<bool, false>{});
   };
 
-  // Tile J0 + j is in stage j % 6; tiles j+1 .. j+4 are loaded or in flight.  Step j computes
-  // tile j, issues tile j+5 (clamped to the last tile, so every wave issues SL loads per step)
-  // into the stage of tile j-1 and waits until tile j+1 has landed.
+  // Tile J0 + j is in stage j % NST; tiles j+1 .. j+NST-2 are loaded or in flight.  Step j
+  // computes tile j, issues tile j+NST-1 (clamped to the last tile, so every wave issues SL
+  // loads per step) into the stage of tile j-1 and waits until tile j+1 has landed.
   const int nt_ = J_end - J0;
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p) issue(stage(p), J0 + min(p, nt_ - 1));
