@@ -168,7 +168,35 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-FLUSH_BYTES = 512 << 20       # written between timed repetitions (larger than the 256 MB MALL)
+FLUSH_BYTES = 512 << 20       # touched between timed repetitions (larger than the 256 MB MALL)
+
+
+class CacheFlush:
+    """Evicts the inputs from the caches between timed repetitions by touching FLUSH_BYTES of
+    another buffer, outside the timed events.  "read" (default) sums the buffer: the caches end
+    up full of clean lines, so the next repetition pays no write-back.  "write" fills it: up to
+    the memory-side cache's 256 MB of dirty lines are then written back to HBM while the next
+    repetition runs, which slows short steps (decode) by the time of that write-back.  "none"
+    leaves the caches warm (the two input copies still alternate)."""
+
+    def __init__(self, mode, dev):
+        import torch
+        self.mode = mode
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) \
+            if mode != "none" else None
+        self.sink = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def __call__(self, i):
+        import torch
+        if self.mode == "read":
+            torch.sum(self.buf, dim=0, out=self.sink)
+        elif self.mode == "write":
+            self.buf.fill_(float(i))
+
+    def describe(self):
+        return {"read": f"{FLUSH_BYTES} B read (sum) between reps",
+                "write": f"{FLUSH_BYTES} B written (fill) between reps",
+                "none": "none (warm caches)"}[self.mode]
 
 
 class SclkSampler:
@@ -359,7 +387,7 @@ def bench_prefill(args, dev):
     # two copies of the inputs, used alternately, and a 512 MB write between repetitions, so
     # that no repetition finds its inputs in the caches (the MALL holds 256 MB)
     copies = [(q, k, v), tuple(t.clone() for t in (q, k, v))]
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = CacheFlush(args.flush, dev)
 
     def step(i, ev=None):
         qq, kk, vv = copies[i % 2]
@@ -383,7 +411,7 @@ def bench_prefill(args, dev):
     log("warmup")
     for i in range(args.warmup):
         step(i)
-        flush.fill_(float(i))
+        flush(i)
     torch.cuda.synchronize()
     if x.granularity == "stripe" and lists.overflowed():
         raise SystemExit("stripe list capacity exceeded; raise --stripe-capacity")
@@ -394,7 +422,7 @@ def bench_prefill(args, dev):
         t0 = time.perf_counter()
         for i in range(args.steps):
             step(i, evs[i])
-            flush.fill_(float(i))               # outside the timed events
+            flush(i)                            # outside the timed events
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     est_ms = [e[0].elapsed_time(e[1]) for e in evs]
@@ -477,7 +505,7 @@ def bench_prefill(args, dev):
                    "attention_ms_median_p10_p90": [round(att_avg, 3), round(att_p10, 3), round(att_p90, 3)],
                    "step_ms_mean": round(float(np.mean(step_ms)), 3),
                    "wall_ms_per_rep_incl_flush": round(wall * 1e3 / args.steps, 3),
-                   "input_copies": 2, "flush_bytes_between_reps": FLUSH_BYTES,
+                   "input_copies": 2, "flush_between_reps": flush.describe(),
                    "sclk": sclk.summary()},
         "estimate_ms": round(est_avg, 3), "attention_ms": round(att_avg, 3),
         "estimate_over_attention": round(est_avg / att_avg, 4),
@@ -547,14 +575,14 @@ def bench_decode(args, dev):
     kc2, vc2 = kc.clone(), vc.clone()
     kbar2 = tuple(t.clone() for t in kbar) if isinstance(kbar, tuple) else kbar.clone()
     copies = [(q, kc, vc, kbar), (q.clone(), kc2, vc2, kbar2)]
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = CacheFlush(args.flush, dev)
     ws = torch.empty(sa.workspace_size(sa.SA_OP_DECODE, shape=sa._decode_shape(q, kc, vc, o),
                                        decode_params=_decode_params(x, kw)),
                      dtype=torch.uint8, device=dev)
     for i in range(args.warmup):
         qq, kk, vv, kb = copies[i % 2]
         sa.sparse_decode(qq, kk, vv, kb, cl, out=o, workspace=ws, return_selected=False, **kw)
-        flush.fill_(float(i))
+        flush(i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -564,7 +592,7 @@ def bench_decode(args, dev):
             evs[i][0].record(stream)
             sa.sparse_decode(qq, kk, vv, kb, cl, out=o, workspace=ws, return_selected=False, **kw)
             evs[i][1].record(stream)
-            flush.fill_(float(i))
+            flush(i)
         torch.cuda.synchronize()
     rep_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
     us, us_p10, us_p90 = pct(rep_us)
@@ -589,7 +617,7 @@ def bench_decode(args, dev):
                                                         "on the library's stream",
                        "us_median_p10_p90": [round(us, 2), round(us_p10, 2), round(us_p90, 2)],
                        "us_mean": round(float(np.mean(rep_us)), 2),
-                       "input_copies": 2, "flush_bytes_between_reps": FLUSH_BYTES,
+                       "input_copies": 2, "flush_between_reps": flush.describe(),
                        "sclk": sclk.summary()},
             "mean_blocks_selected": round(n_sel / (B * Hkv), 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -642,6 +670,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--stripe-capacity", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="how the caches are flushed between timed repetitions")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (byte-counter scale)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
