@@ -70,10 +70,10 @@ def summarize_pmc(fetch_dir, write_dir, kernel, workload, src, command):
                 if kernel in r["Kernel_Name"]:
                     vals.append(float(r["Counter_Value"]))
                 elif "copyBuffer" in r["Kernel_Name"]:
-                    copy.append(float(r["Counter_Value"]))
-        # the calibration copy is by far the largest copy dispatch of the run
+                    copy.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        # the calibration copy is the run's last copy dispatch (after the timed steps)
         return (sum(vals) / len(vals) if vals else float("nan"),
-                max(copy) if copy else float("nan"), len(vals))
+                max(copy)[1] if copy else float("nan"), len(vals))
 
     f_k, f_c, n_f = per_dispatch(fetch_dir, "FETCH_SIZE")
     w_k, w_c, n_w = per_dispatch(write_dir, "WRITE_SIZE")
@@ -107,6 +107,18 @@ def _pmc_values(d, counter, kernel):
     return vals
 
 
+def _last_copy(d, counter):
+    """`counter` of the run's last copy dispatch (the calibration copy after the timed steps)."""
+    import csv
+    import glob
+    copy = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]:
+                copy.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return max(copy)[1] if copy else float("nan")
+
+
 def summarize_mfma(util_dir, raw_dir, kernel, workload, src, command):
     """MFMA counters of `kernel`: the derived MfmaUtil (MFMA-busy cycles summed over SIMDs over
     GPU-active cycles times the SIMD count) from one pass, and the bf16 / int8 MFMA operation
@@ -134,8 +146,8 @@ def summarize_kernels(fetch_dir, write_dir, stats_csv, kernels, workload, comman
     dur = {}
     for r in csv.DictReader(open(stats_csv)):
         dur[r["Name"]] = float(r["AverageNs"])
-    fc = max(_pmc_values(fetch_dir, "FETCH_SIZE", "copyBuffer") or [float("nan")])
-    wc = max(_pmc_values(write_dir, "WRITE_SIZE", "copyBuffer") or [float("nan")])
+    fc = _last_copy(fetch_dir, "FETCH_SIZE")
+    wc = _last_copy(write_dir, "WRITE_SIZE")
     fs, ws = COPY_BYTES / (fc * 1024.0), COPY_BYTES / (wc * 1024.0)
     lines = [f"# HBM bytes and achieved GB/s per kernel on {workload}",
              f"command: {command}",
@@ -152,6 +164,23 @@ def summarize_kernels(fetch_dir, write_dir, stats_csv, kernels, workload, comman
         us = dur[names[0]] / 1e3 if names else float("nan")
         lines.append(f"{k:44s} {fb / 1e6:10.1f} {wb / 1e6:10.1f} {us:10.1f} "
                      f"{(fb + wb) / (us * 1e3):8.0f}")
+    return "\n".join(lines)
+
+
+def summarize_stats(stats_csv, title, command):
+    """Text summary of a rocprofv3 --kernel-trace --stats run: calls, average duration, total
+    and share per kernel (longest total first), with the hashes of the kernel sources."""
+    import csv
+    rows = sorted(csv.DictReader(open(stats_csv)), key=lambda r: -float(r["TotalDurationNs"]))
+    srcs = {n: source_hash(os.path.join(ROOT, "block_sparse_attention_estimate_amd", "csrc", n + ".hip"))
+            for n in ("attn_kernels", "est_kernels", "anchor_kernels", "decode_kernels")}
+    lines = [f"# Kernel trace summary, {title}",
+             f"command: {command}",
+             "kernel_sources_sha256_16: " + ", ".join(f"{k} {v}" for k, v in srcs.items()),
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.2f} {float(r['Percentage']):6.2f}")
     return "\n".join(lines)
 
 
@@ -680,6 +709,9 @@ def main():
                     help="print the MFMA counter summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-kernels", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_CSV"),
                     help="print per-kernel HBM bytes and GB/s for --kernels and exit")
+    ap.add_argument("--summarize-stats", metavar="STATS_CSV",
+                    help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--title", default="", help="title line of --summarize-stats")
     ap.add_argument("--kernels", default="est_quant_k,est_anchor_pool,est_score_block,est_compact")
     ap.add_argument("--kernel", default="attn_block")
     ap.add_argument("--summary", choices=["bf16", "q4", "fp4"], default="bf16",
@@ -717,6 +749,9 @@ def main():
     if args.summarize_kernels:
         print(summarize_kernels(*args.summarize_kernels, args.kernels.split(","), args.workload,
                                 args.command))
+        return
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats, args.title, args.command))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the workload "
