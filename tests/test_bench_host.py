@@ -16,10 +16,12 @@ def _write_counters(d, rows):
     """A rocprofv3 --pmc output folder with one counter_collection CSV of (kernel, counter, value)."""
     os.makedirs(d, exist_ok=True)
     with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value"])
         w.writeheader()
-        for k, c, v in rows:
-            w.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+        for i, (k, c, v) in enumerate(rows):       # dispatches in the order given
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": k, "Counter_Name": c,
+                        "Counter_Value": v})
 
 
 def _kv(text):
@@ -33,14 +35,18 @@ def _kv(text):
 
 def test_summarize_pmc_scales_by_the_copy(tmp_path):
     # FETCH_SIZE reads half the copy's bytes (scale 2), WRITE_SIZE all of them (scale 1); the
-    # kernel's two dispatches average to 3000 KiB fetched and 500 KiB written.
+    # kernel's two dispatches average to 3000 KiB fetched and 500 KiB written.  The calibration
+    # copy is the run's last copy dispatch: earlier copies (input copies, larger or smaller)
+    # do not count.
     copy_kib = bench.COPY_BYTES / 1024
-    _write_counters(tmp_path / "f", [("void attn_block<128, 4, false, false>(AttnArgs)", "FETCH_SIZE", 2000),
+    _write_counters(tmp_path / "f", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 3.0),
+                                     ("__amd_rocclr_copyBuffer", "FETCH_SIZE", copy_kib * 4),
+                                     ("void attn_block<128, 4, false, false>(AttnArgs)", "FETCH_SIZE", 2000),
                                      ("void attn_block<128, 4, false, false>(AttnArgs)", "FETCH_SIZE", 4000),
-                                     ("__amd_rocclr_copyBuffer", "FETCH_SIZE", copy_kib / 2),
-                                     ("__amd_rocclr_copyBuffer", "FETCH_SIZE", 3.0),
-                                     ("est_compact(EstArgs)", "FETCH_SIZE", 99999)])
-    _write_counters(tmp_path / "w", [("void attn_block<128, 4, false, false>(AttnArgs)", "WRITE_SIZE", 500),
+                                     ("est_compact(EstArgs)", "FETCH_SIZE", 99999),
+                                     ("__amd_rocclr_copyBuffer", "FETCH_SIZE", copy_kib / 2)])
+    _write_counters(tmp_path / "w", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", copy_kib * 8),
+                                     ("void attn_block<128, 4, false, false>(AttnArgs)", "WRITE_SIZE", 500),
                                      ("void attn_block<128, 4, false, false>(AttnArgs)", "WRITE_SIZE", 500),
                                      ("__amd_rocclr_copyBuffer", "WRITE_SIZE", copy_kib)])
     text = bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "attn_block", "w",
