@@ -198,6 +198,13 @@ sa_status check_decode(const sa_shape* s, const sa_decode_params* p) {
   if (isnan(p->softmax_scale) || isinf(p->softmax_scale)) return SA_ERR_PARAM;
   if (!(p->top_p >= 0.f && p->top_p <= 1.f)) return SA_ERR_PARAM;
   if (ceil_div(s->seq_k, p->block_k) > 8192) return SA_ERR_UNSUPPORTED;
+  // K must hold the whole forced set at every cache length: the blocks the sink tokens
+  // overlap plus the most blocks a window of `local` tokens can overlap (unless K covers
+  // every block of the cache, when everything is selected anyway)
+  const int64_t f_max = ((int64_t)p->sink_tokens + p->block_k - 1) / p->block_k +
+                        ((int64_t)p->local_tokens - 1) / p->block_k + 2;
+  if (p->top_k_blocks < f_max && p->top_k_blocks < ceil_div(s->seq_k, p->block_k))
+    return SA_ERR_PARAM;
   if (!strides_ok(s->q_stride) || !strides_ok(s->k_stride) || !strides_ok(s->v_stride) ||
       !strides_ok(s->o_stride))
     return SA_ERR_SHAPE;

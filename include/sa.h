@@ -152,7 +152,11 @@ typedef struct {
  * selector's distribution over blocks): 0 selects exactly min(K, blocks) blocks; in (0, 1]
  * the forced blocks plus the fewest others, in (score desc, block asc) order, whose share of
  * pi_J = softmax over the cache's blocks of score_J brings the cumulative share to at least
- * top_p -- at most K blocks in all.  Other values: SA_ERR_PARAM. */
+ * top_p -- at most K blocks in all.  Other values: SA_ERR_PARAM.
+ * K (top_k_blocks) must hold the whole forced set at every cache length, i.e. be at least
+ * ceil(sink / block_k) + floor((local - 1) / block_k) + 2 (the sink blocks plus the most blocks
+ * a window of `local` tokens can overlap), unless it covers every block of seq_k; a smaller K
+ * is SA_ERR_PARAM (6 for block_k 64, sink 32, local 256; 10 for block_k 32). */
 typedef struct {
   int32_t block_k, top_k_blocks, sink_tokens, local_tokens, n_splits;
   float softmax_scale;

@@ -147,7 +147,17 @@ def test_validation_codes(lib):
     assert lib.sa_sparse_decode(*args, FAKE, dneed - 1, None) == _lib.SA_ERR_WORKSPACE
     dp.top_k_blocks = 0
     assert lib.sa_sparse_decode(*args, FAKE, dneed, None) == _lib.SA_ERR_PARAM
-    dp.top_k_blocks = 8
+    # K below the largest forced set (1 sink block + up to 5 window blocks at block_k 64,
+    # local 256) cannot hold it; K = 6 is the smallest accepted (the workspace query validates
+    # the same parameters and answers 0 for an invalid request)
+    dp.top_k_blocks = 5
+    assert lib.sa_sparse_decode(*args, FAKE, dneed, None) == _lib.SA_ERR_PARAM
+    assert lib.sa_workspace_size(_lib.SA_OP_DECODE, ctypes.byref(ds), ctypes.byref(dp)) == 0
+    dp.top_k_blocks = 6
+    assert lib.sa_workspace_size(_lib.SA_OP_DECODE, ctypes.byref(ds), ctypes.byref(dp)) > 0
+    dp.block_k, dp.top_k_blocks = 32, 9                      # 1 + 7 + 2 = 10 at block_k 32
+    assert lib.sa_workspace_size(_lib.SA_OP_DECODE, ctypes.byref(ds), ctypes.byref(dp)) == 0
+    dp.block_k, dp.top_k_blocks = 64, 8
     for bad in (float("nan"), -0.1, 1.5):
         dp.top_p = bad
         assert lib.sa_sparse_decode(*args, FAKE, dneed, None) == _lib.SA_ERR_PARAM
