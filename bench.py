@@ -384,6 +384,55 @@ def cpu_baseline_prefill(x, dense_flops, n_est_rows=None, n_attn_rows=512, seed=
             "attention_s_extrapolated": round(att_layer, 1)}
 
 
+def cpu_one_thread(seed=1):
+    """The oracle with its BLAS limited to one thread on the two smaller prefill
+    configurations: the 4K tiny layer in full (estimate and attention, measured) and the 32K
+    layer on 256 random estimate rows and 128 random attention query blocks (scaled by rows to
+    the layer).  Returns seconds per layer for each leg."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_limits
+    out = {"blas_threads": 1}
+    with threadpool_limits(1):
+        x = synth.make_prefill("tiny_4k")
+        kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+        t0 = time.perf_counter()
+        ref = oracle.estimate_all(x.q, x.k, x.theta, **kw)
+        t_est = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.attention_all(x.q, x.k, x.v, {k: r["kept"] for k, r in ref.items()},
+                             block_q=x.block_q, block_k=x.block_k)
+        t_att = time.perf_counter() - t0
+        out["tiny_4k"] = {"estimate_s": round(t_est, 3), "attention_s": round(t_att, 3),
+                          "kind": "measured over the whole layer"}
+        x = synth.make_prefill("llama8b_32k")
+        B, N, Hq, D = x.q.shape
+        Hkv = x.k.shape[2]
+        G = Hq // Hkv
+        nqb = -(-N // x.block_q)
+        kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+        rng = np.random.default_rng(seed)
+        all_rows = [(b, g, i) for b in range(B) for g in range(Hkv) for i in range(nqb)]
+        rows = sorted(all_rows[j] for j in rng.choice(len(all_rows), size=256, replace=False))
+        t0 = time.perf_counter()
+        ref = oracle.estimate_rows(x.q, x.k, x.theta, rows=rows, keep_margins=False, **kw)
+        t_est = time.perf_counter() - t0
+        arows = []
+        for j in rng.choice(len(rows), size=128, replace=False):
+            b, g, i = rows[j]
+            arows.append((b, g * G + int(rng.integers(0, G)), i))
+        arows.sort(key=lambda r: (r[0], r[1] // G, r[1], r[2]))
+        t0 = time.perf_counter()
+        oracle.attention_rows(x.q, x.k, x.v, {k: r["kept"] for k, r in ref.items()}, rows=arows,
+                              block_q=x.block_q, block_k=x.block_k)
+        t_att = time.perf_counter() - t0
+        out["llama8b_32k"] = {"estimate_s": round(t_est * len(all_rows) / len(rows), 2),
+                              "attention_s": round(t_att * B * Hq * nqb / len(arows), 2),
+                              "kind": "256 estimate rows and 128 attention query blocks, "
+                                      "scaled by rows to the layer"}
+    return out
+
+
 def bench_prefill(args, dev):
     import torch
     import block_sparse_attention_estimate_amd as sa
@@ -565,6 +614,8 @@ def bench_prefill(args, dev):
     if args.cpu_baseline:
         log("cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline_prefill(x, dense_flops)
+        log("oracle with one BLAS thread (tiny 4K, 32K sample)")
+        out["cpu_baseline"]["one_thread"] = cpu_one_thread()
     return out
 
 
@@ -693,7 +744,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_128k",
                     choices=list(PREFILL) + ["decode_b16_128k"])
     ap.add_argument("--seed", type=int, default=0)
