@@ -91,10 +91,11 @@ def merge_partials(o_a, lse_a, o_b, lse_b):
 
 
 def resume_rows(q, k, v, lists, state, *, block_q: int, block_k: int, sink: int, local: int,
-                rows, scale: float | None = None, kv_of_q=None) -> dict:
+                rows, scale: float | None = None, kv_of_q=None, granularity: str = "block") -> dict:
     """The sparse pass that resumes from the anchor state: attention over the tokens of the
-    block list of (b, g, i) that are causal for row r and outside A(r), merged with
-    ``state[(b, h, i)]``.  Returns {(b, h, i): (O [rows, d], LSE [rows])}."""
+    list of (b, g, i) (key blocks, or key columns with granularity "stripe") that are causal
+    for row r and outside A(r), merged with ``state[(b, h, i)]``.  Returns
+    {(b, h, i): (O [rows, d], LSE [rows])}."""
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     c = float(softmax_scale(D, scale))
@@ -105,8 +106,11 @@ def resume_rows(q, k, v, lists, state, *, block_q: int, block_k: int, sink: int,
         g = int(kv_of_q[h])
         r0, r1 = query_block_rows(i, N, block_q)
         kept = np.asarray(lists[(b, g, i)], dtype=np.int64)
-        toks = (kept[:, None] * block_k + np.arange(block_k)[None, :]).reshape(-1)
-        toks = toks[toks < N]
+        if granularity == "stripe":
+            toks = kept[kept < N]
+        else:
+            toks = (kept[:, None] * block_k + np.arange(block_k)[None, :]).reshape(-1)
+            toks = toks[toks < N]
         kf = _f64(k[b, toks, g, :])
         vf = _f64(v[b, toks, g, :])
         qb = _f64(q[b, r0:r1, h, :])

@@ -150,6 +150,35 @@ def test_resume_equals_attention_over_list(sink, local, bq):
     assert nkb > 8
 
 
+@pytest.mark.parametrize("sink,local,bq", [(32, 256, 128), (0, 100, 64), (70, 40, 128)])
+def test_resume_equals_attention_over_column_list(sink, local, bq):
+    """Column lists: the state over A(r) merged with the listed columns outside A(r) is the
+    attention over the list when the list holds the forced columns (a superset of A(r)); the
+    lists also hold columns past the block's last row, which no row may see."""
+    N, Hq, Hkv, D = 700, 4, 2, 32
+    q, k, v = _inputs(17, N, Hq, Hkv, D)
+    rng = np.random.default_rng(18)
+    nqb = -(-N // bq)
+    lists = {}
+    for g in range(Hkv):
+        for i in range(nqb):
+            cols = np.nonzero(rng.random(N) < 0.1)[0]              # any column, future ones too
+            lists[(0, g, i)] = np.union1d(cols, oracle.forced_columns(i, N, bq, sink, local))
+    rows = [(0, h, i) for h in range(Hq) for i in range(nqb)]
+    st = oracle.anchor_state_rows(q, k, v, block_q=bq, sink=sink, local=local, rows=rows)
+    res = oracle.resume_rows(q, k, v, lists, st, block_q=bq, block_k=64, sink=sink, local=local,
+                             rows=rows, granularity="stripe")
+    ref = oracle.attention_rows(q, k, v, lists, block_q=bq, block_k=64, rows=rows,
+                                granularity="stripe")
+    for key in rows:
+        np.testing.assert_allclose(res[key][0], ref[key][0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(res[key][1], ref[key][1], rtol=0, atol=1e-12)
+    # a planted mistake shows: resuming with the block reading of the same ids differs
+    bad = oracle.resume_rows(q, k, v, lists, st, block_q=bq, block_k=64, sink=sink, local=local,
+                             rows=rows[-1:])
+    assert not np.allclose(bad[rows[-1]][0], ref[rows[-1]][0], atol=1e-6)
+
+
 def test_resume_without_rest_returns_state():
     """local >= N and sink = 0: every causal listed token is in A(r), the state is final."""
     N, Hq, Hkv, D, bq, bk = 300, 2, 1, 32, 128, 64
