@@ -38,7 +38,9 @@ def anchor_region(r: int, sink: int, local: int) -> np.ndarray:
 
 def _softmax_rows(z: np.ndarray, vf: np.ndarray):
     """Per row of z (scores, -inf = excluded): O = softmax(z) v and LSE; rows with no
-    finite score give O = 0 and LSE = -inf."""
+    finite score (an empty token set included) give O = 0 and LSE = -inf."""
+    if z.shape[1] == 0:
+        return np.zeros((z.shape[0], vf.shape[1])), np.full(z.shape[0], -np.inf)
     m = z.max(axis=1, keepdims=True)
     ok = np.isfinite(m)
     ms = np.where(ok, m, 0.0)

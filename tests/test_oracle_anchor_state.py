@@ -179,6 +179,22 @@ def test_resume_equals_attention_over_column_list(sink, local, bq):
     assert not np.allclose(bad[rows[-1]][0], ref[rows[-1]][0], atol=1e-6)
 
 
+def test_resume_with_an_empty_list_returns_state():
+    """An empty list (block or column) adds no token: the resume is the state itself."""
+    N, Hq, Hkv, D, bq = 300, 2, 1, 32, 128
+    q, k, v = _inputs(19, N, Hq, Hkv, D)
+    nqb = -(-N // bq)
+    rows = [(0, h, i) for h in range(Hq) for i in range(nqb)]
+    st = oracle.anchor_state_rows(q, k, v, block_q=bq, sink=32, local=64, rows=rows)
+    empty = {(0, 0, i): np.zeros(0, np.int64) for i in range(nqb)}
+    for gran in ("block", "stripe"):
+        res = oracle.resume_rows(q, k, v, empty, st, block_q=bq, block_k=64, sink=32, local=64,
+                                 rows=rows, granularity=gran)
+        for key in rows:
+            np.testing.assert_allclose(res[key][0], st[key][0], rtol=0, atol=1e-15)
+            np.testing.assert_array_equal(res[key][1], st[key][1])
+
+
 def test_resume_without_rest_returns_state():
     """local >= N and sink = 0: every causal listed token is in A(r), the state is final."""
     N, Hq, Hkv, D, bq, bk = 300, 2, 1, 32, 128, 64
