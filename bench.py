@@ -451,8 +451,8 @@ def bench_prefill(args, dev):
     if x.granularity == "stripe":
         stride = args.stripe_capacity
     reuse = args.anchor_reuse
-    if reuse and (est != "pooled" or x.granularity != "block"):
-        raise SystemExit("--anchor-reuse needs the pooled estimator and block lists")
+    if reuse and est != "pooled":
+        raise SystemExit("--anchor-reuse needs the pooled estimator")
     lists = sa.alloc_lists(q, k, block_q=x.block_q, block_k=x.block_k,
                            granularity=x.granularity, stride=stride)
     op = sa.SA_OP_ESTIMATE_STATE if reuse else sa.SA_OP_ESTIMATE
@@ -472,8 +472,9 @@ def bench_prefill(args, dev):
         if ev is not None:
             ev[0].record(stream)
         if reuse:
-            sa.estimate_mask_anchor_state(qq, kk, vv, x.theta, step=args.step, workspace=ws,
-                                          out=lists, state=state, **kw)
+            sa.estimate_mask_anchor_state(qq, kk, vv, x.theta, granularity=x.granularity,
+                                          step=args.step, workspace=ws, out=lists, state=state,
+                                          **kw)
         else:
             sa.estimate_mask(qq, kk, x.theta, granularity=x.granularity, estimator=est,
                              step=args.step, workspace=ws, out=lists, **kw)
@@ -526,7 +527,8 @@ def bench_prefill(args, dev):
     units_desc = f"{kept_units} kept {unit_name} x {flops_per_unit / 1e6:.3f} MFLOP"
     if reuse:
         # the resuming pass visits, per 64-row work item, the listed tiles that start before
-        # the item's last row's local window and do not lie inside the sink tokens
+        # the item's last row's local window and do not lie inside the sink tokens (block
+        # lists), or the listed columns in [sink, last row - local] (column lists)
         idx = lists.idx.cpu().numpy().reshape(-1, lists.stride).astype(np.int64)
         cnt = counts.reshape(-1)
         valid = np.arange(lists.stride)[None, :] < cnt[:, None]
@@ -536,13 +538,21 @@ def bench_prefill(args, dev):
             r0 = iq * x.block_q + tsub * 64
             ok_row = r0 < N
             cut = np.minimum(r0 + 63, N - 1) - x.local + 1
-            vis = valid & (idx * 64 < cut[:, None]) & (idx * 64 + 63 >= x.sink) & ok_row[:, None]
-            visited += int(vis.sum())
-        kept_units = visited * G                                  # visited (head, 64x64 tile)
-        flops_per_unit = 4.0 * 64 * x.block_k * D
+            if x.granularity == "block":
+                vis = valid & (idx * 64 < cut[:, None]) & (idx * 64 + 63 >= x.sink)
+            else:
+                vis = valid & (idx < cut[:, None]) & (idx >= x.sink)
+            visited += int((vis & ok_row[:, None]).sum())
+        kept_units = visited * G
+        if x.granularity == "block":
+            flops_per_unit = 4.0 * 64 * x.block_k * D             # (head, 64-row, 64-key tile)
+            units_desc = (f"{kept_units} visited (head, 64x{x.block_k} tile) x "
+                          f"{flops_per_unit / 1e6:.3f} MFLOP (the anchor state covers the rest)")
+        else:
+            flops_per_unit = 4.0 * 64 * D                         # (head, 64-row item, column)
+            units_desc = (f"{kept_units} visited (head, 64-row item, column) x "
+                          f"{flops_per_unit / 1e3:.1f} KFLOP (the anchor state covers the rest)")
         kept_flops = kept_units * flops_per_unit
-        units_desc = (f"{kept_units} visited (head, 64x{x.block_k} tile) x "
-                      f"{flops_per_unit / 1e6:.3f} MFLOP (the anchor state covers the rest)")
     dense_flops = 2.0 * N * N * D * Hq * B
     att_avg, att_p10, att_p90 = pct(att_ms)
     est_avg, est_p10, est_p90 = pct(est_ms)

@@ -252,18 +252,21 @@ def sparse_prefill(q, k, v, lists: Lists, *, block_q=128, block_k=64, sink=32, l
 
 
 def estimate_mask_anchor_state(q, k, v, theta, *, block_q=128, block_k=64, sink=32, local=256,
-                               softmax_scale=0.0, margins=False, step=1, workspace=None,
+                               granularity="block", softmax_scale=0.0, stride=None,
+                               margins=False, step=1, workspace=None,
                                out: Lists | None = None, state: AnchorState | None = None,
                                kv_head_of_q=None, stream=None):
     """Estimation pass with the anchor state (sa_estimate_mask_anchor_state; pooled
-    estimator, block lists).  Returns (lists, state): the lists equal estimate_mask's, and
-    the state holds the attention over each row's anchor region for sparse_prefill_resume."""
+    estimator, block or column lists).  Returns (lists, state): the lists equal
+    estimate_mask's, and the state holds the attention over each row's anchor region for
+    sparse_prefill_resume."""
     lib = _lib.load()
     _check_bf16("v", v, 4)
     s = _prefill_shape(q, k, v, kv_head_of_q=kv_head_of_q)
-    p, keep = _sparse_params(block_q, block_k, sink, local, "block", theta, softmax_scale,
+    p, keep = _sparse_params(block_q, block_k, sink, local, granularity, theta, softmax_scale,
                              q.shape[2], "pooled", step)
     lists = out if out is not None else alloc_lists(q, k, block_q=block_q, block_k=block_k,
+                                                    granularity=granularity, stride=stride,
                                                     margins=margins)
     st = state if state is not None else alloc_anchor_state(q)
     _check_state(st, q)
@@ -283,8 +286,8 @@ def estimate_mask_anchor_state(q, k, v, theta, *, block_q=128, block_k=64, sink=
 def sparse_prefill_resume(q, k, v, lists: Lists, state: AnchorState, *, block_q=128, block_k=64,
                           sink=32, local=256, softmax_scale=0.0, out=None, lse=True,
                           kv_head_of_q=None, stream=None):
-    """Block-sparse attention that starts from the anchor state and skips each row's anchor
-    region (sa_sparse_prefill_resume).  Returns (o [B, N, Hq, d] bf16, lse [B, Hq, N] fp32 or
+    """Sparse attention (block or column lists) that starts from the anchor state and skips
+    each row's anchor region (sa_sparse_prefill_resume).  Returns (o [B, N, Hq, d] bf16, lse [B, Hq, N] fp32 or
     None)."""
     lib = _lib.load()
     _check_bf16("v", v, 4)

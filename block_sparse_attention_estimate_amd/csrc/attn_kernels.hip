@@ -19,7 +19,8 @@
 //  * work items are ordered longest-first (last query blocks first), the two 64-row halves of
 //    a 128-row query block (same list, same K/V) land on the same XCD, and the KV group
 //    rotates every 16 query blocks;
-//  * instances: block lists, column lists (gathered rows), and resuming from an anchor state.
+//  * instances: block lists, column lists (gathered rows), 32-key block lists, and resuming
+//    from an anchor state (block or column lists).
 #include <stdlib.h>
 
 #include "sa_common.h"
@@ -127,10 +128,24 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
       }
       return lo;
     };
-    const int n0 = count_le(r0);                 // entries visible to every row of the item
-    n = count_le(r_last);
-    ntile = (n + 63) / 64;
-    n_main = n0 / 64;                            // full tiles of entries <= r0
+    if constexpr (RESUME) {
+      // Resuming from the anchor state: row r needs the listed columns in [sink, r - local]
+      // (the state holds its sink and window tokens), so the item needs the entries in
+      // [sink, r_last - local], and those <= r0 - local are needed by every row (no mask).
+      const int first = a.sink > 0 ? count_le(a.sink - 1) : 0;
+      const int n_need = count_le(r_last - a.local);
+      const int n_all = count_le(r0 - a.local);
+      list += first;
+      list_g += first;
+      n = max(n_need - first, 0);
+      ntile = (n + 63) / 64;
+      n_main = max(n_all - first, 0) / 64;
+    } else {
+      const int n0 = count_le(r0);               // entries visible to every row of the item
+      n = count_le(r_last);
+      ntile = (n + 63) / 64;
+      n_main = n0 / 64;                          // full tiles of entries <= r0
+    }
   } else if (BK32) {
     // 32-key block lists: two listed blocks per tile; blocks from `r_last + 1` on hold no key
     // of this work item; the tiles from n_main on need a mask (a block past the first row's
@@ -433,7 +448,9 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int tok = __shfl(mine, mt * 32 + half * 4 + 8 * (r >> 2) + (r & 3));
-          if (tok > row || tok >= a.N) sacc[mt][r] = NEG_INF;
+          const bool drop = RESUME ? (tok < a.sink || tok >= row - a.local + 1 || tok >= a.N)
+                                   : (tok > row || tok >= a.N);
+          if (drop) sacc[mt][r] = NEG_INF;
         }
       return;
     }
@@ -485,7 +502,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
     DMA_BARRIER(SLOTS);
     f32x16 sa[2], sbb[2];
     qk(st0, sa);
-    if (n_main == 0 || (RESUME && j0.v[0] * 64 < a.sink)) mask(0, j0, sa);
+    if (n_main == 0 || (RESUME && !STRIPE && j0.v[0] * 64 < a.sink)) mask(0, j0, sa);
     auto step = [&](unsigned char* sc, unsigned char* sn, unsigned char* sd, int t,
                     f32x16* cur, f32x16* nxt, bool may_mask) {
       issue(sd, jc);
@@ -572,7 +589,9 @@ static hipError_t launch_block(const AttnArgs& a0, hipStream_t s) {
   a.n_hp = a.G / HPW;
   a.total = a.B * a.Hkv * a.n_hp * a.nQB * a.tpb;
   if (a.total == 0) return hipSuccess;
-  if (a.st_o)
+  if (a.st_o && a.stripe)
+    hipLaunchKernelGGL((attn_block<D, HPW, true, 1>), dim3(a.total), dim3(128 * HPW), 0, s, a);
+  else if (a.st_o)
     hipLaunchKernelGGL((attn_block<D, HPW, true, 0>), dim3(a.total), dim3(128 * HPW), 0, s, a);
   else if (a.stripe)
     hipLaunchKernelGGL((attn_block<D, HPW, false, 1>), dim3(a.total), dim3(128 * HPW), 0, s, a);

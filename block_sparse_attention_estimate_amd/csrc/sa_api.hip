@@ -234,8 +234,7 @@ size_t sa_workspace_size(int op, const sa_shape* shape, const void* params) {
   if (op == SA_OP_ESTIMATE || op == SA_OP_ESTIMATE_STATE) {
     const sa_sparse_params* p = (const sa_sparse_params*)params;
     if (check_prefill_shape(shape) != SA_OK || check_sparse_params(shape, p, true) != SA_OK) return 0;
-    if (op == SA_OP_ESTIMATE_STATE &&
-        (p->estimator != SA_EST_POOLED || p->granularity != SA_BLOCK || p->block_k != 64))
+    if (op == SA_OP_ESTIMATE_STATE && (p->estimator != SA_EST_POOLED || p->block_k != 64))
       return 0;
     return est_layout(shape, p, op == SA_OP_ESTIMATE_STATE).total;
   }
@@ -269,9 +268,7 @@ static sa_status estimate_impl(const sa_shape* shape, const sa_sparse_params* pa
   if (!aligned16(q) || !aligned16(k)) return SA_ERR_SHAPE;
   const bool with_state = state != nullptr;
   if (with_state) {
-    if (params->estimator != SA_EST_POOLED || params->granularity != SA_BLOCK ||
-        params->block_k != 64)
-      return SA_ERR_UNSUPPORTED;
+    if (params->estimator != SA_EST_POOLED || params->block_k != 64) return SA_ERR_UNSUPPORTED;
     if (!v || !state->o || !state->lse) return SA_ERR_NULL;
     if (!aligned16(v) || !aligned16(state->o) || ((uintptr_t)state->lse & 3u) != 0) return SA_ERR_SHAPE;
   }
@@ -339,7 +336,7 @@ static sa_status prefill_impl(const sa_shape* shape, const sa_sparse_params* par
   if (!q || !k || !v || !o || !lists || !lists->counts || !lists->idx) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SA_ERR_SHAPE;
   if (state) {
-    if (params->granularity != SA_BLOCK || params->block_k != 64) return SA_ERR_UNSUPPORTED;
+    if (params->block_k != 64) return SA_ERR_UNSUPPORTED;
     if (!state->o || !state->lse) return SA_ERR_NULL;
     if (!aligned16(state->o) || ((uintptr_t)state->lse & 3u) != 0) return SA_ERR_SHAPE;
   }

@@ -211,8 +211,8 @@ typedef struct {
   float* lse;
 } sa_anchor_state;
 
-/* sa_estimate_mask (pooled estimator, block granularity only; SA_ERR_UNSUPPORTED otherwise)
- * preceded by the anchor-state pass: one bf16 MFMA online softmax over each row's anchor
+/* sa_estimate_mask (pooled estimator, block_k 64, block or column lists; SA_ERR_UNSUPPORTED
+ * otherwise) preceded by the anchor-state pass: one bf16 MFMA online softmax over each row's anchor
  * region writes `state` and hands the per-row anchors x_a (the same MFMA sequence, so the
  * same values and the same lists as sa_estimate_mask) to the estimate.  v: device bf16
  * [B, seq, Hkv, d] (v_stride).  ws: at least sa_workspace_size(SA_OP_ESTIMATE_STATE, ...)
@@ -222,14 +222,14 @@ sa_status sa_estimate_mask_anchor_state(const sa_shape* shape, const sa_sparse_p
                                         const sa_lists* out, const sa_anchor_state* state,
                                         void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* sa_sparse_prefill resuming from an anchor state (block granularity only): row r starts
- * from state (o, lse) and adds the listed tokens j <= r outside A(r) (sink_tokens and
+/* sa_sparse_prefill resuming from an anchor state (block_k 64; block or column lists): row r
+ * starts from state (o, lse) and adds the listed tokens j <= r outside A(r) (sink_tokens and
  * local_tokens of params define A(r); they and softmax_scale must be the ones the state was
- * made with); tiles of the list that lie wholly inside every row's anchor region are
- * skipped.  The result is the
- * attention over A(r) and the listed causal tokens, which for lists of the estimate (they
- * hold the forced blocks, a superset of A(r)) is sa_sparse_prefill's result.  o, lse as in
- * sa_sparse_prefill; the state is read only. */
+ * made with); block tiles that lie wholly inside every row's anchor region, and listed
+ * columns inside it, are skipped.  The result is the attention over A(r) and the listed
+ * causal tokens, which for lists of the estimate (they hold the forced blocks or columns, a
+ * superset of A(r)) is sa_sparse_prefill's result.  o, lse as in sa_sparse_prefill; the
+ * state is read only. */
 sa_status sa_sparse_prefill_resume(const sa_shape* shape, const sa_sparse_params* params,
                                    const void* q, const void* k, const void* v,
                                    const sa_lists* lists, const sa_anchor_state* state, void* o,

@@ -245,16 +245,19 @@ def test_anchor_state_validation(lib):
     pr.estimator = _lib.SA_EST_RELATIVE
     assert est(pp=pr) == _lib.SA_ERR_UNSUPPORTED
     assert lib.sa_workspace_size(_lib.SA_OP_ESTIMATE_STATE, ctypes.byref(s), ctypes.byref(pr)) == 0
+    # column lists take the anchor state too (validation reaches the workspace check)
     pst, keep3 = _params(4.0, gran=_lib.SA_STRIPE)
-    assert est(pp=pst) == _lib.SA_ERR_UNSUPPORTED
+    need_sst = lib.sa_workspace_size(_lib.SA_OP_ESTIMATE_STATE, ctypes.byref(s), ctypes.byref(pst))
+    assert need_sst > lib.sa_workspace_size(_lib.SA_OP_ESTIMATE, ctypes.byref(s), ctypes.byref(pst))
+    assert est(pp=pst, ws_bytes=need_sst - 1) == _lib.SA_ERR_WORKSPACE
     # resume validation
     def resume(state=ctypes.byref(st), pp=p):
         return lib.sa_sparse_prefill_resume(ctypes.byref(s), ctypes.byref(pp), FAKE, FAKE, FAKE,
                                             ctypes.byref(ls), state, FAKE, None, None)
     assert resume(state=None) == _lib.SA_ERR_NULL
-    assert resume(pp=pst) == _lib.SA_ERR_UNSUPPORTED
     st.o = FAKE + 8
     assert resume() == _lib.SA_ERR_SHAPE
+    assert resume(pp=pst) == _lib.SA_ERR_SHAPE           # column lists accepted, then the check
     st.o = FAKE
     ls.stride = 3
     assert resume() == _lib.SA_ERR_CAPACITY

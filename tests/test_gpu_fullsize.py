@@ -44,7 +44,8 @@ def _gpu_run(dev, name, estimator, reuse, theta, seed):
     stride = 8192 if x.granularity == "stripe" else None
     st = None
     if reuse:
-        lists, st = sa.estimate_mask_anchor_state(q, k, v, x.theta, **kw)
+        lists, st = sa.estimate_mask_anchor_state(q, k, v, x.theta, granularity=x.granularity,
+                                                  stride=stride, **kw)
         o, lse = sa.sparse_prefill_resume(q, k, v, lists, st, **kw)
     else:
         lists = sa.estimate_mask(q, k, x.theta, granularity=x.granularity, stride=stride,
@@ -166,9 +167,10 @@ def test_llama8b_32k_relative_mxfp4_sampled(dev):
                     theta=4.83)
 
 
-@pytest.mark.parametrize("name", ["llama8b_32k", "llama8b_128k"])
+@pytest.mark.parametrize("name", ["llama8b_32k", "llama8b_128k", "stripe_64k"])
 def test_anchor_reuse_sampled(dev, name):
-    """Anchor-state reuse in the launch configuration bench.py --anchor-reuse times."""
+    """Anchor-state reuse in the launch configuration bench.py --anchor-reuse times (block
+    lists at 32K and 128K, column lists at 64K)."""
     _prefill_parity(dev, name, n_rows=24, n_attn=10, reuse=True)
 
 
