@@ -45,13 +45,14 @@ def head_l1_error(o_ref: np.ndarray, o: np.ndarray) -> np.ndarray:
 
 def calibrate_theta(q, k, v, *, tau0: float = 0.008, err_bound: float = 0.4,
                     max_halvings: int = 16, block_q: int, block_k: int, sink: int, local: int,
-                    scale=None, estimator: str = "pooled") -> dict:
+                    scale=None, estimator: str = "pooled", kv_of_q=None) -> dict:
     """Returns dict(theta [Hq] float32, err [Hq] float64, halvings [Hq] int, history: list of
     (theta, err) per round).  estimator "relative" calibrates SALE's own element-wise
-    estimate (``estimate_sale``) instead of the pooled one."""
+    estimate (``estimate_sale``) instead of the pooled one.  kv_of_q: the KV head of each
+    query head (default h // (Hq / Hkv)), passed to the estimate and the attention."""
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
-    kw = dict(block_q=block_q, block_k=block_k)
+    kw = dict(block_q=block_q, block_k=block_k, kv_of_q=kv_of_q)
     o_ref, _ = attention_all(q, k, v, full_lists(N, B, Hkv, block_q, block_k), scale=scale, **kw)
     theta0 = -math.log(tau0)
     halv = np.zeros(Hq, dtype=np.int64)

@@ -95,3 +95,24 @@ def test_zero_bound_stops_at_full_lists():
     # the thetas are -ln(tau0) + k ln 2, rounded once to fp32
     want = np.array([-math.log(1e-16) + kh * math.log(2.0) for kh in r["halvings"]], dtype=np.float32)
     np.testing.assert_array_equal(r["theta"], want)
+
+
+def test_head_map_permutes_the_calibration():
+    """Reordering the query heads of Q, with the head map reordered alike, reorders the
+    calibrated thetas, halvings and errors alike (the map reaches the estimate and the
+    attention of every round); a map that ignored the reordering would pair heads with the
+    wrong KV head and change them."""
+    q, k, v = _inputs(seed=5, N=1536, Hq=8, Hkv=2, D=32)
+    # a short window and a large tau0 so the estimate drops blocks and the heads' errors differ
+    kw = dict(block_q=64, block_k=64, sink=16, local=64, tau0=0.5, err_bound=2e-4,
+              max_halvings=3)
+    base = oracle.calibrate_theta(q, k, v, **kw)
+    perm = np.array([5, 0, 7, 2, 1, 6, 3, 4])
+    kv_of_q = perm // 4                            # the KV head of the reordered head j
+    got = oracle.calibrate_theta(q[:, :, perm, :], k, v, kv_of_q=kv_of_q, **kw)
+    np.testing.assert_array_equal(got["halvings"], base["halvings"][perm])
+    np.testing.assert_array_equal(got["theta"], base["theta"][perm])
+    np.testing.assert_allclose(got["err"], base["err"][perm], rtol=0, atol=1e-12)
+    assert len(set(base["halvings"].tolist())) > 1    # the heads differ, so the order shows
+    wrong = oracle.calibrate_theta(q[:, :, perm, :], k, v, **kw)   # default map, wrong pairing
+    assert not np.allclose(wrong["err"], base["err"][perm], atol=1e-6)
