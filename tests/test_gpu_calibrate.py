@@ -75,3 +75,32 @@ def test_calibrate_against_oracle(dev, estimator, bound):
         else:
             assert abs(err[h] - ref["err"][h]) < BAND, (h, err[h], ref["err"][h])
         np.testing.assert_equal(th[h], np.float32(-math.log(0.008) + kg * math.log(2.0)))
+
+
+def test_calibrate_with_head_map(dev):
+    """A GQA head map that is not h // G (two groups of four, interleaved): the calibrated
+    halvings per query head agree with the oracle's under the same map (up to near-ties at
+    the bound), and differ from the calibration under the default map."""
+    import block_sparse_attention_estimate_amd as sa
+    kv_of_q = np.array([1, 0, 0, 1, 1, 0, 1, 0], np.int32)
+    x, q, k, v = _data(dev)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    bound = 0.05
+    th, err, hv = sa.calibrate_theta(q, k, v, tau0=0.008, err_bound=bound, max_halvings=24,
+                                     kv_head_of_q=kv_of_q, **kw)
+    ref = oracle.calibrate_theta(x.q, x.k, x.v, tau0=0.008, err_bound=bound, max_halvings=24,
+                                 kv_of_q=kv_of_q, **kw)
+    log(f"head map: gpu halvings {hv.tolist()} oracle {ref['halvings'].tolist()}")
+    hist = np.array([e for _, e in ref["history"]])
+    for h in range(q.shape[2]):
+        kg, ko = int(hv[h]), int(ref["halvings"][h])
+        if kg != ko:
+            r = min(kg, ko)
+            assert r < hist.shape[0] and abs(hist[r, h] - bound) < BAND, (h, kg, ko, hist[:, h])
+        else:
+            assert abs(err[h] - ref["err"][h]) < BAND, (h, err[h], ref["err"][h])
+    # the map is in effect: the default map pairs the heads with other KV heads
+    _, err0, _ = sa.calibrate_theta(q, k, v, tau0=0.008, err_bound=bound, max_halvings=0, **kw)
+    _, errm, _ = sa.calibrate_theta(q, k, v, tau0=0.008, err_bound=bound, max_halvings=0,
+                                    kv_head_of_q=kv_of_q, **kw)
+    assert not np.allclose(err0, errm, atol=1e-6)
