@@ -14,6 +14,7 @@
 //  * O^T += V^T P^T: P^T is the S^T accumulator converted to bf16 in place (no LDS round
 //    trip), V^T is read with transposing LDS reads;
 //  * software pipeline: S(t+1) is computed while tile t's exponentials run;
+//  * O is written through LDS, so every store instruction writes whole rows;
 //  * the running max moves only when a tile's probabilities would exceed 2^16, so O is rarely
 //    rescaled;
 //  * work items are ordered longest-first (last query blocks first), the two 64-row halves of
@@ -563,8 +564,15 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
 
   const float lt = half_pair_sum(l_run);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (row < a.N) {
-    uint16_t* op = a.o + b * a.os0 + (int64_t)row * a.os1 + h * a.os2 + half * 4;
+  // O leaves through LDS: each wave writes its 32 x D tile (bf16) into a region of the stages
+  // of its own, then stores whole rows, 16 bytes per lane, so that a store instruction writes
+  // complete rows instead of 16 bytes of each of 32 rows.
+  constexpr int OPITCH = ROWB + 16;
+  static_assert(2 * 32 * OPITCH <= STAGE, "two waves' output tiles must fit in a stage");
+  __syncthreads();                   // no wave still reads a stage and no load still fills one
+  {
+    const int sel = wave >> 1;
+    unsigned char* ob = (sel == 0 ? st0 : sel == 1 ? st1 : sel == 2 ? st2 : st3) + (wave & 1) * 32 * OPITCH;
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
@@ -573,12 +581,22 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
                                 ((unsigned int)float_to_bf16_bits(oacc[dm][4 * q4 + 1] * inv) << 16);
         const unsigned int hi = float_to_bf16_bits(oacc[dm][4 * q4 + 2] * inv) |
                                 ((unsigned int)float_to_bf16_bits(oacc[dm][4 * q4 + 3] * inv) << 16);
-        *(u32x2*)(op + dm * 32 + 8 * q4) = (u32x2){lo, hi};
+        *(u32x2*)(ob + l32 * OPITCH + (dm * 32 + 8 * q4 + half * 4) * 2) = (u32x2){lo, hi};
       }
-    if (a.lse && half == 0)
-      a.lse[((int64_t)b * a.Hq + h) * a.N + row] =
-          lt > 0.f ? (m_run + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
+    constexpr int CPR = ROWB / 16;   // 16-byte chunks of a row
+    constexpr int RPI = 64 / CPR;    // rows per store instruction
+    const int c = lane % CPR, rr = lane / CPR;
+    uint16_t* obase = a.o + b * a.os0 + h * a.os2 + c * 8;
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int lr = rr + k * RPI;
+      const u32x4 v = *(const u32x4*)(ob + lr * OPITCH + c * 16);
+      if (rw + lr < a.N) *(u32x4*)(obase + (int64_t)(rw + lr) * a.os1) = v;
+    }
   }
+  if (a.lse && half == 0 && row < a.N)
+    a.lse[((int64_t)b * a.Hq + h) * a.N + row] =
+        lt > 0.f ? (m_run + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
