@@ -10,9 +10,12 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libsa_debug.so")
 
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_PARAM, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY, \
-    SA_ERR_WORKSPACE, SA_ERR_DEVICE = range(8)
+    SA_ERR_WORKSPACE, SA_ERR_DEVICE, SA_ERR_CHECK = range(9)
+# bits of sa_debug_flags() (debug build)
+SA_DBG_COUNT, SA_DBG_RANGE, SA_DBG_ORDER, SA_DBG_CACHE_LEN = 1, 2, 4, 8
 SA_BLOCK, SA_STRIPE = 0, 1
 SA_EST_POOLED, SA_EST_RELATIVE, SA_EST_RELATIVE_MXFP4 = 0, 1, 2
 SA_OP_ESTIMATE, SA_OP_PREFILL, SA_OP_DECODE, SA_OP_CALIBRATE, SA_OP_ESTIMATE_STATE = 0, 1, 2, 3, 4
@@ -22,7 +25,8 @@ EXPORTED = ("sa_workspace_size", "sa_estimate_mask", "sa_sparse_prefill",
             "sa_build_block_summary", "sa_sparse_decode", "sa_quantize_block_summary",
             "sa_sparse_decode_q4", "sa_calibrate_theta", "sa_status_string",
             "sa_estimate_mask_anchor_state", "sa_sparse_prefill_resume",
-            "sa_quantize_block_summary_fp4", "sa_sparse_decode_fp4", "sa_sparse_decode_noalloc")
+            "sa_quantize_block_summary_fp4", "sa_sparse_decode_fp4", "sa_sparse_decode_noalloc",
+            "sa_debug_flags")
 SA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
@@ -68,9 +72,15 @@ def load(path: str | None = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    path = path or os.environ.get("SA_LIB_PATH") or LIB_PATH
+    _lib = open_library(path or os.environ.get("SA_LIB_PATH") or LIB_PATH)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A build of the library at `path` (libsa.so or libsa_debug.so) with its prototypes set;
+    not cached."""
     if not os.path.exists(path):
-        raise RuntimeError(f"libsa.so not found at {path}: build it with "
+        raise RuntimeError(f"{os.path.basename(path)} not found at {path}: build it with "
                            f"__graft_entry__.build() (hipcc --offload-arch=gfx950)")
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
@@ -114,7 +124,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                        P(ctypes.c_float), P(ctypes.c_int32), vp, ctypes.c_size_t, vp]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_status_string.argtypes = [ctypes.c_int]
-    _lib = lib
+    lib.sa_debug_flags.restype = ctypes.c_uint32
+    lib.sa_debug_flags.argtypes = []
     return lib
 
 

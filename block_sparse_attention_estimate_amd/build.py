@@ -28,17 +28,30 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
-    with ThreadPoolExecutor(len(cmds)) as pool:
+# the debug build: the same sources with the kernels' checks of caller data compiled in
+DEBUG_LIB = os.path.join(PKG, "libsa_debug.so")
+OBJ_DEBUG = os.path.join(OBJ, "debug")
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Compile libsa.so (and, with debug, libsa_debug.so) in-tree; every source compiles in
+    parallel."""
+    variants = [(LIB, OBJ, [])] + ([(DEBUG_LIB, OBJ_DEBUG, ["-DSA_DEBUG"])] if debug else [])
+    cmds, links = [], []
+    for lib, obj_dir, extra in variants:
+        os.makedirs(obj_dir, exist_ok=True)
+        objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds += [[HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", o]
+                 for s, o in zip(SOURCES, objs)]
+        links.append((lib, objs))
+    with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 8)) as pool:
         list(pool.map(_run, cmds))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+    for lib, objs in links:
+        tmp = lib + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+        os.replace(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 

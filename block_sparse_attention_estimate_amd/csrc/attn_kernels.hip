@@ -108,6 +108,19 @@ __global__ __launch_bounds__(128 * HPW) void attn_block(AttnArgs a) {
   int n = min(((const __attribute__((address_space(4))) int32_t*)a.counts)[lrow], a.stride);
   // the same list through a plain pointer, for per-lane reads of gathered column ids
   const int32_t* list_g = a.idx + lrow * a.stride;
+#ifdef SA_DEBUG
+  if (wave == 0 && tsub == 0) {
+    // caller-built lists: a count in [0, stride], entries inside the sequence, ascending
+    const int cnt = ((const __attribute__((address_space(4))) int32_t*)a.counts)[lrow];
+    SA_DCHECK(a.dbg, cnt >= 0 && cnt <= a.stride, SA_DBG_COUNT);
+    const int lim = STRIPE ? a.N : BK32 ? (a.N + 31) >> 5 : (a.N + 63) >> 6;
+    for (int e = lane; e < n; e += 64) {
+      const int v = list_g[e];
+      SA_DCHECK(a.dbg, v >= 0 && v < lim, SA_DBG_RANGE);
+      if (e > 0) SA_DCHECK(a.dbg, list_g[e - 1] < v, SA_DBG_ORDER);
+    }
+  }
+#endif
   int ntile, n_main;
   if (STRIPE) {
     // column lists: the entries this work item can see (<= r_last, ascending); tiles of 64

@@ -43,6 +43,8 @@ template <int D>
 __global__ __launch_bounds__(256) void dec_block_summary(DecArgs a) {
   const int J = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lb = min(max(a.cache_len[b], 0), a.L);
+  if (J == 0 && tid == 0)
+    SA_DCHECK(a.dbg, a.cache_len[b] >= 0 && a.cache_len[b] <= a.L, SA_DBG_CACHE_LEN);
   const int t0 = J * a.bk, t1 = min(lb, t0 + a.bk);
   for (int base = 0; base < a.Hkv * D; base += 1024) {
     const int idx = base + tid * 4;
@@ -466,6 +468,8 @@ __global__ __launch_bounds__(256) void dec_select_radix(DecArgs a) {
   __shared__ float s_max[4];
   __shared__ int s_nf;
   const int lb = min(max(a.cache_len[b], 0), a.L);
+  if (g == 0 && tid == 0)
+    SA_DCHECK(a.dbg, a.cache_len[b] >= 0 && a.cache_len[b] <= a.L, SA_DBG_CACHE_LEN);
   const int nb = (lb + a.bk - 1) / a.bk;
   const float* sc = a.scores + ((int64_t)b * a.Hkv + g) * a.nKB;
   // Thread t owns blocks t, t + 256, ... in every loop over the blocks below.  Its scores are

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "sa_internal.h"
@@ -14,6 +15,54 @@
 static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
+
+// Debug builds: one check word per device (SA_DBG_* bits set by the kernels' checks),
+// allocated and cleared on the first checked call with that device.  A checked entry point
+// waits for its stream, reads the word and clears it; the bits of the last failing call stay
+// readable through sa_debug_flags().  Release builds pass no word and never synchronise.
+std::atomic<unsigned int> g_dbg_last{0};
+#ifdef SA_DEBUG
+constexpr int kMaxDbgDevices = 64;
+std::mutex g_dbg_mutex;
+unsigned int* g_dbg_word[kMaxDbgDevices] = {};
+#endif
+
+unsigned int* debug_word() {
+#ifdef SA_DEBUG
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDbgDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_dbg_mutex);
+  if (!g_dbg_word[dev]) {
+    void* p = nullptr;
+    if (hipMalloc(&p, sizeof(unsigned int)) != hipSuccess) return nullptr;
+    if (hipMemset(p, 0, sizeof(unsigned int)) != hipSuccess) return nullptr;
+    g_dbg_word[dev] = (unsigned int*)p;
+  }
+  return g_dbg_word[dev];
+#else
+  return nullptr;
+#endif
+}
+
+// The status of a checked call: st itself unless this is a debug build whose kernels set a
+// check bit (then SA_ERR_CHECK, the bits kept for sa_debug_flags()).
+sa_status debug_finish(sa_status st, unsigned int* word, hipStream_t stream) {
+#ifdef SA_DEBUG
+  if (st != SA_OK) return st;
+  if (!word) return SA_ERR_DEVICE;
+  unsigned int bits = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SA_ERR_DEVICE;
+  if (hipMemcpy(&bits, word, sizeof(bits), hipMemcpyDeviceToHost) != hipSuccess) return SA_ERR_DEVICE;
+  if (bits == 0) return SA_OK;
+  if (hipMemset(word, 0, sizeof(unsigned int)) != hipSuccess) return SA_ERR_DEVICE;
+  g_dbg_last.store(bits);
+  return SA_ERR_CHECK;
+#else
+  (void)word;
+  (void)stream;
+  return st;
+#endif
+}
 
 constexpr size_t kAlign = 256;
 
@@ -215,6 +264,8 @@ sa_status check_decode(const sa_shape* s, const sa_decode_params* p) {
 
 extern "C" {
 
+uint32_t sa_debug_flags(void) { return g_dbg_last.load(); }
+
 const char* sa_status_string(sa_status st) {
   switch (st) {
     case SA_OK: return "ok";
@@ -225,6 +276,7 @@ const char* sa_status_string(sa_status st) {
     case SA_ERR_CAPACITY: return "list capacity too small";
     case SA_ERR_WORKSPACE: return "workspace missing or too small";
     case SA_ERR_DEVICE: return "device error";
+    case SA_ERR_CHECK: return "invalid caller data found by a debug-build kernel check";
   }
   return "unknown status";
 }
@@ -367,9 +419,10 @@ static sa_status prefill_impl(const sa_shape* shape, const sa_sparse_params* par
     a.sink = params->sink_tokens;
     a.local = params->local_tokens;
   }
+  a.dbg = debug_word();
   if (launch_prefill(a, shape->head_dim, params->granularity, stream) != hipSuccess)
     return SA_ERR_DEVICE;
-  return SA_OK;
+  return debug_finish(SA_OK, a.dbg, stream);
 }
 
 extern "C" {
@@ -427,8 +480,9 @@ sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k, const v
   a.kc = (const uint16_t*)k_cache;
   a.cache_len = cache_len;
   a.ksum = (const uint16_t*)k_summary;
+  a.dbg = debug_word();
   if (launch_block_summary(a, stream) != hipSuccess) return SA_ERR_DEVICE;
-  return SA_OK;
+  return debug_finish(SA_OK, a.dbg, stream);
 }
 
 // shared by the bf16-, 4-bit- and FP4-summary decode entries (exactly one summary form given:
@@ -473,8 +527,9 @@ static sa_status decode_impl(const sa_shape* shape, const sa_decode_params* para
   a.local = params->local_tokens;
   a.n_splits = decode_splits(shape, params);
   a.c = resolve_scale(params->softmax_scale, shape->head_dim);
+  a.dbg = debug_word();
   if (launch_decode(a, stream) != hipSuccess) return SA_ERR_DEVICE;
-  return SA_OK;
+  return debug_finish(SA_OK, a.dbg, stream);
 }
 
 namespace {

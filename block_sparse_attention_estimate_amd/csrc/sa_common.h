@@ -30,6 +30,24 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 #define SA_DEV static __device__ __forceinline__
 
+// Debug builds (-DSA_DEBUG, libsa_debug.so): kernels check the caller data that the release
+// kernels clamp -- list counts and entries, cache lengths -- and set bits of a device word
+// that the host reads after the call.  The release build compiles no check.
+#define SA_DBG_COUNT 1u       // a list count outside [0, stride]
+#define SA_DBG_RANGE 2u       // a list entry outside the sequence's key blocks (or columns)
+#define SA_DBG_ORDER 4u       // list entries not strictly ascending
+#define SA_DBG_CACHE_LEN 8u   // a cache length outside [0, seq_k]
+#ifdef SA_DEBUG
+#define SA_DCHECK(word, cond, bit)       \
+  do {                                   \
+    if (!(cond)) atomicOr((word), (bit)); \
+  } while (0)
+#else
+#define SA_DCHECK(word, cond, bit) \
+  do {                             \
+  } while (0)
+#endif
+
 // 32x32x16 bf16 MFMA: A lane l holds A[l%32][(l/32)*8 .. +8]; B lane l holds
 // B[(l/32)*8 .. +8][l%32]; C lane l holds C[(l/32)*4 + 8*(r/4) + r%4][l%32], r = 0..15.
 SA_DEV f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {

@@ -66,6 +66,7 @@ struct AttnArgs {
   int sink, local;
   int stripe;              // 1: the lists name key columns (gathered rows), 0: key blocks
   int bk32;                // 1: block lists of 32-key blocks (two per 64-key tile)
+  unsigned int* dbg;       // debug builds: the check word (SA_DBG_* bits); unused otherwise
   uint8_t qh[SA_MAX_Q_HEADS];  // query head of packed head g * G + j
 };
 
@@ -89,6 +90,7 @@ struct DecArgs {
   int B, Hq, Hkv, G, D, L, bk, nKB, top_k, sink, local, n_splits;
   float c;
   float top_p;             // 0: fixed K; (0, 1]: top-p budget capped at K
+  unsigned int* dbg;       // debug builds: the check word (SA_DBG_* bits); unused otherwise
   uint8_t qh[SA_MAX_Q_HEADS];  // query head of packed head g * G + j
 };
 

@@ -58,7 +58,8 @@ typedef enum {
   SA_ERR_UNSUPPORTED = 4,  /* valid but not implemented (head_dim, block sizes, group size)*/
   SA_ERR_CAPACITY = 5,     /* list stride too small for a block list                       */
   SA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than sa_workspace_size()           */
-  SA_ERR_DEVICE = 7        /* a HIP call or kernel launch failed                           */
+  SA_ERR_DEVICE = 7,       /* a HIP call or kernel launch failed                           */
+  SA_ERR_CHECK = 8         /* debug build only: a kernel found invalid caller data         */
 } sa_status;
 
 enum { SA_BLOCK = 0, SA_STRIPE = 1 };
@@ -353,6 +354,18 @@ sa_status sa_calibrate_theta(const sa_shape* shape, const sa_sparse_params* para
 
 /* Static description of a status code. */
 const char* sa_status_string(sa_status status);
+
+/* Debug build (libsa_debug.so, the same sources compiled with -DSA_DEBUG), for callers that
+ * build their own lists or cache lengths.  The kernels then check the data that the release
+ * kernels clamp -- each list's count in [0, stride], its entries inside the sequence's key
+ * blocks (columns for stripe lists) and strictly ascending, each cache length in [0, seq_k] --
+ * and sa_sparse_prefill(_resume), sa_sparse_decode(_q4, _fp4, _noalloc) and
+ * sa_build_block_summary wait for their stream after the launches and return SA_ERR_CHECK when
+ * a check failed (results are then those of the clamped data).  Bits of the last such call:
+ * 1 a count outside [0, stride], 2 an entry out of range, 4 entries not strictly ascending,
+ * 8 a cache length outside [0, seq_k].  The debug build allocates one 4-byte word per device on
+ * its first checked call; the release build checks nothing, never waits and returns 0 here. */
+uint32_t sa_debug_flags(void);
 
 #ifdef __cplusplus
 }

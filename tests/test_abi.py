@@ -38,9 +38,22 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in range(8):
-        assert lib.sa_status_string(st)
+    for st in range(9):
+        assert lib.sa_status_string(st) != b"unknown status"
     assert lib.sa_status_string(0) == b"ok"
+    assert lib.sa_status_string(9) == b"unknown status"
+
+
+def test_debug_build_exports_the_same_symbols(lib):
+    """libsa_debug.so (the kernels' checks of caller data compiled in) is built beside libsa.so
+    and exports every declared entry point; the release build reports no check bits."""
+    if not os.path.exists(_lib.DEBUG_LIB_PATH):
+        pytest.fail("libsa_debug.so is not built (run __graft_entry__.build())")
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.DEBUG_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(sa_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert lib.sa_debug_flags() == 0
 
 
 def _shape(B=1, Hq=4, Hkv=1, D=128, N=256):
