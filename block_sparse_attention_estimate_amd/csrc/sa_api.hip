@@ -1,6 +1,8 @@
 // C ABI of libsa: host-side validation, workspace carve-out and kernel launches.
 // Every check runs before the first launch; on error nothing is launched.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -21,6 +23,38 @@ namespace {
 // waits for its stream, reads the word and clears it; the bits of the last failing call stay
 // readable through sa_debug_flags().  Release builds pass no word and never synchronise.
 std::atomic<unsigned int> g_dbg_last{0};
+
+// SA_LOG set (and not "0") in the environment: every launching entry point prints one line to
+// stderr, after its checks and before its launches, with the configuration it launches for.
+bool log_on() {
+  const char* e = getenv("SA_LOG");
+  return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
+
+void log_prefill(const char* name, const sa_shape* s, const sa_sparse_params* p, int tpb,
+                 const void* stream) {
+  if (!log_on()) return;
+  static const char* const est[] = {"pooled", "relative", "relative_mxfp4"};
+  const int e = p->estimator >= 0 && p->estimator <= 2 ? p->estimator : 0;
+  fprintf(stderr,
+          "[sa] %s: B=%d Hq=%d Hkv=%d d=%d N=%d head_map=%s block_q=%d block_k=%d sink=%d "
+          "local=%d granularity=%s estimator=%s step=%d row_tiles_per_block=%d stream=%p\n",
+          name, s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->seq_q,
+          s->kv_head_of_q ? "given" : "h/G", p->block_q, p->block_k, p->sink_tokens,
+          p->local_tokens, p->granularity == SA_STRIPE ? "stripe" : "block", est[e], p->step, tpb,
+          stream);
+}
+
+void log_decode(const char* name, const sa_shape* s, int block_k, const sa_decode_params* p,
+                int n_splits, const char* summary, const void* stream) {
+  if (!log_on()) return;
+  fprintf(stderr,
+          "[sa] %s: B=%d Hq=%d Hkv=%d d=%d L=%d block_k=%d top_k=%d top_p=%g sink=%d local=%d "
+          "splits=%d summary=%s stream=%p\n",
+          name, s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->seq_k,
+          block_k, p ? p->top_k_blocks : 0, p ? (double)p->top_p : 0.0,
+          p ? p->sink_tokens : 0, p ? p->local_tokens : 0, n_splits, summary, stream);
+}
 #ifdef SA_DEBUG
 constexpr int kMaxDbgDevices = 64;
 std::mutex g_dbg_mutex;
@@ -371,7 +405,10 @@ static sa_status estimate_impl(const sa_shape* shape, const sa_sparse_params* pa
     a.st_lse = state->lse;
     a.xa = (float*)(base + L.xa);
     a.xa_ready = 1;
+    log_prefill("sa_estimate_mask_anchor_state", shape, params, params->block_q / 64, stream);
     if (launch_anchor_state(a, stream) != hipSuccess) return SA_ERR_DEVICE;
+  } else {
+    log_prefill("sa_estimate_mask", shape, params, params->block_q / 64, stream);
   }
   if (launch_estimate(a, params->granularity, stream) != hipSuccess) return SA_ERR_DEVICE;
   return SA_OK;
@@ -420,6 +457,7 @@ static sa_status prefill_impl(const sa_shape* shape, const sa_sparse_params* par
     a.local = params->local_tokens;
   }
   a.dbg = debug_word();
+  log_prefill(state ? "sa_sparse_prefill_resume" : "sa_sparse_prefill", shape, params, a.tpb, stream);
   if (launch_prefill(a, shape->head_dim, params->granularity, stream) != hipSuccess)
     return SA_ERR_DEVICE;
   return debug_finish(SA_OK, a.dbg, stream);
@@ -481,6 +519,7 @@ sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k, const v
   a.cache_len = cache_len;
   a.ksum = (const uint16_t*)k_summary;
   a.dbg = debug_word();
+  log_decode("sa_build_block_summary", shape, block_k, nullptr, 0, "bf16", stream);
   if (launch_block_summary(a, stream) != hipSuccess) return SA_ERR_DEVICE;
   return debug_finish(SA_OK, a.dbg, stream);
 }
@@ -528,6 +567,8 @@ static sa_status decode_impl(const sa_shape* shape, const sa_decode_params* para
   a.n_splits = decode_splits(shape, params);
   a.c = resolve_scale(params->softmax_scale, shape->head_dim);
   a.dbg = debug_word();
+  log_decode("sa_sparse_decode", shape, params->block_k, params, a.n_splits,
+             k_summary ? "bf16" : exps ? "fp4" : "q4", stream);
   if (launch_decode(a, stream) != hipSuccess) return SA_ERR_DEVICE;
   return debug_finish(SA_OK, a.dbg, stream);
 }

@@ -1,8 +1,9 @@
-"""The debug build (libsa_debug.so): on valid inputs it returns the release build's results bit
-for bit; on caller data that the release kernels clamp -- a list count past the stride, a list
-entry outside the sequence, entries out of order, a cache length past the cache -- the release
-build still runs (memory-safe, status ok) and the debug build reports SA_ERR_CHECK with the
-matching sa_debug_flags() bits."""
+"""Diagnostics.  The debug build (libsa_debug.so): on valid inputs it returns the release
+build's results bit for bit; on caller data that the release kernels clamp -- a list count past
+the stride, a list entry outside the sequence, entries out of order, a cache length past the
+cache -- the release build still runs (memory-safe, status ok) and the debug build reports
+SA_ERR_CHECK with the matching sa_debug_flags() bits.  SA_LOG: each entry point prints its
+configuration line to stderr."""
 import numpy as np
 import pytest
 
@@ -133,3 +134,37 @@ def test_debug_decode(dev, dbg_lib, monkeypatch):
             st = _status(lambda: _with_lib(monkeypatch, dbg_lib, call))
             assert st == _lib.SA_ERR_CHECK, (bad_len, st)
             assert dbg_lib.sa_debug_flags() & _lib.SA_DBG_CACHE_LEN
+
+
+def test_sa_log_lines(dev, monkeypatch, capfd):
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    x = synth.make_prefill("llama8b_32k", seq=600, hq=8, hkv=2)
+    q, k, v = to_dev(x.q, dev), to_dev(x.k, dev), to_dev(x.v, dev)
+    kw = dict(block_q=x.block_q, block_k=x.block_k, sink=x.sink, local=x.local)
+    theta = np.full(8, 6.0, np.float32)
+    capfd.readouterr()
+    monkeypatch.setenv("SA_LOG", "1")
+    lists = sa.estimate_mask(q, k, theta, **kw)
+    sa.sparse_prefill(q, k, v, lists, **kw)
+    d = synth.make_decode(batch=2, seq=1000, hq=8, hkv=2, head_dim=128, top_k=8)
+    qd, kc, vc = (to_dev(a, dev) for a in (d.q, d.k_cache, d.v_cache))
+    cl = torch.from_numpy(d.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=64)
+    sa.sparse_decode(qd, kc, vc, kbar, cl, block_k=64, top_k=8, sink=32, local=256)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    lines = [ln for ln in err.splitlines() if ln.startswith("[sa] ")]
+    assert len(lines) == 4, err
+    assert lines[0].startswith("[sa] sa_estimate_mask: B=1 Hq=8 Hkv=2 d=128 N=600 head_map=h/G "
+                               f"block_q={x.block_q} block_k=64 sink={x.sink} local={x.local} "
+                               "granularity=block estimator=pooled step=1"), lines[0]
+    assert lines[1].startswith("[sa] sa_sparse_prefill: B=1 Hq=8 Hkv=2 d=128 N=600"), lines[1]
+    assert f"row_tiles_per_block={x.block_q // 64}" in lines[1]
+    assert lines[2].startswith("[sa] sa_build_block_summary: B=2 Hq=2 Hkv=2 d=128 L=1000 block_k=64")
+    assert lines[3].startswith("[sa] sa_sparse_decode: B=2 Hq=8 Hkv=2 d=128 L=1000 block_k=64 top_k=8")
+    assert "summary=bf16" in lines[3]
+    monkeypatch.setenv("SA_LOG", "0")
+    sa.sparse_prefill(q, k, v, lists, **kw)
+    torch.cuda.synchronize()
+    assert "[sa]" not in capfd.readouterr().err
