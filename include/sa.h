@@ -240,7 +240,7 @@ sa_status sa_sparse_prefill_resume(const sa_shape* shape, const sa_sparse_params
  * kbar[b, J, g, :] = mean of the cached keys of block J (fp64 sum and divide, rounded to
  * fp32 then to bf16); blocks at or past cache_len[b] are written as zeros.
  * k_cache: device bf16 [B, seq_k, Hkv, d] (k_stride); cache_len: device int32 [B] with
- * cache_len[b] in [1, seq_k] (values outside are clamped on the device); k_summary:
+ * cache_len[b] in [0, seq_k] (values outside are clamped on the device to that range); k_summary:
  * device bf16 [B, ceil(seq_k/block_k), Hkv, d],
  * contiguous. */
 sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k,
@@ -256,7 +256,8 @@ sa_status sa_build_block_summary(const sa_shape* shape, int32_t block_k,
  * q: device bf16 [B, Hq, d] (q_stride[0] = batch stride, q_stride[2] = head stride);
  * o: device bf16 [B, Hq, d] likewise (o_stride); lse: nullable device fp32 [B, Hq];
  * selected: nullable device int32 [B, Hkv, top_k_blocks], ascending, padded with -1 (with
- * top_p the number of entries before the padding is each (b, g)'s budget).
+ * top_p the number of entries before the padding is each (b, g)'s budget).  An empty cache
+ * (cache_len[b] = 0 after clamping) selects nothing and gives o = 0 and lse = -inf.
  * ws: at least sa_workspace_size(SA_OP_DECODE, ...) bytes. */
 sa_status sa_sparse_decode(const sa_shape* shape, const sa_decode_params* params,
                            const void* q, const void* k_cache, const void* v_cache,

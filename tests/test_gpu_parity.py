@@ -888,3 +888,45 @@ def test_decode_edge_lengths(dev, bk, top_k, top_p, summary):
     assert err.max() < MAX_ABS and err.mean() < MEAN_ABS, (err.max(), err.mean())
     assert np.abs(lse.cpu().numpy() - LSE).max() < 1e-2
     log(f"  decode edge lengths bk={bk} K={top_k} top_p={top_p}: flips={flips} max|dO|={err.max():.2e}")
+
+
+@pytest.mark.parametrize("top_p", [0.0, 0.5])
+def test_decode_empty_cache(dev, top_p):
+    """A cache of length 0 beside non-empty ones: nothing is selected for it, its output is 0
+    and its LSE -inf (the documented result for an empty cache); the other sequences of the
+    batch meet the usual bars against the oracle."""
+    import torch
+    import block_sparse_attention_estimate_amd as sa
+    lens = [0, 40, 700]
+    x = synth.make_decode(batch=len(lens), seq=1024, hq=8, hkv=2, head_dim=128, top_k=8)
+    x.cache_len[:] = np.array(lens, np.int32)
+    log(f"decode empty cache top_p={top_p}")
+    q, kc, vc = to_dev(x.q, dev), to_dev(x.k_cache, dev), to_dev(x.v_cache, dev)
+    cl = torch.from_numpy(x.cache_len).to(dev)
+    kbar = sa.build_block_summary(kc, cl, block_k=64)
+    o, lse, sel = sa.sparse_decode(q, kc, vc, kbar, cl, block_k=64, top_k=8, sink=32, local=256,
+                                   top_p=top_p)
+    torch.cuda.synchronize()
+    assert (kbar[0] == 0).all()
+    assert (o[0].float() == 0).all()
+    assert torch.isneginf(lse[0]).all()
+    assert (sel[0] == -1).all()
+    kbar_ref = oracle.block_summary(x.k_cache[1:], x.cache_len[1:], 64)
+    ref = oracle.decode_select(x.q[1:], kbar_ref, x.cache_len[1:], block_k=64, top_k=8, sink=32,
+                               local=256, top_p=top_p)
+    s = sel.cpu().numpy()[1:]
+    if top_p > 0:
+        used, _, _ = check_topp_selection(s, ref)
+    else:
+        used = {}
+        for (b, g), r in ref.items():
+            k_ = min(8, -(-lens[b + 1] // 64))
+            got = s[b, g, :k_]
+            diff = set(got.tolist()) ^ set(r["selected"].tolist())
+            assert diff <= set(r["ambiguous"].tolist()), ((b, g), sorted(diff))
+            used[(b, g)] = got
+    O, LSE = oracle.decode_attention(x.q[1:], x.k_cache[1:], x.v_cache[1:], x.cache_len[1:], used,
+                                     block_k=64)
+    err = np.abs(o[1:].float().cpu().numpy() - O)
+    assert err.max() < MAX_ABS and err.mean() < MEAN_ABS, (err.max(), err.mean())
+    assert np.abs(lse[1:].cpu().numpy() - LSE).max() < 1e-2
